@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verification step on one MI355X.
+
+Workload: B=256 sequences, k=6 drafts, V=151936 bf16 logits, Zipf-shaped
+synthetic target logits (sorted -1.1*ln(rank) + N(0, 0.5^2), permuted),
+draft = target + N(0, 1), temperature 1, top-p 0.9 on both sides.  A step is
+one verification round over one batch: sv_verify_sample (softmax statistics,
+top-p thresholds, acceptance scan, residual / bonus draw) followed by
+sv_kv_rollback of every row's write pointer and page table (page size 16,
+contexts of 4096..8192 tokens, so that hundreds of steps can each shorten
+every sequence by up to k without running out of context).  Two input batches (2 GB together) alternate
+so that no step finds its logits in the 256 MB last-level cache.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified positions/sec and achieved HBM GB/s (% of peak), B=256 k=6 V=151936 bf16"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=2, help="input batches rotated between steps")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="rows in the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d is not supported (rows are "
+              "independent, so more GPUs would each run this same step on their own rows)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.steps + args.warmup + 20 > 680:
+        print("at most 660 steps: each rollback shortens every sequence by up to k",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_11_amd as sv
+    from rejection_sampling_verify_11_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    B, K, V, P = 256, 6, 151936, 0.9
+    sets = []
+    for r in range(args.sets):
+        inp = W.workload4(r, device=dev, B=B, k=K, V=V)
+        toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, r)
+        call = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
+                             None, seed=0, offset=0)
+        sets.append((inp, toks, call))
+    torch.cuda.synchronize()
+
+    # rollback state: contexts U[4096, 8192] plus the k+1 slots this round wrote
+    rows = W.workload5_rows(0, B=B, ctx_lo=4096, ctx_hi=8192)
+    kv_len0 = rows.kv_len0 + (K + 1)
+    ps = 16
+    MP = int(math.ceil((8192 + K + 1) / ps))
+    kv = W.paged_kv(kv_len0, ps, MP, spare_pages=0, seed=0)
+    kv_len = kv_len0.to(dev)
+    rb_calls = [sv.RollbackCall(kv_len, c.outputs["accepted"], kv.page_table.to(dev), ps, K,
+                                free_pages=kv.free_pages.to(dev), free_top=kv.free_top.to(dev),
+                                num_pages=kv.num_pages) for (_, _, c) in sets]
+    # one page table / stack shared by all calls
+    pt = rb_calls[0].args.page_table
+    for c in rb_calls[1:]:
+        c.args.page_table = pt
+        c.args.free_pages = rb_calls[0].args.free_pages
+        c.args.free_top = rb_calls[0].args.free_top
+
+    step_no = [0]
+
+    def step():
+        i = step_no[0]
+        _, _, call = sets[i % len(sets)]
+        call.set_offset(i)
+        call.run()
+        rb_calls[i % len(sets)].run()
+        step_no[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations, measured live with HIP events on the same stream
+    sv.timing_enable(dev, True)
+    for _ in range(min(args.steps, 20)):
+        step()
+    torch.cuda.synchronize()
+    kt = sv.timing_read(dev)
+    sv.timing_enable(dev, False)
+    st = rb_calls[0].row_status
+    assert int((st != 0).sum()) == 0, "rollback flagged rows: %s" % st.unique()
+    assert int((sets[0][2].outputs["row_status"] != 0).sum()) == 0
+
+    positions = B * K
+    alg_bytes = B * (2 * K + 1) * V * 2          # every logit of the batch, once
+    n_stats, ms_stats = kt["stats_bf16"]
+    stats_ms = ms_stats / n_stats
+    achieved = alg_bytes / (stats_ms * 1e-3) / 1e9
+    acc = torch.cat([s[2].outputs["accepted"].float() for s in sets]).mean().item()
+
+    result = {
+        "metric": METRIC,
+        "value": positions / (ms_step * 1e-3),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "B=256 k=6 V=151936 bf16 Zipf-shaped logits, top-p 0.9, T=1",
+                   "global_batch": B, "k": K, "V": V, "top_p": P,
+                   "input_sets": len(sets), "rollback": "page table, page size 16"},
+        "step_hbm_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "kernels_ms": {k: v[1] / v[0] for k, v in kt.items()},
+        "mean_accepted": acc,
+        "emitted_tokens_per_s": B * (acc + 1) / (ms_step * 1e-3),
+        "wall_s": wall,
+        "roofline": {"bound": "hbm", "kernel": "stats_bf16", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None},
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import svref
+        cores = len(os.sched_getaffinity(0))
+        inp, toks, _ = sets[0]
+        R = min(args.cpu_rows, B)
+        idx = torch.arange(R, device=dev)
+        tgt = W.host_logits(inp.target[idx])
+        dft = W.host_logits(inp.draft[idx])
+        tk = toks[:R].cpu().numpy()
+        T = inp.temperature[:R].cpu().numpy()
+        Pp = inp.top_p[:R].cpu().numpy()
+        t0 = time.perf_counter()
+        svref.verify_sample(tgt, dft, tk, T, Pp, seed=0, offset=0, nthreads=cores)
+        cpu_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": R * K / cpu_s, "unit": "verified positions/s",
+                                  "cores": cores, "kind": "oracle",
+                                  "sample": "%d of 256 rows of one batch (%d positions), "
+                                            "%.2f s wall" % (R, R * K, cpu_s)}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

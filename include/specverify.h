@@ -1,0 +1,232 @@
+/*
+ * specverify.h -- C ABI of the speculative-decoding verification step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then address):
+ *   [SSD] "自投机解码：层跳过与KV复用实现大模型无损推理加速"  (xdnf.cn/news/378309)
+ *   [SD]  "企业官网建设流程全解析" -- HTML title of a page explaining the
+ *         original draft-model speculative decoding (hotelren.com/news/5905390)
+ *   [FS]  FlashSpec speculative-decoding practice write-up (nzsm.cn/news/47291)
+ * Notation: p = target distribution, q = draft distribution, x_i = draft token
+ * at draft position i, k_b = draft length of row b, a_b = accepted count.
+ *
+ * Conventions for every entry point
+ *   - Pointers in the argument blocks are DEVICE pointers unless the field
+ *     says otherwise; the argument block itself lives in host memory and is
+ *     read before the call returns.
+ *   - The caller owns every buffer.  The library allocates no device memory;
+ *     scratch comes from the caller's workspace, sized by the *_bytes calls.
+ *   - Work is enqueued on the given stream and the call returns at once: no
+ *     synchronisation, no device-to-host copy.  Outputs are valid once the
+ *     stream has reached the call.
+ *   - Host-detectable problems (NULL required pointer, sizes out of range,
+ *     bad dtype, stride < V, workspace too small) return an error before any
+ *     launch and touch no output.
+ *   - Problems in the data itself are reported per row in row_status (bits
+ *     below).  A flagged row gets out_tokens = -1, accepted = -1,
+ *     num_emitted = 0 and NaN probabilities; other rows are unaffected.
+ *   - A handle caches device properties only.  One handle per host thread,
+ *     or lock around it.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sv_handle_s* sv_handle;
+
+typedef enum {
+  SV_OK = 0,
+  SV_E_ARG = 1,       /* NULL required pointer or a size out of range     */
+  SV_E_DTYPE = 2,     /* unknown dtype                                    */
+  SV_E_WORKSPACE = 3, /* workspace missing or smaller than required       */
+  SV_E_DEVICE = 4,    /* a HIP call or a launch failed                    */
+  SV_E_INTERNAL = 5
+} sv_status;
+
+typedef enum { SV_FP32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Limits checked on the host. */
+#define SV_MAX_K 32          /* k_max <= SV_MAX_K                          */
+#define SV_MAX_V (1 << 30)   /* V <= SV_MAX_V (greedy)                     */
+#define SV_MAX_V_SAMPLED (1 << 21) /* V bound of sampled verification and
+                                      draft sampling                        */
+
+/* row_status bits */
+#define SV_ROW_NONFINITE_LOGIT (1u << 0) /* NaN or +inf in a vector the row uses */
+#define SV_ROW_NO_FINITE       (1u << 1) /* a vector with no finite entry        */
+#define SV_ROW_BAD_TOKEN       (1u << 2) /* draft token outside [0, V)           */
+#define SV_ROW_BAD_K           (1u << 3) /* k_b outside [1, k_max]               */
+#define SV_ROW_BAD_TEMPERATURE (1u << 4) /* T <= 0 or not finite                 */
+#define SV_ROW_BAD_TOP_P       (1u << 5) /* top_p <= 0 or NaN                    */
+#define SV_ROW_BAD_PAGES       (1u << 6) /* page table inconsistent with kv_len  */
+#define SV_ROW_FREE_OVERFLOW   (1u << 7) /* released pages do not fit the stack  */
+#define SV_ROW_BAD_ACCEPTED    (1u << 8) /* accepted outside [0, k_b] (e.g. -1
+                                            from a flagged verify) or a length
+                                            that would go negative            */
+
+/* verify flags */
+#define SV_FLAG_TOPP_TARGET_ONLY (1u << 0) /* truncate p only, keep q whole
+                                              ([SSD] §3.4, the author's
+                                              preferred variant)              */
+
+/* Poison pattern written into rolled-back KV slots when a pool is given. */
+#define SV_POISON_BF16 0xFFFFu
+
+sv_status sv_create(int hip_device, sv_handle* out);
+sv_status sv_destroy(sv_handle h);
+const char* sv_status_string(sv_status s);
+
+/* Kernel timing (diagnostics).  While enabled, every kernel this handle
+ * launches is bracketed by two HIP events recorded on the caller's stream
+ * (events are created on first use and reused; at most 4096 launches are
+ * kept between reads).  sv_timing_read waits for those events, writes up to
+ * max_entries (kernel name, launch count, total milliseconds) triples
+ * accumulated since the previous read, clears the record and returns the
+ * number of distinct kernels.  Names point to static strings. */
+sv_status sv_timing_enable(sv_handle h, int on);
+int sv_timing_read(sv_handle h, int max_entries, const char** names,
+                   int32_t* launches, double* total_ms);
+
+/* ------------------------------------------------------------------------ */
+/* Verification                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Argument block shared by the sampled and greedy entry points.
+ *
+ * Layout: target vector (b, i), i in [0, k_max], starts at element
+ * (b*(k_max+1) + i) * target_vec_stride of target_logits; draft vector
+ * (b, i), i in [0, k_max), at (b*k_max + i) * draft_vec_stride.  Elements
+ * are fp32 or bf16 (dtype) and contiguous inside a vector; strides are in
+ * elements and must be >= V.  A torch tensor of shape [B, k_max+1, V]
+ * (contiguous) has target_vec_stride = V.  16-byte aligned vectors take the
+ * wide-load path; any alignment is accepted.
+ *
+ * Positions beyond a row's k_b are ignored (their logits need not be valid).
+ */
+typedef struct {
+  int32_t B, k_max, V;
+  int32_t dtype;                     /* sv_dtype                               */
+  const void* target_logits;         /* [B][k_max+1][vec_stride]               */
+  int64_t target_vec_stride;
+  const void* draft_logits;          /* [B][k_max][vec_stride]; greedy: NULL
+                                        means use draft_tokens                 */
+  int64_t draft_vec_stride;
+  const int32_t* draft_tokens;       /* [B][k_max]; sampled: required          */
+  const int32_t* k_per_row;          /* [B] in [1, k_max]; NULL -> k_max       */
+  const float* temperature;          /* [B] > 0, one value for p AND q
+                                        ([SSD] §2.4; [FS] §5.1); sampled only */
+  const float* top_p;                /* [B] in (0, 1]; NULL or >= 1 -> off     */
+  uint64_t seed, offset;             /* Philox key word 0 / round counter      */
+  uint32_t flags;                    /* SV_FLAG_*                              */
+
+  int32_t* out_tokens;               /* [B][k_max+1], -1 padded                */
+  int32_t* accepted;                 /* [B]                                    */
+  int32_t* num_emitted;              /* [B] or NULL                            */
+  float* p_at_draft;                 /* [B][k_max] or NULL: p'_i(x_i)          */
+  float* q_at_draft;                 /* [B][k_max] or NULL: q'_i(x_i)          */
+  int32_t* row_status;               /* [B] or NULL                            */
+
+  void* workspace;                   /* device scratch, >= the *_bytes figure  */
+  size_t workspace_bytes;
+} sv_verify_args;
+
+/* Workspace for sv_verify_sample / sv_verify_greedy / sv_draft_sample with
+ * these sizes (the maximum over the three).  Pure host function. */
+size_t sv_verify_workspace_bytes(int32_t B, int32_t k_max, int32_t V,
+                                 int32_t dtype, uint32_t flags);
+
+/* Host-side validation only (no HIP call).  mode: 0 sampled, 1 greedy,
+ * 2 draft sampling.  Returns what the entry point would return before
+ * launching anything. */
+sv_status sv_check_verify_args(const sv_verify_args* a, int mode);
+
+/* Rejection-sampling verification ([SSD] §2.4, §4.3; [SD] §2.1-§2.2; [FS]
+ * §2.3 with its letters swapped back):
+ *   p = softmax(target/T), q = softmax(draft/T), each optionally truncated
+ *   to its tie-closed top-p set and renormalised (p', q');
+ *   scanning i = 0..k_b-1, accept x_i iff u(b,i,0) < p'(x_i)/q'(x_i)
+ *   (ratio 0 when q'(x_i) = 0);
+ *   at the first rejection a, emit y ~ norm(max(0, p'_a - q'_a)) by inverse
+ *   CDF in token order with u(b,a,1) (p'_a itself if that residual is zero);
+ *   if all k_b accepted, emit a bonus y ~ p'_{k_b} with u(b,k_b,1).
+ * u(b,pos,draw) is the top 24 bits of word 0 of Philox4x64-10 at counter
+ * (b, pos, draw, offset) and key (seed, 0), times 2^-24.
+ * Outputs: out_tokens[b] = x_0..x_{a-1}, y, -1...; accepted = a;
+ * num_emitted = a + 1; p_at_draft/q_at_draft = p'_i(x_i), q'_i(x_i) for
+ * i < k_b and 0 beyond. */
+sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s);
+
+/* Greedy branch ([SSD] §2.4, §5.2): g_i = argmax of the raw target logits at
+ * position i (lowest index on ties; temperature and top-p ignored); x_i =
+ * draft_tokens, or the argmax of draft_logits when those are given; a = first
+ * i with x_i != g_i, else k_b; emits x_0..x_{a-1}, g_a.  p_at_draft and
+ * q_at_draft are not written. */
+sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s);
+
+/* Draft sampling, the step before verification ([SSD] §4.2; [FS] §3.2):
+ * writes draft_tokens[b][i] = inverse CDF of q'_i with u(b,i,2) for i < k_b
+ * and -1 beyond (draft_tokens is an OUTPUT here, cast away from const).
+ * Uses draft_logits, temperature, top_p, k_per_row, seed, offset, flags and
+ * row_status; target_logits and the verify outputs are ignored. */
+sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s);
+
+/* ------------------------------------------------------------------------ */
+/* KV rollback                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Paged KV pool layout (only read when poisoning):
+ *   bf16 [num_pages][num_layers][2 (K, V)][kv_heads][page_size][head_dim].
+ */
+typedef struct {
+  int32_t B, k_max, page_size, max_pages_per_seq;
+  int32_t* kv_len;          /* [B] in: length after this round's k_b + 1
+                               speculative writes; out: committed length     */
+  const int32_t* k_per_row; /* [B] or NULL -> k_max                          */
+  const int32_t* accepted;  /* [B] from a verify call on the same stream     */
+  int32_t* page_table;      /* [B][max_pages_per_seq]; -1 = unmapped         */
+  int32_t num_pages;        /* physical pages in the pool: mapped entries
+                               must be in [0, num_pages); required (> 0)
+                               when kv_pool is given, 0 = unchecked otherwise */
+  int32_t* free_pages;      /* free-page stack storage, or NULL to keep
+                               pages mapped and only shrink lengths          */
+  int32_t* free_top;        /* [1] stack height (device)                     */
+  int32_t free_capacity;   /* a stack height outside [0, capacity] makes
+                               every releasing row overflow                 */
+  void* kv_pool;            /* NULL, or a bf16 pool whose rolled-back slots
+                               are overwritten with SV_POISON_BF16           */
+  int32_t num_layers, kv_heads, head_dim;
+  int32_t* row_status;      /* [B] or NULL                                   */
+  void* workspace;          /* needed only with kv_pool                      */
+  size_t workspace_bytes;
+} sv_rollback_args;
+
+size_t sv_rollback_workspace_bytes(int32_t B);
+sv_status sv_check_rollback_args(const sv_rollback_args* a);
+
+/* Rolls each row's KV write pointer back to the accepted prefix ([SSD] §3.3,
+ * §4.3: "reset the write pointer to seq_len + i"; §4.5: one offset per
+ * sequence):
+ *   new = kv_len - (k_b - a_b);
+ * logical pages [ceil(new/ps), ceil(old/ps)) are released ([SSD] §3.3: paged
+ * caches roll back at page granularity): their entries become -1 and the
+ * physical pages are pushed on the free stack in (row, page) order.  A row's
+ * pages are pushed iff the running total of releases over the valid rows up
+ * to it fits the capacity; otherwise the row gets SV_ROW_FREE_OVERFLOW and is
+ * left unchanged.  With free_pages = NULL nothing is released and only the
+ * length shrinks ([SD] §4.3).  Rows failing a check (bad k, accepted, page
+ * table) are left unchanged and flagged.  With kv_pool, the slots
+ * [new, old) of committed rows are poisoned in every layer and head. */
+sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

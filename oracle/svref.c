@@ -193,6 +193,10 @@ static void load_draft(const row_ctx* c, int32_t b, int32_t i) {
     c->z[j] = decode_logit(a->draft, a->dtype, base + j);
 }
 
+static uint64_t row_id(const svref_verify_args* a, int32_t b) {
+  return a->row_ids ? (uint64_t)a->row_ids[b] : (uint64_t)b;
+}
+
 static double row_top_p(const svref_verify_args* a, int32_t b) {
   return a->top_p ? (double)a->top_p[b] : 1.0;
 }
@@ -315,7 +319,7 @@ static void sample_row(row_ctx* c, int32_t b) {
   int32_t acc = k;
   for (int32_t i = 0; i < k; ++i) {
     double rho = qx[i] > 0.0 ? px[i] / qx[i] : 0.0;
-    double u = svref_uniform(a->seed, (uint64_t)b, (uint64_t)i, 0, a->offset);
+    double u = svref_uniform(a->seed, row_id(a, b), (uint64_t)i, 0, a->offset);
     if (a->diag_rho) a->diag_rho[(int64_t)b * K + i] = rho;
     if (a->diag_acc_margin) a->diag_acc_margin[(int64_t)b * K + i] = u - rho;
     if (!(u < rho)) { acc = i; break; }
@@ -324,12 +328,12 @@ static void sample_row(row_ctx* c, int32_t b) {
     double rho = qx[i] > 0.0 ? px[i] / qx[i] : 0.0;
     if (a->diag_rho) a->diag_rho[(int64_t)b * K + i] = rho;
     if (a->diag_acc_margin) {
-      double u = svref_uniform(a->seed, (uint64_t)b, (uint64_t)i, 0, a->offset);
+      double u = svref_uniform(a->seed, row_id(a, b), (uint64_t)i, 0, a->offset);
       a->diag_acc_margin[(int64_t)b * K + i] = u - rho;
     }
   }
 
-  double u1 = svref_uniform(a->seed, (uint64_t)b, (uint64_t)acc, 1, a->offset);
+  double u1 = svref_uniform(a->seed, row_id(a, b), (uint64_t)acc, 1, a->offset);
   int32_t y;
   double margin = INFINITY, R = -1.0;
   if (acc < k) {
@@ -434,20 +438,29 @@ static void draft_row(row_ctx* c, int32_t b, int32_t* out) {
   const svref_verify_args* a = c->a;
   const int32_t V = a->V, K = a->k_max;
   int32_t k;
+  /* status bits follow the verify call: header checks, then the data
+   * checks of every vector the row uses when k_b itself is valid */
   int st = row_header_status(a, b, &k, 1);
   for (int32_t i = 0; i < K; ++i) out[(int64_t)b * K + i] = -1;
-  if (st) { if (a->row_status) a->row_status[b] = st; return; }
+  if (!(st & SVREF_ROW_BAD_K)) {
+    for (int32_t i = 0; i < k; ++i) {
+      load_draft(c, b, i);
+      st |= vector_status(c->z, V);
+    }
+  }
+  if (a->row_status) a->row_status[b] = st;
+  if (st) return;
   const double T = (double)a->temperature[b];
   const double P = (a->flags & SVREF_TOPP_TARGET_ONLY) ? 1.0 : row_top_p(a, b);
   for (int32_t i = 0; i < k; ++i) {
     load_draft(c, b, i);
-    int s = svref_softmax_topp(c->z, V, T, P, c->qa, NULL, NULL, NULL);
-    if (s) { st |= s; continue; }
-    double u = svref_uniform(a->seed, (uint64_t)b, (uint64_t)i, 2, a->offset);
-    out[(int64_t)b * K + i] = inverse_cdf(c->qa, V, u, NULL, NULL);
+    double G, above, margin;
+    svref_softmax_topp(c->z, V, T, P, c->qa, &G, &above, NULL);
+    double u = svref_uniform(a->seed, row_id(a, b), (uint64_t)i, 2, a->offset);
+    out[(int64_t)b * K + i] = inverse_cdf(c->qa, V, u, &margin, NULL);
+    if (a->diag_acc_margin) a->diag_acc_margin[(int64_t)b * K + i] = margin;
+    if (a->diag_topp_margin_d) a->diag_topp_margin_d[(int64_t)b * K + i] = topp_margin(P, G, above);
   }
-  if (st) for (int32_t i = 0; i < K; ++i) out[(int64_t)b * K + i] = -1;
-  if (a->row_status) a->row_status[b] = st;
 }
 
 /* ====================================================================== */
@@ -526,6 +539,7 @@ int svref_kv_rollback(const svref_rollback_args* a) {
       a->max_pages_per_seq < 1 || !a->kv_len || !a->accepted || !a->page_table)
     return -1;
   if (a->free_pages && (!a->free_top || a->free_capacity < 0)) return -1;
+  if (a->kv_pool && a->num_pages <= 0) return -1;
   const int32_t ps = a->page_size, MP = a->max_pages_per_seq;
   int32_t* st = (int32_t*)calloc((size_t)(a->B > 0 ? a->B : 1), sizeof(int32_t));
   int32_t* newlen = (int32_t*)calloc((size_t)(a->B > 0 ? a->B : 1), sizeof(int32_t));
@@ -547,7 +561,8 @@ int svref_kv_rollback(const svref_rollback_args* a) {
       int32_t used = ceil_div(old, ps);
       for (int32_t pg = 0; pg < MP; ++pg) {
         int32_t e = a->page_table[(int64_t)b * MP + pg];
-        if (pg < used ? (e < 0) : (e != -1)) st[b] |= SVREF_ROW_BAD_PAGES;
+        int bad_map = e < 0 || (a->num_pages > 0 && e >= a->num_pages);
+        if (pg < used ? bad_map : (e != -1)) st[b] |= SVREF_ROW_BAD_PAGES;
       }
     }
     if (!st[b]) {
@@ -569,7 +584,7 @@ int svref_kv_rollback(const svref_rollback_args* a) {
     if (st[b]) continue;
     running += nrel[b];
     if (!a->free_pages || nrel[b] == 0) continue;
-    if ((int64_t)top0 + running > a->free_capacity) {
+    if (top0 < 0 || (int64_t)top0 + running > a->free_capacity) {
       st[b] |= SVREF_ROW_FREE_OVERFLOW;
       continue;
     }

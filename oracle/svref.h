@@ -101,6 +101,9 @@ typedef struct {
   uint64_t seed, offset;
   uint32_t flags;              /* SVREF_TOPP_TARGET_ONLY                  */
   int32_t nthreads;            /* worker threads over rows; <= 0 means 1  */
+  const int32_t* row_ids;      /* [B] or NULL: the row index each row uses
+                                  in the random counter (lets a subset of a
+                                  batch be checked row by row)            */
 
   /* outputs (host memory) */
   int32_t* out_tokens;  /* [B][k_max+1], -1 padded                        */
@@ -119,6 +122,8 @@ typedef struct {
   double* diag_topp_margin_d; /* [B][k_max]                               */
   double* diag_residual_mass; /* [B]   R at the resampled position, or -1
                                  when the bonus path was taken            */
+  /* draft sampling fills diag_acc_margin[b][i] with the CDF margin of its
+   * draw at position i and diag_topp_margin_d with the top-p margins      */
 } svref_verify_args;
 
 /* Rejection-sampling verification, one row at a time ([SSD] §2.4, §4.3;
@@ -143,6 +148,8 @@ typedef struct {
   const int32_t* k_per_row;    /* [B] or NULL -> k_max                     */
   const int32_t* accepted;     /* [B]                                      */
   int32_t* page_table;         /* [B][max_pages_per_seq], -1 = unmapped    */
+  int32_t num_pages;           /* pool size; mapped entries must be below
+                                  it (0 = unchecked, not allowed with a pool) */
   int32_t* free_pages;         /* stack storage, or NULL = keep pages      */
   int32_t* free_top;           /* [1] stack height                         */
   int32_t free_capacity;

@@ -38,7 +38,7 @@ class VerifyArgs(C.Structure):
         ("draft", _P), ("draft_vec_stride", C.c_int64),
         ("draft_tokens", _P), ("k_per_row", _P), ("temperature", _P), ("top_p", _P),
         ("seed", C.c_uint64), ("offset", C.c_uint64), ("flags", C.c_uint32),
-        ("nthreads", C.c_int32),
+        ("nthreads", C.c_int32), ("row_ids", _P),
         ("out_tokens", _P), ("accepted", _P), ("num_emitted", _P),
         ("p_at_draft", _P), ("q_at_draft", _P), ("row_status", _P),
         ("diag_rho", _P), ("diag_acc_margin", _P), ("diag_cdf_margin", _P),
@@ -52,7 +52,7 @@ class RollbackArgs(C.Structure):
         ("B", C.c_int32), ("k_max", C.c_int32), ("page_size", C.c_int32),
         ("max_pages_per_seq", C.c_int32),
         ("kv_len", _P), ("k_per_row", _P), ("accepted", _P), ("page_table", _P),
-        ("free_pages", _P), ("free_top", _P), ("free_capacity", C.c_int32),
+        ("num_pages", C.c_int32), ("free_pages", _P), ("free_top", _P), ("free_capacity", C.c_int32),
         ("kv_pool", _P), ("num_layers", C.c_int32), ("kv_heads", C.c_int32),
         ("head_dim", C.c_int32), ("row_status", _P),
     ]
@@ -139,7 +139,7 @@ def _logits(x):
 
 
 def _verify_args(target, draft, draft_tokens, temperature, top_p, k_per_row,
-                 seed, offset, flags, nthreads, V=None):
+                 seed, offset, flags, nthreads, V=None, row_ids=None):
     target, dt = _logits(target)
     B, K1, Vs = target.shape
     K = K1 - 1
@@ -169,15 +169,20 @@ def _verify_args(target, draft, draft_tokens, temperature, top_p, k_per_row,
         a.top_p = _ptr(keep["P"])
     a.seed, a.offset, a.flags = int(seed), int(offset), int(flags)
     a.nthreads = int(nthreads)
+    if row_ids is not None:
+        keep["rows"] = np.ascontiguousarray(row_ids, dtype=np.int32).reshape(B)
+        a.row_ids = _ptr(keep["rows"])
     return a, keep, B, K
 
 
 def verify_sample(target, draft, draft_tokens, temperature, top_p=None,
-                  k_per_row=None, seed=0, offset=0, flags=0, nthreads=1, V=None):
+                  k_per_row=None, seed=0, offset=0, flags=0, nthreads=1, V=None,
+                  row_ids=None):
     """Sampled verification of every row; returns a dict of numpy outputs and
-    the comparator diagnostics."""
+    the comparator diagnostics.  row_ids: the batch row index of each given
+    row (for checking a subset of a batch)."""
     a, keep, B, K = _verify_args(target, draft, draft_tokens, temperature, top_p,
-                                 k_per_row, seed, offset, flags, nthreads, V)
+                                 k_per_row, seed, offset, flags, nthreads, V, row_ids)
     out = {
         "out_tokens": np.full((B, K + 1), -7, np.int32),
         "accepted": np.full(B, -7, np.int32),
@@ -225,8 +230,9 @@ def verify_greedy(target, draft=None, draft_tokens=None, k_per_row=None, nthread
 
 
 def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=0,
-                 flags=0, nthreads=1, V=None):
-    """Draft tokens x_i ~ q'_i with draw 2 (int32 [B][k_max]) and row status."""
+                 flags=0, nthreads=1, V=None, diagnostics=False):
+    """Draft tokens x_i ~ q'_i with draw 2 (int32 [B][k_max]) and row status;
+    with diagnostics=True also the CDF and top-p margins of every draw."""
     draft, dt = _logits(draft)
     B, K, Vs = draft.shape
     # the argument block wants a target; point it at the draft (unused here)
@@ -239,15 +245,20 @@ def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=
     toks = np.full((B, K), -7, np.int32)
     st = np.full(B, -7, np.int32)
     a.row_status = _ptr(st)
+    cdf = np.full((B, K), np.inf)
+    topp = np.full((B, K), np.inf)
+    a.diag_acc_margin, a.diag_topp_margin_d = _ptr(cdf), _ptr(topp)
     rc = lib().svref_draft_sample(C.byref(a), _ptr(toks))
     if rc != 0:
         raise ValueError("svref_draft_sample rejected its arguments")
+    if diagnostics:
+        return toks, st, cdf, topp
     return toks, st
 
 
 def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
                 free_pages=None, free_top=None, free_capacity=0, kv_pool=None,
-                num_layers=0, kv_heads=0, head_dim=0):
+                num_layers=0, kv_heads=0, head_dim=0, num_pages=0):
     """Runs the oracle rollback IN PLACE on the given numpy arrays; returns the
     row status array."""
     B = kv_len.shape[0]
@@ -257,6 +268,7 @@ def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
     for arr in (kv_len, accepted, page_table):
         assert arr.dtype == np.int32 and arr.flags.c_contiguous
     a.kv_len, a.accepted, a.page_table = _ptr(kv_len), _ptr(accepted), _ptr(page_table)
+    a.num_pages = int(num_pages if kv_pool is None or num_pages else kv_pool.shape[0])
     keep = []
     if k_per_row is not None:
         kp = np.ascontiguousarray(k_per_row, dtype=np.int32)

@@ -1,0 +1,367 @@
+"""ctypes binding of libspecverify.so (the C ABI in include/specverify.h).
+
+Argument marshalling only: torch provides device buffers and the current
+HIP stream; every step of the computation runs in the library's kernels.
+The library must have been built (rejection_sampling_verify_11_amd/build.py);
+there is no fallback of any kind.
+"""
+import ctypes as C
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK, SV_E_ARG, SV_E_DTYPE, SV_E_WORKSPACE, SV_E_DEVICE, SV_E_INTERNAL = range(6)
+SV_FP32, SV_BF16 = 0, 1
+SV_MAX_K = 32
+SV_MAX_V = 1 << 30
+SV_MAX_V_SAMPLED = 1 << 21
+FLAG_TOPP_TARGET_ONLY = 1 << 0
+POISON_BF16 = 0xFFFF
+
+ROW_NONFINITE_LOGIT = 1 << 0
+ROW_NO_FINITE = 1 << 1
+ROW_BAD_TOKEN = 1 << 2
+ROW_BAD_K = 1 << 3
+ROW_BAD_TEMPERATURE = 1 << 4
+ROW_BAD_TOP_P = 1 << 5
+ROW_BAD_PAGES = 1 << 6
+ROW_FREE_OVERFLOW = 1 << 7
+ROW_BAD_ACCEPTED = 1 << 8
+
+_P = C.c_void_p
+
+
+class VerifyArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("k_max", C.c_int32), ("V", C.c_int32), ("dtype", C.c_int32),
+        ("target_logits", _P), ("target_vec_stride", C.c_int64),
+        ("draft_logits", _P), ("draft_vec_stride", C.c_int64),
+        ("draft_tokens", _P), ("k_per_row", _P), ("temperature", _P), ("top_p", _P),
+        ("seed", C.c_uint64), ("offset", C.c_uint64), ("flags", C.c_uint32),
+        ("out_tokens", _P), ("accepted", _P), ("num_emitted", _P),
+        ("p_at_draft", _P), ("q_at_draft", _P), ("row_status", _P),
+        ("workspace", _P), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class RollbackArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("k_max", C.c_int32), ("page_size", C.c_int32),
+        ("max_pages_per_seq", C.c_int32),
+        ("kv_len", _P), ("k_per_row", _P), ("accepted", _P), ("page_table", _P),
+        ("num_pages", C.c_int32),
+        ("free_pages", _P), ("free_top", _P), ("free_capacity", C.c_int32),
+        ("kv_pool", _P), ("num_layers", C.c_int32), ("kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("row_status", _P),
+        ("workspace", _P), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
+           "sv_verify_workspace_bytes",
+           "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
+           "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback")
+
+_lib = None
+_lock = threading.Lock()
+_handles = {}
+
+
+def library():
+    """Loads libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError("libspecverify.so is not built: run "
+                                      "`python -c 'import __graft_entry__ as g; g.build()'`")
+                L = C.CDLL(LIB_PATH)
+                L.sv_create.argtypes = [C.c_int, C.POINTER(_P)]
+                L.sv_create.restype = C.c_int
+                L.sv_destroy.argtypes = [_P]
+                L.sv_destroy.restype = C.c_int
+                L.sv_status_string.argtypes = [C.c_int]
+                L.sv_status_string.restype = C.c_char_p
+                L.sv_timing_enable.argtypes = [_P, C.c_int]
+                L.sv_timing_enable.restype = C.c_int
+                L.sv_timing_read.argtypes = [_P, C.c_int, _P, _P, _P]
+                L.sv_timing_read.restype = C.c_int
+                L.sv_verify_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32,
+                                                        C.c_int32, C.c_uint32]
+                L.sv_verify_workspace_bytes.restype = C.c_size_t
+                L.sv_check_verify_args.argtypes = [C.POINTER(VerifyArgs), C.c_int]
+                L.sv_check_verify_args.restype = C.c_int
+                for f in (L.sv_verify_sample, L.sv_verify_greedy, L.sv_draft_sample):
+                    f.argtypes = [_P, C.POINTER(VerifyArgs), _P]
+                    f.restype = C.c_int
+                L.sv_rollback_workspace_bytes.argtypes = [C.c_int32]
+                L.sv_rollback_workspace_bytes.restype = C.c_size_t
+                L.sv_check_rollback_args.argtypes = [C.POINTER(RollbackArgs)]
+                L.sv_check_rollback_args.restype = C.c_int
+                L.sv_kv_rollback.argtypes = [_P, C.POINTER(RollbackArgs), _P]
+                L.sv_kv_rollback.restype = C.c_int
+                _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return library().sv_status_string(code).decode()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, what, code):
+        super().__init__("%s: %s (%d)" % (what, status_string(code), code))
+        self.code = code
+
+
+def handle(device: torch.device):
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    h = _handles.get(idx)
+    if h is None:
+        out = _P()
+        rc = library().sv_create(idx, C.byref(out))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_create", rc)
+        h = _handles[idx] = out
+    return h
+
+
+def timing_enable(device, on=True):
+    """Brackets every library kernel launch on this device with HIP events."""
+    rc = library().sv_timing_enable(handle(torch.device(device)), 1 if on else 0)
+    if rc != SV_OK:
+        raise SpecVerifyError("sv_timing_enable", rc)
+
+
+def timing_read(device):
+    """{kernel name: (launches, total ms)} since the last read (waits for the
+    recorded events)."""
+    n = 64
+    names = (C.c_char_p * n)()
+    launches = (C.c_int32 * n)()
+    ms = (C.c_double * n)()
+    k = library().sv_timing_read(handle(torch.device(device)), n, names, launches, ms)
+    return {names[i].decode(): (launches[i], ms[i]) for i in range(min(k, n))}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return _P(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_FP32
+    raise TypeError("logits must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _vec_stride(t, npos, name):
+    """[B, npos, V] tensor whose vector (b, i) starts at (b*npos + i)*stride."""
+    if t.dim() != 3 or t.shape[1] != npos:
+        raise ValueError("%s must be [B, %d, V], got %s" % (name, npos, tuple(t.shape)))
+    B, _, V = t.shape
+    if V > 1 and t.stride(2) != 1:
+        raise ValueError("%s: each vector must be contiguous" % name)
+    if npos == 1:
+        s = t.stride(0) if B > 1 else V
+    else:
+        s = t.stride(1)
+        if B > 1 and t.stride(0) != npos * s:
+            raise ValueError("%s: vectors must be evenly strided" % name)
+    if s < V:
+        raise ValueError("%s: vector stride %d < V = %d" % (name, s, V))
+    return s
+
+
+def _i32(t, shape, name, device):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) \
+            or t.device != device:
+        raise ValueError("%s must be a contiguous int32 %s tensor on %s" % (name, shape, device))
+    return t
+
+
+def _f32(t, shape, name, device):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) \
+            or t.device != device:
+        raise ValueError("%s must be a contiguous float32 %s tensor on %s" % (name, shape, device))
+    return t
+
+
+class VerifyCall:
+    """One prepared verification call: buffers allocated once, the argument
+    block filled once; run() only enqueues the library call."""
+
+    def __init__(self, mode, target, draft, draft_tokens=None, temperature=None, top_p=None,
+                 k_per_row=None, seed=0, offset=0, flags=0, want_probs=True):
+        self.mode = mode  # "sample", "greedy" or "draft"
+        ref = draft if mode == "draft" else target
+        dev = ref.device
+        if dev.type != "cuda":
+            raise ValueError("logits must be on a GPU")
+        B = ref.shape[0]
+        if mode == "draft":
+            K = draft.shape[1]
+            V = draft.shape[2]
+        else:
+            K = target.shape[1] - 1
+            V = target.shape[2]
+        a = VerifyArgs()
+        a.B, a.k_max, a.V = B, K, V
+        a.dtype = _dtype_code(ref)
+        keep = []
+        if mode != "draft":
+            a.target_logits = _ptr(target)
+            a.target_vec_stride = _vec_stride(target, K + 1, "target")
+            keep.append(target)
+        if draft is not None:
+            if draft.dtype != ref.dtype or draft.device != dev:
+                raise ValueError("draft logits must match the target's dtype and device")
+            a.draft_logits = _ptr(draft)
+            a.draft_vec_stride = _vec_stride(draft, K, "draft")
+            keep.append(draft)
+        if mode == "draft":
+            draft_tokens = torch.full((B, K), -1, dtype=torch.int32, device=dev)
+        keep.append(_i32(draft_tokens, (B, K), "draft_tokens", dev))
+        a.draft_tokens = _ptr(draft_tokens)
+        keep.append(_i32(k_per_row, (B,), "k_per_row", dev))
+        a.k_per_row = _ptr(k_per_row)
+        keep.append(_f32(temperature, (B,), "temperature", dev))
+        a.temperature = _ptr(temperature)
+        keep.append(_f32(top_p, (B,), "top_p", dev))
+        a.top_p = _ptr(top_p)
+        a.seed, a.offset, a.flags = int(seed), int(offset), int(flags)
+        self.outputs = {}
+        if mode != "draft":
+            o = self.outputs
+            o["out_tokens"] = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+            o["accepted"] = torch.empty(B, dtype=torch.int32, device=dev)
+            o["num_emitted"] = torch.empty(B, dtype=torch.int32, device=dev)
+            a.out_tokens, a.accepted = _ptr(o["out_tokens"]), _ptr(o["accepted"])
+            a.num_emitted = _ptr(o["num_emitted"])
+            if mode == "sample" and want_probs:
+                o["p_at_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+                o["q_at_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+                a.p_at_draft, a.q_at_draft = _ptr(o["p_at_draft"]), _ptr(o["q_at_draft"])
+        else:
+            self.outputs["draft_tokens"] = draft_tokens
+        self.outputs["row_status"] = torch.empty(B, dtype=torch.int32, device=dev)
+        a.row_status = _ptr(self.outputs["row_status"])
+        L = library()
+        nbytes = L.sv_verify_workspace_bytes(B, K, V, a.dtype, a.flags) if B > 0 else 256
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
+        self.args = a
+        self._keep = keep
+        self.device = dev
+        self._fn = {"sample": L.sv_verify_sample, "greedy": L.sv_verify_greedy,
+                    "draft": L.sv_draft_sample}[mode]
+        self._h = handle(dev)
+        self._ref = C.byref(self.args)
+
+    def set_offset(self, offset):
+        self.args.offset = int(offset)
+
+    def run(self, stream=None):
+        rc = self._fn(self._h, self._ref, _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("specverify " + self.mode, rc)
+        return self.outputs
+
+
+def verify_sample(target, draft, draft_tokens, temperature, top_p=None, k_per_row=None,
+                  seed=0, offset=0, flags=0, stream=None):
+    """Rejection-sampling verification (sv_verify_sample).  Returns a dict of
+    device tensors: out_tokens, accepted, num_emitted, p_at_draft, q_at_draft,
+    row_status."""
+    return VerifyCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
+                      seed, offset, flags).run(stream)
+
+
+def verify_greedy(target, draft_tokens=None, draft=None, k_per_row=None, stream=None):
+    """Greedy verification (sv_verify_greedy)."""
+    return VerifyCall("greedy", target, draft, draft_tokens, None, None, k_per_row).run(stream)
+
+
+def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=0, flags=0,
+                 stream=None):
+    """Draft tokens ~ q' with draw 2 (sv_draft_sample); returns (tokens, row_status)."""
+    out = VerifyCall("draft", None, draft, None, temperature, top_p, k_per_row, seed, offset,
+                     flags).run(stream)
+    return out["draft_tokens"], out["row_status"]
+
+
+class RollbackCall:
+    """One prepared rollback call over fixed device tensors (updated in place
+    by every run())."""
+
+    def __init__(self, kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
+                 free_pages=None, free_top=None, kv_pool=None, num_pages=0, num_layers=0,
+                 kv_heads=0, head_dim=0):
+        dev = kv_len.device
+        if dev.type != "cuda":
+            raise ValueError("rollback state must be on a GPU")
+        B = kv_len.shape[0]
+        a = RollbackArgs()
+        a.B, a.k_max, a.page_size = B, int(k_max), int(page_size)
+        a.max_pages_per_seq = page_table.shape[1]
+        _i32(kv_len, (B,), "kv_len", dev)
+        _i32(accepted, (B,), "accepted", dev)
+        _i32(page_table, tuple(page_table.shape), "page_table", dev)
+        a.kv_len, a.accepted, a.page_table = _ptr(kv_len), _ptr(accepted), _ptr(page_table)
+        _i32(k_per_row, (B,), "k_per_row", dev)
+        a.k_per_row = _ptr(k_per_row)
+        a.num_pages = int(num_pages)
+        if free_pages is not None:
+            _i32(free_pages, tuple(free_pages.shape), "free_pages", dev)
+            _i32(free_top, (1,), "free_top", dev)
+            a.free_pages, a.free_top = _ptr(free_pages), _ptr(free_top)
+            a.free_capacity = free_pages.numel()
+        self.workspace = None
+        if kv_pool is not None:
+            if kv_pool.dtype != torch.bfloat16 or not kv_pool.is_contiguous():
+                raise ValueError("kv_pool must be a contiguous bfloat16 tensor")
+            a.kv_pool = _ptr(kv_pool)
+            a.num_layers, a.kv_heads, a.head_dim = int(num_layers), int(kv_heads), int(head_dim)
+            if a.num_pages == 0:
+                a.num_pages = kv_pool.shape[0]
+            nbytes = library().sv_rollback_workspace_bytes(B)
+            self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
+        self.row_status = torch.empty(B, dtype=torch.int32, device=dev)
+        a.row_status = _ptr(self.row_status)
+        self._keep = (kv_len, accepted, page_table, k_per_row, free_pages, free_top, kv_pool)
+        self.args = a
+        self.device = dev
+        self._h = handle(dev)
+        self._ref = C.byref(a)
+
+    def run(self, stream=None):
+        rc = library().sv_kv_rollback(self._h, self._ref, _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_kv_rollback", rc)
+        return self.row_status
+
+
+def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
+                free_pages=None, free_top=None, kv_pool=None, num_pages=0, num_layers=0,
+                kv_heads=0, head_dim=0, stream=None):
+    """KV pointer / page-table rollback (sv_kv_rollback), in place on the
+    given device tensors.  Returns the row_status tensor."""
+    call = RollbackCall(kv_len, accepted, page_table, page_size, k_max, k_per_row, free_pages,
+                        free_top, kv_pool, num_pages, num_layers, kv_heads, head_dim)
+    return call.run(stream)

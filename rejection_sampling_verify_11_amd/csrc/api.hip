@@ -1,0 +1,330 @@
+// Host side of the specverify C ABI: argument validation, workspace sizing
+// and kernel launches on the caller's stream.  No device memory is
+// allocated, no stream is synchronised and nothing is copied back.
+#include <new>
+#include <string.h>
+#include <vector>
+
+#include "sv_internal.h"
+
+namespace {
+
+// Event pairs around kernel launches, read back on request.
+class EventTimer final : public sv::Timer {
+ public:
+  static constexpr size_t kMax = 4096;
+  ~EventTimer() override {
+    for (auto& e : pool_) {
+      hipEventDestroy(e.first);
+      hipEventDestroy(e.second);
+    }
+  }
+  void begin(const char* name, hipStream_t s) override {
+    if (used_ >= kMax) { cur_ = -1; return; }
+    if (used_ == pool_.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) { cur_ = -1; return; }
+      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); cur_ = -1; return; }
+      pool_.push_back({a, b});
+    }
+    cur_ = (long)used_++;
+    names_.resize(used_);
+    names_[cur_] = name;
+    hipEventRecord(pool_[cur_].first, s);
+  }
+  void end(hipStream_t s) override {
+    if (cur_ >= 0) hipEventRecord(pool_[cur_].second, s);
+    cur_ = -1;
+  }
+  int read(int max_entries, const char** names, int32_t* launches, double* total_ms) {
+    std::vector<const char*> un;
+    std::vector<int32_t> cnt;
+    std::vector<double> ms;
+    for (size_t i = 0; i < used_; ++i) {
+      float t = 0.f;
+      hipEventSynchronize(pool_[i].second);
+      if (hipEventElapsedTime(&t, pool_[i].first, pool_[i].second) != hipSuccess) t = 0.f;
+      size_t k = 0;
+      while (k < un.size() && strcmp(un[k], names_[i]) != 0) ++k;
+      if (k == un.size()) { un.push_back(names_[i]); cnt.push_back(0); ms.push_back(0.0); }
+      cnt[k] += 1;
+      ms[k] += t;
+    }
+    used_ = 0;
+    for (size_t k = 0; k < un.size() && (int)k < max_entries; ++k) {
+      if (names) names[k] = un[k];
+      if (launches) launches[k] = cnt[k];
+      if (total_ms) total_ms[k] = ms[k];
+    }
+    return (int)un.size();
+  }
+
+ private:
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool_;
+  std::vector<const char*> names_;
+  size_t used_ = 0;
+  long cur_ = -1;
+};
+
+}  // namespace
+
+struct sv_handle_s {
+  int device;
+  int num_cus;
+  char arch[64];
+  bool timing;
+  EventTimer* timer;
+  sv::Timer* active() { return timing ? timer : nullptr; }
+};
+
+namespace {
+
+constexpr int32_t kMaxVSampled = SV_MAX_V_SAMPLED;  // inverse-CDF segment table bound
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t sample_ws(int32_t B, int32_t K) {
+  return align_up((size_t)B * sv::slots_per_row(K) * sizeof(sv::VecRec), 256);
+}
+
+size_t greedy_ws(int32_t B, int32_t K, int32_t V) {
+  return align_up((size_t)B * (2 * (size_t)K + 1) * sv::greedy_chunks(V) * sizeof(sv::ArgmaxPart), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_E_ARG: return "invalid argument";
+    case SV_E_DTYPE: return "unsupported dtype";
+    case SV_E_WORKSPACE: return "workspace missing or too small";
+    case SV_E_DEVICE: return "HIP device or launch error";
+    case SV_E_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+sv_status sv_create(int hip_device, sv_handle* out) {
+  if (!out) return SV_E_ARG;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || hip_device < 0 || hip_device >= n) return SV_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) return SV_E_DEVICE;
+  sv_handle h = new (std::nothrow) sv_handle_s;
+  if (!h) return SV_E_INTERNAL;
+  h->device = hip_device;
+  h->timing = false;
+  h->timer = nullptr;
+  h->num_cus = prop.multiProcessorCount;
+  strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
+  h->arch[sizeof(h->arch) - 1] = 0;
+  *out = h;
+  return SV_OK;
+}
+
+sv_status sv_destroy(sv_handle h) {
+  if (h) delete h->timer;
+  delete h;
+  return SV_OK;
+}
+
+sv_status sv_timing_enable(sv_handle h, int on) {
+  if (!h) return SV_E_ARG;
+  if (on && !h->timer) {
+    h->timer = new (std::nothrow) EventTimer();
+    if (!h->timer) return SV_E_INTERNAL;
+  }
+  h->timing = on != 0;
+  return SV_OK;
+}
+
+int sv_timing_read(sv_handle h, int max_entries, const char** names, int32_t* launches,
+                   double* total_ms) {
+  if (!h || !h->timer) return 0;
+  return h->timer->read(max_entries, names, launches, total_ms);
+}
+
+size_t sv_verify_workspace_bytes(int32_t B, int32_t k_max, int32_t V, int32_t dtype,
+                                 uint32_t flags) {
+  (void)dtype;
+  (void)flags;
+  if (B < 0 || k_max < 1 || k_max > SV_MAX_K || V < 1) return 0;
+  const size_t a = sample_ws(B, k_max), g = greedy_ws(B, k_max, V);
+  const size_t n = a > g ? a : g;
+  return n > 0 ? n : 256;
+}
+
+sv_status sv_check_verify_args(const sv_verify_args* a, int mode) {
+  if (!a || mode < 0 || mode > 2) return SV_E_ARG;
+  if (a->B < 0 || a->k_max < 1 || a->k_max > SV_MAX_K || a->V < 1 || a->V > SV_MAX_V)
+    return SV_E_ARG;
+  if (a->dtype != SV_FP32 && a->dtype != SV_BF16) return SV_E_DTYPE;
+  if ((int64_t)a->B * (2 * a->k_max + 1) * sv::greedy_chunks(a->V) > 0x7FFFFFFFLL) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (mode != 1 && a->V > kMaxVSampled) return SV_E_ARG;
+  if (mode == 0) {
+    if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
+        !a->out_tokens || !a->accepted)
+      return SV_E_ARG;
+    if (a->target_vec_stride < a->V || a->draft_vec_stride < a->V) return SV_E_ARG;
+  } else if (mode == 1) {
+    if (!a->target_logits || !a->out_tokens || !a->accepted) return SV_E_ARG;
+    if (!a->draft_logits && !a->draft_tokens) return SV_E_ARG;
+    if (a->target_vec_stride < a->V) return SV_E_ARG;
+    if (a->draft_logits && a->draft_vec_stride < a->V) return SV_E_ARG;
+  } else {
+    if (!a->draft_logits || !a->draft_tokens || !a->temperature) return SV_E_ARG;
+    if (a->draft_vec_stride < a->V) return SV_E_ARG;
+  }
+  const size_t need = mode == 1 ? greedy_ws(a->B, a->k_max, a->V) : sample_ws(a->B, a->k_max);
+  if (!a->workspace || a->workspace_bytes < need) return SV_E_WORKSPACE;
+  return SV_OK;
+}
+
+static sv::StatsParams stats_params(const sv_verify_args* a, int mode) {
+  sv::StatsParams p;
+  p.target = a->target_logits;
+  p.draft = a->draft_logits;
+  p.t_stride = a->target_vec_stride;
+  p.d_stride = a->draft_vec_stride;
+  p.tokens = a->draft_tokens;
+  p.k_per_row = a->k_per_row;
+  p.temperature = a->temperature;
+  p.top_p = a->top_p;
+  p.B = a->B;
+  p.K = a->k_max;
+  p.V = a->V;
+  p.flags = a->flags;
+  p.mode = mode;
+  p.recs = (sv::VecRec*)a->workspace;
+  return p;
+}
+
+static sv::FinalizeParams finalize_params(const sv_verify_args* a) {
+  sv::FinalizeParams f;
+  f.target = a->target_logits;
+  f.draft = a->draft_logits;
+  f.t_stride = a->target_vec_stride;
+  f.d_stride = a->draft_vec_stride;
+  f.tokens = a->draft_tokens;
+  f.k_per_row = a->k_per_row;
+  f.temperature = a->temperature;
+  f.top_p = a->top_p;
+  f.B = a->B;
+  f.K = a->k_max;
+  f.V = a->V;
+  f.dtype = a->dtype;
+  f.flags = a->flags;
+  f.seed = a->seed;
+  f.offset = a->offset;
+  f.recs = (const sv::VecRec*)a->workspace;
+  f.out_tokens = a->out_tokens;
+  f.accepted = a->accepted;
+  f.num_emitted = a->num_emitted;
+  f.p_at_draft = a->p_at_draft;
+  f.q_at_draft = a->q_at_draft;
+  f.row_status = a->row_status;
+  f.draft_out = const_cast<int32_t*>(a->draft_tokens);
+  return f;
+}
+
+sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
+  const sv_status st = sv_check_verify_args(a, 0);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (sv::launch_stats(stats_params(a, 0), a->dtype, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_finalize_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
+  const sv_status st = sv_check_verify_args(a, 2);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (sv::launch_stats(stats_params(a, 1), a->dtype, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_draft_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s) {
+  const sv_status st = sv_check_verify_args(a, 1);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::GreedyParams g;
+  g.target = a->target_logits;
+  g.draft = a->draft_logits;
+  g.t_stride = a->target_vec_stride;
+  g.d_stride = a->draft_vec_stride;
+  g.tokens = a->draft_tokens;
+  g.k_per_row = a->k_per_row;
+  g.B = a->B;
+  g.K = a->k_max;
+  g.V = a->V;
+  g.dtype = a->dtype;
+  g.parts = (sv::ArgmaxPart*)a->workspace;
+  g.out_tokens = a->out_tokens;
+  g.accepted = a->accepted;
+  g.num_emitted = a->num_emitted;
+  g.row_status = a->row_status;
+  if (sv::launch_greedy(g, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+size_t sv_rollback_workspace_bytes(int32_t B) {
+  if (B < 0) return 0;
+  const size_t n = align_up((size_t)B * sizeof(sv::RollRec), 256);
+  return n > 0 ? n : 256;
+}
+
+sv_status sv_check_rollback_args(const sv_rollback_args* a) {
+  if (!a) return SV_E_ARG;
+  if (a->B < 0 || a->k_max < 1 || a->k_max > SV_MAX_K || a->page_size < 1 ||
+      a->max_pages_per_seq < 1 || a->num_pages < 0)
+    return SV_E_ARG;
+  if ((int64_t)a->page_size * a->max_pages_per_seq > 0x7FFFFFFFLL) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (!a->kv_len || !a->accepted || !a->page_table) return SV_E_ARG;
+  if (a->free_pages && (!a->free_top || a->free_capacity < 0)) return SV_E_ARG;
+  if (a->kv_pool) {
+    if (a->num_pages < 1 || a->num_layers < 1 || a->kv_heads < 1 || a->head_dim < 1) return SV_E_ARG;
+    if (!a->workspace || a->workspace_bytes < sv_rollback_workspace_bytes(a->B)) return SV_E_WORKSPACE;
+  }
+  return SV_OK;
+}
+
+sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) {
+  const sv_status st = sv_check_rollback_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::RollbackParams p;
+  p.B = a->B;
+  p.K = a->k_max;
+  p.ps = a->page_size;
+  p.MP = a->max_pages_per_seq;
+  p.kv_len = a->kv_len;
+  p.k_per_row = a->k_per_row;
+  p.accepted = a->accepted;
+  p.page_table = a->page_table;
+  p.num_pages = a->num_pages;
+  p.free_pages = a->free_pages;
+  p.free_top = a->free_top;
+  p.free_capacity = a->free_capacity;
+  p.kv_pool = (uint16_t*)a->kv_pool;
+  p.L = a->num_layers;
+  p.H = a->kv_heads;
+  p.D = a->head_dim;
+  p.row_status = a->row_status;
+  p.recs = (sv::RollRec*)a->workspace;
+  if (sv::launch_rollback(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,367 @@
+// Per-row decision of the sampled verification, and the inverse-CDF draws.
+//
+// One workgroup per row ([SD] §2.2, [SSD] §4.3 accept_or_reject):
+//   rho_i = p'_i(x_i) / q'_i(x_i) (0 when q'_i(x_i) = 0), taken from the
+//   per-vector records; accept while u(b,i,0) < rho_i; the first rejection a
+//   is followed by one draw from norm(max(0, p'_a - q'_a)) ([SSD] §2.4,
+//   §5.2; [SD] §2.1), or from p'_a when that residual is identically zero
+//   ([SSD] §4.3); if nothing is rejected the bonus comes from p'_{k_b}
+//   ([SD] §2.2).
+//
+// The draw is an inverse CDF in token-index order: y = min{j : C_j > u R},
+// C the inclusive prefix of r, R its total.  The vector is read in tiles of
+// 1024 x 8 contiguous logits (one 16-byte load per thread for bf16); each
+// wave owns a segment of 512 consecutive tokens per tile.  Pass 1 sums r per
+// segment (fp64); a scan over segments finds the one holding u R; pass 2
+// re-derives that segment's 512 values, scans them across lanes and picks
+// the token.  Probabilities are exp2 of fp32 arguments (v_exp_f32) scaled by
+// fp64 normalisers; all sums are fp64.
+#include <math.h>
+
+#include "philox.h"
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = kThreads * 8;   // logits per tile
+constexpr int kSeg = 512;             // logits per (tile, wave) segment
+constexpr int kMaxSeg = 4096;         // V <= 2^21 on this path
+
+struct Dist {
+  const void* vec;
+  float m, tau, c2;  // c2 = log2(e) / T
+  double inv;
+};
+
+// Loads 8 consecutive logits starting at j0 (elements >= V read as -inf).
+__device__ __forceinline__ void load8(const void* vec, int dtype, int64_t j0, int V,
+                                      bool aligned, float z[8]) {
+  if (aligned && j0 + 8 <= V) {
+    if (dtype == SV_BF16) {
+      const uint4 d = *(const uint4*)((const uint16_t*)vec + j0);
+      const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        z[2 * t] = __uint_as_float(w[t] << 16);
+        z[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 a = *(const float4*)((const float*)vec + j0);
+      const float4 b = *(const float4*)((const float*)vec + j0 + 4);
+      z[0] = a.x; z[1] = a.y; z[2] = a.z; z[3] = a.w;
+      z[4] = b.x; z[5] = b.y; z[6] = b.z; z[7] = b.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t j = j0 + t;
+    if (j >= V) { z[t] = -INFINITY; continue; }
+    z[t] = dtype == SV_BF16 ? __uint_as_float((uint32_t)((const uint16_t*)vec)[j] << 16)
+                            : ((const float*)vec)[j];
+  }
+}
+
+__device__ __forceinline__ double prob(const Dist& d, float z) {
+  if (!(z >= d.tau)) return 0.0;
+  return (double)__builtin_amdgcn_exp2f((z - d.m) * d.c2) * d.inv;
+}
+
+// r_j for the 8 logits at j0: residual max(0, p' - q') (mode 0) or p' (mode 1).
+__device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int dtype,
+                                   int64_t j0, int V, bool aligned, double r[8]) {
+  float zp[8], zq[8];
+  load8(P.vec, dtype, j0, V, aligned, zp);
+  if (mode == 0) load8(Q.vec, dtype, j0, V, aligned, zq);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const double pp = prob(P, zp[t]);
+    if (mode == 0) {
+      const double d = pp - prob(Q, zq[t]);
+      r[t] = d > 0.0 ? d : 0.0;
+    } else {
+      r[t] = pp;
+    }
+  }
+}
+
+struct CdfScratch {
+  double seg[kMaxSeg];
+  double wsum[kWaves];
+  double R;
+  int sstar;
+  int y;
+  double base;
+};
+
+__device__ __forceinline__ bool is_aligned16(const void* p) {
+  return (((uintptr_t)p) & 15u) == 0;
+}
+
+// Inverse CDF over one position, all threads of the block participate.
+// mode 0: residual of (P, Q), falling back to P if it is identically zero;
+// mode 1: P alone.  Returns y (same value in every thread), or -1 if the
+// distribution is empty.  *zero_residual reports the fallback.
+__device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
+                           CdfScratch& sc, bool* zero_residual) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int nseg = ntiles * kWaves;
+  const bool aligned = is_aligned16(P.vec) && (mode == 1 || is_aligned16(Q.vec));
+  *zero_residual = false;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // pass 1: per-segment sums
+    for (int s = 0; s < ntiles; ++s) {
+      const int64_t j0 = (int64_t)s * kTile + 8 * tid;
+      double r[8];
+      r8(P, Q, mode, dtype, j0, V, aligned, r);
+      double ls = 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ls += r[t];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+      if (l == 0) sc.seg[s * kWaves + w] = ls;
+    }
+    __syncthreads();
+    // exclusive scan over segments (in token order), one pass of 1024 at a time
+    double carry = 0.0;
+    for (int s0 = 0; s0 < nseg; s0 += kThreads) {
+      const int i = s0 + tid;
+      const double v = i < nseg ? sc.seg[i] : 0.0;
+      double inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(inc, o, 64);
+        if (l >= o) inc += t;
+      }
+      if (l == 63) sc.wsum[w] = inc;
+      __syncthreads();
+      double before = carry;
+      double tot = 0.0;
+      for (int k = 0; k < kWaves; ++k) {
+        if (k < w) before += sc.wsum[k];
+        tot += sc.wsum[k];
+      }
+      __syncthreads();
+      if (i < nseg) sc.seg[i] = before + (inc - v);  // exclusive prefix
+      carry += tot;
+    }
+    if (tid == 0) sc.R = carry;
+    __syncthreads();
+    const double R = sc.R;
+    if (mode == 0 && R == 0.0 && attempt == 0) {
+      mode = 1;
+      *zero_residual = true;
+      __syncthreads();
+      continue;
+    }
+    if (!(R > 0.0)) return -1;
+    const double target = u * R;
+    // segment holding the crossing: the last segment whose exclusive prefix
+    // is <= target and whose mass is positive
+    if (tid == 0) sc.sstar = -1;
+    __syncthreads();
+    for (int i = tid; i < nseg; i += kThreads) {
+      const double ex = sc.seg[i];
+      const double nx = i + 1 < nseg ? sc.seg[i + 1] : R;
+      if (ex <= target && nx > ex && nx > target) atomicMax(&sc.sstar, i);
+    }
+    __syncthreads();
+    int ss = sc.sstar;
+    if (ss < 0) {  // rounding edge: take the last segment with mass
+      if (tid == 0) {
+        for (int i = nseg - 1; i >= 0; --i) {
+          const double nx = i + 1 < nseg ? sc.seg[i + 1] : R;
+          if (nx > sc.seg[i]) { ss = i; break; }
+        }
+        sc.sstar = ss;
+      }
+      __syncthreads();
+      ss = sc.sstar;
+    }
+    if (ss < 0) ss = 0;  // R > 0 guarantees a segment with mass; stay in bounds regardless
+    // pass 2: wave 0 re-derives segment ss and finds the token
+    if (w == 0) {
+      const int st = ss / kWaves, sw = ss % kWaves;
+      const int64_t j0 = (int64_t)st * kTile + (int64_t)sw * kSeg + 8 * l;
+      double r[8];
+      r8(P, Q, mode, dtype, j0, V, aligned, r);
+      double ls = 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ls += r[t];
+      double inc = ls;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(inc, o, 64);
+        if (l >= o) inc += t;
+      }
+      double exl = __shfl_up(inc, 1, 64);
+      if (l == 0) exl = 0.0;
+      const double base = sc.seg[ss] + exl;
+      int hit = 0x7FFFFFFF, lastpos = -1;
+      double loc = 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        loc += r[t];
+        if (r[t] > 0.0) {
+          lastpos = (int)(j0 + t);
+          if (hit == 0x7FFFFFFF && base + loc > target) hit = (int)(j0 + t);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        hit = min(hit, __shfl_xor(hit, o, 64));
+        lastpos = max(lastpos, __shfl_xor(lastpos, o, 64));
+      }
+      if (l == 0) sc.y = hit != 0x7FFFFFFF ? hit : lastpos;
+    }
+    __syncthreads();
+    return sc.y;
+  }
+  return -1;
+}
+
+__device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, int dtype,
+                          const VecRec& rec, float T) {
+  Dist d;
+  d.vec = (const char*)base + vec_index * stride * (dtype == SV_BF16 ? 2 : 4);
+  d.m = rec.m;
+  d.tau = rec.tau;
+  d.c2 = (float)(1.4426950408889634 / (double)T);
+  d.inv = rec.inv_kept;
+  return d;
+}
+
+struct RowShared {
+  int kb, acc, mode, go;
+  uint32_t status;
+  float T;
+  double u1;
+};
+
+__global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParams p) {
+  __shared__ CdfScratch sc;
+  __shared__ RowShared rs;
+  const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
+  const int per = slots_per_row(K);
+  const VecRec* recs = p.recs + (int64_t)b * per;
+  if (tid == 0) {
+    uint32_t st = 0;
+    const int kb = p.k_per_row ? p.k_per_row[b] : K;
+    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
+    const float T = p.temperature[b];
+    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
+    const float P = p.top_p ? p.top_p[b] : 1.0f;
+    if (isnan(P) || P <= 0.0f) st |= SV_ROW_BAD_TOP_P;
+    int acc = 0;
+    if (!(st & SV_ROW_BAD_K)) {
+      for (int i = 0; i < kb; ++i) {
+        const int x = p.tokens[(int64_t)b * K + i];
+        if (x < 0 || x >= V) st |= SV_ROW_BAD_TOKEN;
+      }
+      for (int i = 0; i <= kb; ++i) st |= recs[i].status;
+      for (int i = 0; i < kb; ++i) st |= recs[K + 1 + i].status;
+    }
+    if (!st) {
+      // left-to-right chain with early stop
+      acc = kb;
+      for (int i = 0; i < kb; ++i) {
+        const double px = recs[i].px, qx = recs[K + 1 + i].px;
+        const double rho = qx > 0.0 ? px / qx : 0.0;
+        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 0, p.offset);
+        if (!(u < rho)) { acc = i; break; }
+      }
+      for (int i = 0; i < K; ++i) {
+        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + i] = i < kb ? (float)recs[i].px : 0.0f;
+        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + i] = i < kb ? (float)recs[K + 1 + i].px : 0.0f;
+      }
+    } else {
+      for (int j = 0; j <= K; ++j) p.out_tokens[(int64_t)b * (K + 1) + j] = -1;
+      p.accepted[b] = -1;
+      if (p.num_emitted) p.num_emitted[b] = 0;
+      for (int i = 0; i < K; ++i) {
+        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + i] = NAN;
+        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + i] = NAN;
+      }
+      if (p.row_status) p.row_status[b] = (int32_t)st;
+    }
+    rs.kb = kb;
+    rs.acc = acc;
+    rs.go = st == 0;
+    rs.status = st;
+    rs.T = T;
+    rs.mode = acc < kb ? 0 : 1;
+    rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, p.offset);
+  }
+  __syncthreads();
+  if (!rs.go) return;
+  const int kb = rs.kb, acc = rs.acc, mode = rs.mode;
+  const Dist P = make_dist(p.target, (int64_t)b * (K + 1) + acc, p.t_stride, p.dtype, recs[acc], rs.T);
+  Dist Q = P;
+  if (mode == 0) Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, recs[K + 1 + acc], rs.T);
+  bool zero = false;
+  const int y = inverse_cdf(P, Q, mode, p.dtype, V, rs.u1, sc, &zero);
+  if (tid == 0) {
+    int32_t* out = p.out_tokens + (int64_t)b * (K + 1);
+    for (int j = 0; j <= K; ++j) out[j] = -1;
+    for (int i = 0; i < acc; ++i) out[i] = p.tokens[(int64_t)b * K + i];
+    out[acc] = y;
+    p.accepted[b] = acc;
+    if (p.num_emitted) p.num_emitted[b] = acc + 1;
+    if (p.row_status) p.row_status[b] = 0;
+  }
+}
+
+// Draft sampling: one workgroup per (row, draft position).
+__global__ __launch_bounds__(kThreads) void draft_sample_kernel(FinalizeParams p) {
+  __shared__ CdfScratch sc;
+  __shared__ int go;
+  __shared__ float Ts;
+  const int b = blockIdx.x / p.K, i = blockIdx.x % p.K, K = p.K, tid = threadIdx.x;
+  const int per = slots_per_row(K);
+  const VecRec* recs = p.recs + (int64_t)b * per;
+  if (tid == 0) {
+    uint32_t st = 0;
+    const int kb = p.k_per_row ? p.k_per_row[b] : K;
+    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
+    const float T = p.temperature[b];
+    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
+    const float P = p.top_p ? p.top_p[b] : 1.0f;
+    if (isnan(P) || P <= 0.0f) st |= SV_ROW_BAD_TOP_P;
+    if (!(st & SV_ROW_BAD_K))
+      for (int j = 0; j < kb; ++j) st |= recs[K + 1 + j].status;
+    // every workgroup of the row sees the same status; position 0 reports it
+    if (i == 0 && p.row_status) p.row_status[b] = (int32_t)st;
+    go = (st == 0 && i < kb) ? 1 : 0;
+    if (!go) p.draft_out[(int64_t)b * K + i] = -1;
+    Ts = T;
+  }
+  __syncthreads();
+  if (!go) return;
+  const Dist Q = make_dist(p.draft, (int64_t)b * K + i, p.d_stride, p.dtype, recs[K + 1 + i], Ts);
+  bool zero = false;
+  const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 2, p.offset);
+  const int y = inverse_cdf(Q, Q, 1, p.dtype, p.V, u, sc, &zero);
+  if (tid == 0) p.draft_out[(int64_t)b * K + i] = y;
+}
+
+}  // namespace
+
+hipError_t launch_finalize_sample(const FinalizeParams& p, hipStream_t s, Timer* t) {
+  if (p.B == 0) return hipSuccess;
+  TimedScope ts(t, "finalize_sample", s);
+  hipLaunchKernelGGL(finalize_sample_kernel, dim3(p.B), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_sample(const FinalizeParams& p, hipStream_t s, Timer* t) {
+  if (p.B == 0) return hipSuccess;
+  TimedScope ts(t, "draft_sample", s);
+  hipLaunchKernelGGL(draft_sample_kernel, dim3((unsigned)p.B * (unsigned)p.K), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sv

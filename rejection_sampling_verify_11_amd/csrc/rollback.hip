@@ -1,0 +1,217 @@
+// KV write-pointer and page-table rollback after verification.
+//
+// [SSD] §3.3 and §4.3: the KV written for rejected drafts must be dropped by
+// moving the write pointer back to the accepted prefix ("seq_len + i"), and
+// the pointer must equal the sequence length after every rollback; with a
+// paged cache the position -> page map is separate and rollback works at
+// page granularity.  [SSD] §4.5: ragged acceptance needs one offset per
+// sequence.  [SD] §4.3: with a preallocated slot per request only the valid
+// length shrinks.
+//
+// One workgroup walks the rows in tiles of 1024: per-row checks, the new
+// length, the number of whole pages released, and an exclusive scan of the
+// releases (valid rows only) that gives every row its slots on the free
+// stack in (row, page) order.  A row whose releases would pass the stack
+// capacity is flagged and left unchanged.  With a KV pool the decision is
+// written to the workspace first, a second kernel poisons the rolled-back
+// slots while the page table still maps them, and a third commits.
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ int ceil_div(int x, int d) { return (x + d - 1) / d; }
+
+struct Decision {
+  uint32_t st;
+  int new_len, old_len, nrel;
+};
+
+__device__ Decision decide_row(const RollbackParams& p, int b) {
+  Decision d;
+  d.st = 0;
+  d.nrel = 0;
+  const int k = p.k_per_row ? p.k_per_row[b] : p.K;
+  const int acc = p.accepted[b];
+  const int old = p.kv_len[b];
+  d.old_len = old;
+  d.new_len = old;
+  if (k < 1 || k > p.K) d.st |= SV_ROW_BAD_K;
+  else if (acc < 0 || acc > k || old - (k - acc) < 0) d.st |= SV_ROW_BAD_ACCEPTED;
+  if (old < 0 || ceil_div(old, p.ps) > p.MP) d.st |= SV_ROW_BAD_PAGES;
+  if (!d.st) {
+    const int used = ceil_div(old, p.ps);
+    const int32_t* row = p.page_table + (int64_t)b * p.MP;
+    for (int pg = 0; pg < p.MP; ++pg) {
+      const int e = row[pg];
+      if (pg < used ? (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) : (e != -1)) {
+        d.st |= SV_ROW_BAD_PAGES;
+        break;
+      }
+    }
+  }
+  if (!d.st) {
+    d.new_len = old - (k - acc);
+    d.nrel = ceil_div(old, p.ps) - ceil_div(d.new_len, p.ps);
+  }
+  return d;
+}
+
+// phase 0: decide and commit; phase 1: decide into p.recs only.
+__global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, int phase) {
+  __shared__ int wsum[kWaves];
+  __shared__ int wmax[kWaves];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int top0 = p.free_pages ? p.free_top[0] : 0;
+  int carry = 0;     // releases of valid rows before this tile
+  int pushed = 0;    // running total at the last committed row that released
+  for (int t0 = 0; t0 < p.B; t0 += kThreads) {
+    const int b = t0 + tid;
+    Decision d;
+    d.st = 0; d.nrel = 0; d.new_len = 0; d.old_len = 0;
+    if (b < p.B) d = decide_row(p, b);
+    const int rel = (b < p.B && !d.st) ? d.nrel : 0;
+    // inclusive scan of rel across the block
+    int inc = rel;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (l >= o) inc += v;
+    }
+    if (l == 63) wsum[w] = inc;
+    __syncthreads();
+    int before = carry, tot = 0;
+    for (int k = 0; k < kWaves; ++k) {
+      if (k < w) before += wsum[k];
+      tot += wsum[k];
+    }
+    __syncthreads();
+    const int running = before + inc;  // inclusive, over valid rows
+    if (b < p.B && !d.st && p.free_pages && rel > 0 &&
+        (top0 < 0 || (int64_t)top0 + running > (int64_t)p.free_capacity))
+      d.st |= SV_ROW_FREE_OVERFLOW;
+    const bool commit = b < p.B && !d.st;
+    const int push_base = top0 + running - rel;
+    int my_pushed = (commit && p.free_pages && rel > 0) ? running : 0;
+    if (phase == 1) {
+      if (b < p.B) {
+        RollRec r;
+        r.committed = commit ? 1 : 0;
+        r.new_len = d.new_len;
+        r.old_len = d.old_len;
+        r.push_base = push_base;
+        p.recs[b] = r;
+        if (p.row_status) p.row_status[b] = (int32_t)d.st;
+      }
+    } else {
+      if (commit) {
+        int32_t* row = p.page_table + (int64_t)b * p.MP;
+        if (p.free_pages) {
+          const int first = ceil_div(d.new_len, p.ps);
+          for (int j = 0; j < rel; ++j) {
+            p.free_pages[push_base + j] = row[first + j];
+            row[first + j] = -1;
+          }
+        }
+        p.kv_len[b] = d.new_len;
+      }
+      if (b < p.B && p.row_status) p.row_status[b] = (int32_t)d.st;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) my_pushed = max(my_pushed, __shfl_xor(my_pushed, o, 64));
+    if (l == 0) wmax[w] = my_pushed;
+    __syncthreads();
+    for (int k = 0; k < kWaves; ++k) pushed = max(pushed, wmax[k]);
+    __syncthreads();
+    carry += tot;
+  }
+  if (phase == 0 && tid == 0 && p.free_pages) p.free_top[0] = top0 + pushed;
+}
+
+// Commit from recorded decisions (after poisoning).
+__global__ __launch_bounds__(kThreads) void rollback_commit_kernel(RollbackParams p) {
+  __shared__ int wmax[kWaves];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int top0 = p.free_pages ? p.free_top[0] : 0;
+  int pushed = 0;
+  for (int t0 = 0; t0 < p.B; t0 += kThreads) {
+    const int b = t0 + tid;
+    int my_pushed = 0;
+    if (b < p.B) {
+      const RollRec r = p.recs[b];
+      if (r.committed) {
+        int32_t* row = p.page_table + (int64_t)b * p.MP;
+        if (p.free_pages) {
+          const int first = ceil_div(r.new_len, p.ps);
+          const int rel = ceil_div(r.old_len, p.ps) - first;
+          for (int j = 0; j < rel; ++j) {
+            p.free_pages[r.push_base + j] = row[first + j];
+            row[first + j] = -1;
+          }
+          if (rel > 0) my_pushed = r.push_base + rel - top0;
+        }
+        p.kv_len[b] = r.new_len;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) my_pushed = max(my_pushed, __shfl_xor(my_pushed, o, 64));
+    if (l == 0) wmax[w] = my_pushed;
+    __syncthreads();
+    for (int k = 0; k < kWaves; ++k) pushed = max(pushed, wmax[k]);
+    __syncthreads();
+  }
+  if (tid == 0 && p.free_pages) p.free_top[0] = top0 + pushed;
+}
+
+// One workgroup per (row, layer): overwrite the rolled-back slots with the
+// poison pattern.  Pool layout [page][layer][K|V][head][slot][dim].
+__global__ __launch_bounds__(256) void poison_kernel(RollbackParams p) {
+  const int b = blockIdx.x / p.L, layer = blockIdx.x % p.L;
+  const RollRec r = p.recs[b];
+  if (!r.committed) return;
+  const int nslots = r.old_len - r.new_len;
+  const int per_slot = 2 * p.H * p.D;
+  const int32_t* row = p.page_table + (int64_t)b * p.MP;
+  for (int e = threadIdx.x; e < nslots * per_slot; e += blockDim.x) {
+    const int s = e / per_slot, rem = e % per_slot;
+    const int kvh = rem / p.D, dim = rem % p.D;  // kvh = kv * H + head
+    const int pos = r.new_len + s;
+    const int page = row[pos / p.ps];
+    const int64_t off =
+        ((((int64_t)page * p.L + layer) * 2 * p.H + kvh) * p.ps + pos % p.ps) * p.D + dim;
+    p.kv_pool[off] = (uint16_t)SV_POISON_BF16;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t) {
+  if (p.B == 0) return hipSuccess;
+  if (!p.kv_pool) {
+    TimedScope ts(t, "rollback", s);
+    hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 0);
+    return hipGetLastError();
+  }
+  {
+    TimedScope ts(t, "rollback_decide", s);
+    hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 1);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.L > 0 && p.H > 0 && p.D > 0) {
+    TimedScope ts(t, "rollback_poison", s);
+    hipLaunchKernelGGL(poison_kernel, dim3((unsigned)p.B * (unsigned)p.L), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    TimedScope ts(t, "rollback_commit", s);
+    hipLaunchKernelGGL(rollback_commit_kernel, dim3(1), dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

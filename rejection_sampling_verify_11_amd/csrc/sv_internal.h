@@ -1,0 +1,142 @@
+// Internal definitions shared by the host library and the HIP kernels of
+// specverify.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+// Per-vector statistics written by the stats kernels and read by the
+// finalize kernel.  One record per (row, side, position) slot.
+struct VecRec {
+  float m;          // largest finite raw logit of the vector
+  float tau;        // smallest kept raw logit (-inf when nothing is cut)
+  double inv_kept;  // 1 / sum over kept j of exp((z_j - m) / T)
+  double px;        // p'(x) (or q'(x)) of the vector's draft token, 0 if none
+  uint32_t status;  // SV_ROW_* bits found in this vector
+  uint32_t pad;
+};
+static_assert(sizeof(VecRec) == 32, "VecRec layout");
+
+// Greedy argmax partial of one chunk of one vector.
+struct ArgmaxPart {
+  float value;
+  int32_t index;    // -1 if the chunk held no comparable value
+  uint32_t status;  // NONFINITE bit; bit 31 set if any finite entry was seen
+  uint32_t pad;
+};
+static_assert(sizeof(ArgmaxPart) == 16, "ArgmaxPart layout");
+constexpr uint32_t kSawFinite = 1u << 31;
+
+// Rollback decision per row, used when the pool is poisoned.
+struct RollRec {
+  int32_t committed;  // 1 if the row is rolled back
+  int32_t new_len;
+  int32_t old_len;
+  int32_t push_base;  // index on the free stack of the row's first release
+};
+static_assert(sizeof(RollRec) == 16, "RollRec layout");
+
+// Vector slots of one row: target positions 0..K, then draft positions 0..K-1.
+inline __host__ __device__ int slots_per_row(int K) { return 2 * K + 1; }
+
+// Greedy chunking of a vector over several workgroups.
+constexpr int kGreedyChunk = 16384;
+inline __host__ __device__ int greedy_chunks(int V) { return (V + kGreedyChunk - 1) / kGreedyChunk; }
+
+struct StatsParams {
+  const void* target;
+  const void* draft;
+  int64_t t_stride, d_stride;
+  const int32_t* tokens;
+  const int32_t* k_per_row;
+  const float* temperature;
+  const float* top_p;
+  int32_t B, K, V;
+  uint32_t flags;
+  int32_t mode;  // 0 verification (all slots), 1 draft sampling (draft slots only)
+  VecRec* recs;
+};
+
+struct FinalizeParams {
+  const void* target;
+  const void* draft;
+  int64_t t_stride, d_stride;
+  const int32_t* tokens;
+  const int32_t* k_per_row;
+  const float* temperature;
+  const float* top_p;
+  int32_t B, K, V, dtype;
+  uint32_t flags;
+  uint64_t seed, offset;
+  const VecRec* recs;
+  int32_t* out_tokens;
+  int32_t* accepted;
+  int32_t* num_emitted;
+  float* p_at_draft;
+  float* q_at_draft;
+  int32_t* row_status;
+  int32_t* draft_out;  // draft sampling mode: tokens written here
+};
+
+struct GreedyParams {
+  const void* target;
+  const void* draft;  // may be null
+  int64_t t_stride, d_stride;
+  const int32_t* tokens;
+  const int32_t* k_per_row;
+  int32_t B, K, V, dtype;
+  ArgmaxPart* parts;
+  int32_t* out_tokens;
+  int32_t* accepted;
+  int32_t* num_emitted;
+  int32_t* row_status;
+};
+
+struct RollbackParams {
+  int32_t B, K, ps, MP;
+  int32_t* kv_len;
+  const int32_t* k_per_row;
+  const int32_t* accepted;
+  int32_t* page_table;
+  int32_t num_pages;
+  int32_t* free_pages;
+  int32_t* free_top;
+  int32_t free_capacity;
+  uint16_t* kv_pool;
+  int32_t L, H, D;
+  int32_t* row_status;
+  RollRec* recs;
+};
+
+// Optional event bracketing of each launch (see sv_timing_enable).
+class Timer {
+ public:
+  virtual ~Timer() {}
+  virtual void begin(const char* name, hipStream_t s) = 0;
+  virtual void end(hipStream_t s) = 0;
+};
+
+struct TimedScope {
+  Timer* t;
+  hipStream_t s;
+  TimedScope(Timer* t_, const char* name, hipStream_t s_) : t(t_), s(s_) {
+    if (t) t->begin(name, s);
+  }
+  ~TimedScope() {
+    if (t) t->end(s);
+  }
+};
+
+// Launchers (each returns hipGetLastError() of its launch(es)).
+hipError_t launch_stats(const StatsParams& p, int dtype, hipStream_t s, Timer* t);
+hipError_t launch_finalize_sample(const FinalizeParams& p, hipStream_t s, Timer* t);
+hipError_t launch_draft_sample(const FinalizeParams& p, hipStream_t s, Timer* t);
+hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
+hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
+
+}  // namespace sv

@@ -1,0 +1,165 @@
+"""The C ABI on the CPU: the built library loads, exports every entry point
+that include/specverify.h declares, its argument blocks have the layout the
+ctypes binding assumes, and host-side validation rejects bad arguments before
+any HIP call (none of these tests needs a GPU)."""
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from rejection_sampling_verify_11_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.library()
+    names = declared_functions()
+    assert len(names) >= 11
+    assert sorted(_abi.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (sv_\w+)", out))
+    assert set(names) <= exported
+
+
+def _c_layout(struct, fields):
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "specverify.h"',
+           "int main(void){"]
+    src.append('printf("%%zu\\n", sizeof(%s));' % struct)
+    for f in fields:
+        src.append('printf("%%zu\\n", offsetof(%s, %s));' % (struct, f))
+    src.append("return 0;}")
+    d = tempfile.mkdtemp()
+    c = os.path.join(d, "l.c")
+    open(c, "w").write("\n".join(src))
+    exe = os.path.join(d, "l")
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I" + os.path.dirname(HEADER), c, "-o", exe], check=True)
+    vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("cls,cname", [(_abi.VerifyArgs, "sv_verify_args"),
+                                       (_abi.RollbackArgs, "sv_rollback_args")])
+def test_argument_block_layout_matches_header(cls, cname):
+    fields = [f[0] for f in cls._fields_]
+    size, offs = _c_layout(cname, fields)
+    assert size == C.sizeof(cls)
+    assert offs == [getattr(cls, f).offset for f in fields]
+
+
+def good_args(B=4, K=3, V=1000, dtype=_abi.SV_BF16):
+    a = _abi.VerifyArgs()
+    a.B, a.k_max, a.V, a.dtype = B, K, V, dtype
+    fake = 0x10000  # never dereferenced: validation only looks at the values
+    a.target_logits = a.draft_logits = a.draft_tokens = a.temperature = fake
+    a.out_tokens = a.accepted = fake
+    a.target_vec_stride = a.draft_vec_stride = V
+    a.workspace = fake
+    a.workspace_bytes = _abi.library().sv_verify_workspace_bytes(B, K, V, dtype, 0)
+    return a
+
+
+def check(a, mode=0):
+    return _abi.library().sv_check_verify_args(C.byref(a), mode)
+
+
+def test_valid_arguments_pass():
+    for mode in (0, 1, 2):
+        assert check(good_args(), mode) == _abi.SV_OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", -1, _abi.SV_E_ARG),
+    ("k_max", 0, _abi.SV_E_ARG),
+    ("k_max", 33, _abi.SV_E_ARG),
+    ("V", 0, _abi.SV_E_ARG),
+    ("V", (1 << 21) + 1, _abi.SV_E_ARG),
+    ("dtype", 7, _abi.SV_E_DTYPE),
+    ("target_logits", None, _abi.SV_E_ARG),
+    ("draft_logits", None, _abi.SV_E_ARG),
+    ("draft_tokens", None, _abi.SV_E_ARG),
+    ("temperature", None, _abi.SV_E_ARG),
+    ("out_tokens", None, _abi.SV_E_ARG),
+    ("accepted", None, _abi.SV_E_ARG),
+    ("target_vec_stride", 999, _abi.SV_E_ARG),
+    ("draft_vec_stride", 10, _abi.SV_E_ARG),
+    ("workspace", None, _abi.SV_E_WORKSPACE),
+    ("workspace_bytes", 16, _abi.SV_E_WORKSPACE),
+])
+def test_sampled_validation(field, value, code):
+    a = good_args()
+    setattr(a, field, value)
+    assert check(a, 0) == code
+
+
+def test_greedy_validation_and_limits():
+    a = good_args()
+    a.draft_logits = None
+    assert check(a, 1) == _abi.SV_OK          # draft tokens alone are enough
+    a.draft_tokens = None
+    assert check(a, 1) == _abi.SV_E_ARG       # neither tokens nor logits
+    b = good_args(V=(1 << 21) + 5)
+    b.workspace_bytes = _abi.library().sv_verify_workspace_bytes(4, 3, (1 << 21) + 5, 1, 0)
+    assert check(b, 1) == _abi.SV_OK          # greedy allows larger V
+    assert check(b, 0) == _abi.SV_E_ARG
+
+
+def test_entry_points_validate_before_touching_the_device():
+    L = _abi.library()
+    a = good_args()
+    a.V = 0
+    for fn in (L.sv_verify_sample, L.sv_verify_greedy, L.sv_draft_sample):
+        assert fn(None, C.byref(a), None) == _abi.SV_E_ARG
+    a = good_args()
+    assert L.sv_verify_sample(None, C.byref(a), None) == _abi.SV_E_ARG  # no handle
+    e = _abi.VerifyArgs()  # an empty batch needs no buffers at all
+    e.B, e.k_max, e.V, e.dtype = 0, 4, 100, _abi.SV_BF16
+    assert check(e, 0) == _abi.SV_OK
+    assert L.sv_verify_sample(None, C.byref(e), None) == _abi.SV_E_ARG  # but a handle
+
+
+def test_workspace_sizes():
+    L = _abi.library()
+    n = L.sv_verify_workspace_bytes(256, 6, 151936, 1, 0)
+    assert n >= 256 * 13 * 32 and n % 256 == 0
+    assert L.sv_verify_workspace_bytes(0, 6, 100, 1, 0) > 0
+    assert L.sv_verify_workspace_bytes(1, 0, 100, 1, 0) == 0
+    assert L.sv_rollback_workspace_bytes(64) >= 64 * 16
+
+
+def test_rollback_validation():
+    L = _abi.library()
+    a = _abi.RollbackArgs()
+    a.B, a.k_max, a.page_size, a.max_pages_per_seq = 4, 8, 16, 10
+    a.kv_len = a.accepted = a.page_table = 0x10000
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_OK
+    a.kv_pool = 0x10000
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG  # pool without sizes
+    a.num_pages, a.num_layers, a.kv_heads, a.head_dim = 10, 2, 2, 8
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_WORKSPACE
+    a.workspace, a.workspace_bytes = 0x10000, L.sv_rollback_workspace_bytes(4)
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_OK
+    a.free_pages = 0x10000
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG  # stack without height
+    a.page_size = 0
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG
+
+
+def test_status_strings():
+    for code in range(6):
+        assert _abi.status_string(code)
