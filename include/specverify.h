@@ -66,7 +66,11 @@ typedef enum { SV_FP32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_ROW_BAD_K           (1u << 3) /* k_b outside [1, k_max]               */
 #define SV_ROW_BAD_TEMPERATURE (1u << 4) /* T <= 0 or not finite                 */
 #define SV_ROW_BAD_TOP_P       (1u << 5) /* top_p <= 0 or NaN                    */
-#define SV_ROW_BAD_PAGES       (1u << 6) /* page table inconsistent with kv_len  */
+#define SV_ROW_BAD_PAGES       (1u << 6) /* page table inconsistent with kv_len:
+                                            a page holding a rolled-back
+                                            position unmapped (or past the
+                                            pool), or the entry just past the
+                                            old length mapped                 */
 #define SV_ROW_FREE_OVERFLOW   (1u << 7) /* released pages do not fit the stack  */
 #define SV_ROW_BAD_ACCEPTED    (1u << 8) /* accepted outside [0, k_b] (e.g. -1
                                             from a flagged verify) or a length

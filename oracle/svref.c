@@ -558,12 +558,16 @@ int svref_kv_rollback(const svref_rollback_args* a) {
     else if (acc < 0 || acc > k || old - (k - acc) < 0) st[b] |= SVREF_ROW_BAD_ACCEPTED;
     if (old < 0 || ceil_div(old, ps) > MP) st[b] |= SVREF_ROW_BAD_PAGES;
     if (!st[b]) {
+      /* Consistency of the table with the length, where the rollback acts:
+       * every page holding a position in [new, old) is mapped (to a page of
+       * the pool), and the first entry past the old length is unmapped. */
+      int32_t nl = old - (k - acc);
       int32_t used = ceil_div(old, ps);
-      for (int32_t pg = 0; pg < MP; ++pg) {
+      for (int32_t pg = nl / ps; pg < used; ++pg) {
         int32_t e = a->page_table[(int64_t)b * MP + pg];
-        int bad_map = e < 0 || (a->num_pages > 0 && e >= a->num_pages);
-        if (pg < used ? bad_map : (e != -1)) st[b] |= SVREF_ROW_BAD_PAGES;
+        if (e < 0 || (a->num_pages > 0 && e >= a->num_pages)) st[b] |= SVREF_ROW_BAD_PAGES;
       }
+      if (used < MP && a->page_table[(int64_t)b * MP + used] != -1) st[b] |= SVREF_ROW_BAD_PAGES;
     }
     if (!st[b]) {
       newlen[b] = old - (k - acc);

@@ -237,7 +237,7 @@ sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
-  if (sv::launch_stats(stats_params(a, 0), a->dtype, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_stats(stats_params(a, 0), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
   if (sv::launch_finalize_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
 }
@@ -247,7 +247,7 @@ sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
-  if (sv::launch_stats(stats_params(a, 1), a->dtype, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_stats(stats_params(a, 1), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
   if (sv::launch_draft_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
 }

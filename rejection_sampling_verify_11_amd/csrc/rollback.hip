@@ -43,15 +43,16 @@ __device__ Decision decide_row(const RollbackParams& p, int b) {
   else if (acc < 0 || acc > k || old - (k - acc) < 0) d.st |= SV_ROW_BAD_ACCEPTED;
   if (old < 0 || ceil_div(old, p.ps) > p.MP) d.st |= SV_ROW_BAD_PAGES;
   if (!d.st) {
+    // the pages holding the rolled-back positions must be mapped, and the
+    // first entry past the old length must be unmapped
+    const int nl = old - (k - acc);
     const int used = ceil_div(old, p.ps);
     const int32_t* row = p.page_table + (int64_t)b * p.MP;
-    for (int pg = 0; pg < p.MP; ++pg) {
+    for (int pg = nl / p.ps; pg < used; ++pg) {
       const int e = row[pg];
-      if (pg < used ? (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) : (e != -1)) {
-        d.st |= SV_ROW_BAD_PAGES;
-        break;
-      }
+      if (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) d.st |= SV_ROW_BAD_PAGES;
     }
+    if (used < p.MP && row[used] != -1) d.st |= SV_ROW_BAD_PAGES;
   }
   if (!d.st) {
     d.new_len = old - (k - acc);

@@ -9,17 +9,24 @@
 // tie-closed: keep j iff the mass of strictly larger logits is below top_p,
 // i.e. keep {j : z_j >= tau} for the lowest kept value tau.
 //
-// bf16 path (one workgroup of 1024 threads per vector, one pass over HBM):
-// a bf16 logit has only 2^16 possible values, so an exact count of each
-// value determines everything: m is the largest value present, the
-// normaliser is sum_v count(v) * exp((v - m)/T), and the top-p threshold is
-// found by walking values downwards until the cumulative mass reaches
-// top_p * S.  The streaming loop therefore does integer work only (one LDS
-// atomic per logit); the exp()s are taken per distinct value afterwards, in
-// fp64.  Two 16-bit counts share one LDS word: value bits & 0x7FFF select the
-// word, the sign bit selects the half.  A count can only wrap if 65536 or
-// more logits of one vector are bit-identical; the sum of all stored counts
-// then differs from V, which sends the vector down the generic path.
+// bf16 path.  A bf16 logit has only 2^16 possible values, so an exact count
+// of each value determines everything: m is the largest value present, the
+// normaliser is sum_v count(v) exp((v - m)/T), and the top-p threshold is
+// found by walking values downwards until the mass reaches top_p * S.  The
+// streaming loop therefore does integer work only (one LDS atomic per
+// logit) and the exp()s are taken once per distinct value.  Two 16-bit
+// counts share an LDS word: the low 15 bits of the value select the word,
+// the sign bit the half.  A count can only wrap if 65536 or more logits of
+// one vector are bit-identical; the sum of all stored counts then differs
+// from V, which sends that vector down the generic path.
+//
+// The kernel is persistent: one 1024-thread workgroup per CU (the 132 KB
+// count table fills the CU's LDS) walks its share of the vectors.  Per
+// vector: stream the logits into the table; each thread reads and clears
+// its 32 words (the table is then ready for the next vector); the distinct
+// values are compacted into a list in ascending order; masses are formed
+// per list entry (fp32 exp2, fp64 sums) and scanned; the thread whose run
+// holds top_p * S resolves the threshold exactly.
 //
 // Generic path (fp32 logits, or a bf16 vector whose counts wrapped): passes
 // over the vector in global memory: max, fp64 sum, then a 4-pass radix select
@@ -27,6 +34,7 @@
 #include <math.h>
 
 #include "sv_internal.h"
+#include "wave_ops.h"
 
 namespace sv {
 namespace {
@@ -34,18 +42,21 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kHistWords = 32768;
-// One pad word per 64 words, so that 64 lanes reading word i of 64
-// consecutive 64-word blocks hit 64 different banks.
-constexpr int kHistPhys = kHistWords + kHistWords / 64;
+// Fixed-point scale of value masses: a mass is at most 65535 (count) and a
+// vector's total at most V < 2^18, so sums stay below 2^63; one unit is
+// 2^-45 of the largest value's weight.
+constexpr double kFixScale = 35184372088832.0;  // 2^45
+// Distinct finite values listed per vector; a vector with more (none of the
+// workloads comes close: they hold 270..2900) takes the generic path.  Sized
+// to what is left of the CU's 160 KB of LDS.
+constexpr int kListCap = 7000;
 
-__device__ __forceinline__ uint32_t hist_phys(uint32_t word) { return word + (word >> 6); }
 
 // Rank order of bf16 values: rank r in [0, 65536).  r >= 32768 holds the
 // non-negative key r - 32768; r < 32768 holds the negative key
 // 0x8000 | (32767 - r).  Ranks [128, 65407] are finite, 127 is -inf, 65408 is
 // +inf, the rest are NaN.
-constexpr int kRankNegInf = 127;
-constexpr int kRankPosInf = 65408;
+constexpr uint32_t kFlagWrap = 1u << 30;  // internal: a count passed 16 bits
 
 __device__ __forceinline__ uint32_t rank_key(int r) {
   return r >= 32768 ? (uint32_t)(r - 32768) : (0x8000u | (uint32_t)(32767 - r));
@@ -81,15 +92,14 @@ struct Scratch {
   int i[kWaves];
   uint32_t u[kWaves];
   uint32_t u2[kWaves];
+  uint32_t u3[kWaves];
+  uint32_t u4[kWaves];
   float f[kWaves];
-  // broadcast slots
   double bd0, bd1;
   int bi0;
   uint32_t bu0;
-  float bf0;
 };
 
-// Block-wide sums and maxima in a fixed order (deterministic).
 __device__ double block_sum_d(double v, Scratch& s) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -113,10 +123,10 @@ struct Slot {
   double P;      // top-p applied to this vector, >= 1 means none
 };
 
-__device__ Slot slot_of(const StatsParams& p, int dtype) {
+__device__ Slot slot_of(const StatsParams& p, int dtype, int v) {
   Slot s;
   const int per = slots_per_row(p.K);
-  const int b = blockIdx.x / per, j = blockIdx.x % per;
+  const int b = v / per, j = v % per;
   const int kb = p.k_per_row ? p.k_per_row[b] : p.K;
   s.needed = false;
   if (kb < 1 || kb > p.K) return s;
@@ -148,16 +158,27 @@ __device__ __forceinline__ float load_logit(const void* vec, int dtype, int64_t 
   return ((const float*)vec)[j];
 }
 
+// The slot's draft-token logit (NaN when there is none or it is out of range).
+__device__ __forceinline__ float token_logit(const Slot& s, int dtype, int V) {
+  if (s.token < 0 || s.token >= V) return __uint_as_float(0x7FC00000u);
+  return load_logit(s.vec, dtype, s.token);
+}
+
+// Weight exp((z - m) / T) of one value, formed as the finalize kernel forms
+// it: exp2 of an fp32 argument, c2 = log2(e) / T.  (z - m) is exact for bf16.
+__device__ __forceinline__ double weight(float z, float m, float c2) {
+  return (double)__builtin_amdgcn_exp2f((z - m) * c2);
+}
+
 // Writes the record, including p'(x) of the slot's draft token.
-__device__ void write_record(const Slot& s, int dtype, int V, float m, float tau,
-                             double kept, uint32_t status, VecRec* rec) {
+__device__ void write_record(const Slot& s, int V, float m, float tau, double kept,
+                             uint32_t status, float zx, VecRec* rec) {
   double px = 0.0;
   if (s.token >= 0) {
     if (s.token >= V) {
       status |= SV_ROW_BAD_TOKEN;
-    } else if (!status && s.T_ok && kept > 0.0) {
-      const float zx = load_logit(s.vec, dtype, s.token);
-      if (zx >= tau) px = exp(((double)zx - (double)m) / (double)s.T) / kept;
+    } else if (!status && s.T_ok && kept > 0.0 && zx >= tau) {
+      px = weight(zx, m, (float)(1.4426950408889634 / (double)s.T)) / kept;
     }
   } else if (s.token < -1) {
     status |= SV_ROW_BAD_TOKEN;
@@ -182,8 +203,10 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// All threads of the block call this.  hist256 is LDS of 256 doubles.
-__device__ void generic_stats(const Slot& s, int dtype, int V, double* hist256,
+// All threads of the block call this.  hist256 is LDS of 256 doubles.  Kept
+// out of line: it is the rare path of the bf16 kernel and must not add to
+// that kernel's register budget.
+__device__ __attribute__((noinline)) void generic_stats(const Slot& s, int dtype, int V, double* hist256,
                               Scratch& sc, VecRec* rec) {
   const int tid = threadIdx.x;
   // pass 1: largest finite value, NaN / +inf, any finite entry
@@ -203,28 +226,27 @@ __device__ void generic_stats(const Slot& s, int dtype, int V, double* hist256,
   uint32_t flags = 0;
   for (int i = 0; i < kWaves; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
   __syncthreads();
+  const float zx = token_logit(s, dtype, V);
   uint32_t status = flags & SV_ROW_NONFINITE_LOGIT;
   if (!(flags & 0x80000000u)) status |= SV_ROW_NO_FINITE;
   if (status || !s.T_ok) {
-    if (tid == 0) write_record(s, dtype, V, m, -INFINITY, 0.0, status, rec);
+    if (tid == 0) write_record(s, V, m, -INFINITY, 0.0, status, zx, rec);
     return;
   }
-  const double T = (double)s.T, md = (double)m;
+  const float c2 = (float)(1.4426950408889634 / (double)s.T);
   // pass 2: normaliser S
   double acc = 0.0;
-  for (int64_t j = tid; j < V; j += kThreads) {
-    const float z = load_logit(s.vec, dtype, j);
-    acc += exp(((double)z - md) / T);
-  }
+  for (int64_t j = tid; j < V; j += kThreads) acc += weight(load_logit(s.vec, dtype, j), m, c2);
   const double S = block_sum_d(acc, sc);
   if (!(s.P < 1.0)) {
-    if (tid == 0) write_record(s, dtype, V, m, -INFINITY, S, 0, rec);
+    if (tid == 0) write_record(s, V, m, -INFINITY, S, 0, zx, rec);
     return;
   }
   // passes 3-6: radix select of the threshold key, 8 bits at a time
   const double target = s.P * S;
   uint32_t prefix = 0;
-  double above = 0.0, kept = S;
+  double kept = S;
+  double above = 0.0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
@@ -235,7 +257,7 @@ __device__ void generic_stats(const Slot& s, int dtype, int V, double* hist256,
       if (!(z > -INFINITY)) continue;
       const uint32_t k = order_key(z);
       if ((k & hmask) != (prefix & hmask)) continue;
-      const double wgt = exp(((double)z - md) / T);
+      const double wgt = weight(z, m, c2);
       if (wgt > 0.0) atomicAdd(&hist256[(k >> shift) & 255u], wgt);
     }
     __syncthreads();
@@ -260,23 +282,45 @@ __device__ void generic_stats(const Slot& s, int dtype, int V, double* hist256,
     kept = sc.bd1;
     __syncthreads();
   }
-  if (tid == 0) write_record(s, dtype, V, m, key_value(prefix), kept, 0, rec);
+  if (tid == 0) write_record(s, V, m, key_value(prefix), kept, 0, zx, rec);
 }
-
-// ---------------------------------------------------------------- kernels
 
 __global__ __launch_bounds__(kThreads) void stats_generic_kernel(StatsParams p, int dtype) {
   __shared__ double hist256[256];
   __shared__ Scratch sc;
-  const Slot s = slot_of(p, dtype);
+  const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
   generic_stats(s, dtype, p.V, hist256, sc, p.recs + blockIdx.x);
+}
+
+// ---------------------------------------------------------------- bf16 path
+
+// Splits one table word into the counts of +key (lo) and -key (hi): -0 is
+// folded into +0, -inf carries no mass, +inf and NaN are errors.  Returns
+// flag bits.
+__device__ __forceinline__ uint32_t split_counts(uint32_t x, uint32_t key, uint32_t* lo,
+                                                 uint32_t* hi) {
+  uint32_t l = x & 0xFFFFu, h = x >> 16, fl = 0;
+  if (key == 0) {
+    l += h;
+    h = 0;
+    if (l > 0xFFFFu) { fl |= kFlagWrap; l = 0; }
+  }
+  if (key >= 0x7F80u) {
+    if (l) fl |= SV_ROW_NONFINITE_LOGIT;
+    if (h && key > 0x7F80u) fl |= SV_ROW_NONFINITE_LOGIT;
+    l = 0;
+    h = 0;
+  }
+  *lo = l;
+  *hi = h;
+  return fl;
 }
 
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t key16) {
   const uint32_t word = key16 & 0x7FFFu;
   const uint32_t inc = 1u << ((key16 >> 11) & 16u);
-  __hip_atomic_fetch_add(hist + hist_phys(word), inc, __ATOMIC_RELAXED,
+  __hip_atomic_fetch_add(hist + word, inc, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ void hist_add8(uint32_t* hist, const uint4& d) {
@@ -286,175 +330,283 @@ __device__ __forceinline__ void hist_add8(uint32_t* hist, const uint4& d) {
   hist_add(hist, d.w & 0xFFFFu); hist_add(hist, d.w >> 16);
 }
 
-// Count of rank (64*tid + i); -0 is folded into +0.
-__device__ __forceinline__ uint32_t rank_count(const uint32_t* hist, int tid, int i) {
-  if (tid >= 512) {
-    const uint32_t word = 64u * (uint32_t)(tid - 512) + (uint32_t)i;
-    uint32_t c = hist[hist_phys(word)] & 0xFFFFu;
-    if (word == 0) c += hist[hist_phys(0)] >> 16;
-    return c;
+// Streams one vector into the count table.
+__device__ void count_values(const uint16_t* __restrict__ vec, int V, uint32_t* hist) {
+  const int tid = threadIdx.x;
+  const uintptr_t addr = (uintptr_t)vec;
+  int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) >> 1);
+  if (head > V) head = V;
+  if (tid < head) hist_add(hist, vec[tid]);
+  const uint4* body = (const uint4*)(vec + head);
+  const int nb = (V - head) >> 3;
+  // batches of 4 x 16 bytes per thread, the next batch's loads issued
+  // before the current batch's atomics
+  int i = tid;
+  bool have = i + 3 * kThreads < nb;
+  uint4 a0, a1, a2, a3;
+  if (have) {
+    a0 = body[i];
+    a1 = body[i + kThreads];
+    a2 = body[i + 2 * kThreads];
+    a3 = body[i + 3 * kThreads];
   }
-  const uint32_t word = 64u * (uint32_t)(511 - tid) + (uint32_t)(63 - i);
-  if (word == 0) return 0;  // -0, counted with +0
-  return hist[hist_phys(word)] >> 16;
+  while (have) {
+    const int j = i + 4 * kThreads;
+    const bool next = j + 3 * kThreads < nb;
+    uint4 b0, b1, b2, b3;
+    if (next) {
+      b0 = body[j];
+      b1 = body[j + kThreads];
+      b2 = body[j + 2 * kThreads];
+      b3 = body[j + 3 * kThreads];
+    }
+    hist_add8(hist, a0);
+    hist_add8(hist, a1);
+    hist_add8(hist, a2);
+    hist_add8(hist, a3);
+    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+    i = j;
+    have = next;
+  }
+  for (; i < nb; i += kThreads) hist_add8(hist, body[i]);
+  const int t0 = head + (nb << 3);
+  if (t0 + tid < V) hist_add(hist, vec[t0 + tid]);
 }
 
 __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(StatsParams p) {
-  __shared__ __align__(16) uint32_t hist[kHistPhys];
+  __shared__ __align__(16) uint32_t hist[kHistWords];
+  __shared__ uint32_t list[kListCap];
+  __shared__ uint64_t bins1[256];   // fixed-point mass per (rank >> 8)
+  __shared__ uint64_t bins2[256];   // fixed-point mass per rank inside the crossing bin
   __shared__ Scratch sc;
-  const Slot s = slot_of(p, SV_BF16);
-  if (!s.needed) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int V = p.V;
+  const int nslots = p.B * slots_per_row(p.K);
+  uint4* hist4 = reinterpret_cast<uint4*>(hist);
 
-  for (int i = tid; i < kHistPhys; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
+  if (tid < 256) { bins1[tid] = 0; bins2[tid] = 0; }
   __syncthreads();
 
-  // ---- one streaming pass: count every bf16 value
-  {
-    const uint16_t* vec = (const uint16_t*)s.vec;
-    const uintptr_t addr = (uintptr_t)vec;
-    int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) >> 1);
-    if (head > V) head = V;
-    if (tid < head) hist_add(hist, vec[tid]);
-    const uint4* body = (const uint4*)(vec + head);
-    const int nb = (V - head) >> 3;
-    int i = tid;
-    for (; i + 3 * kThreads < nb; i += 4 * kThreads) {
-      const uint4 d0 = body[i];
-      const uint4 d1 = body[i + kThreads];
-      const uint4 d2 = body[i + 2 * kThreads];
-      const uint4 d3 = body[i + 3 * kThreads];
-      hist_add8(hist, d0);
-      hist_add8(hist, d1);
-      hist_add8(hist, d2);
-      hist_add8(hist, d3);
+  for (int v = blockIdx.x; v < nslots; v += gridDim.x) {
+    const Slot s = slot_of(p, SV_BF16, v);
+    if (!s.needed) continue;
+    VecRec* rec = p.recs + v;
+    const float zx = tid == 0 ? token_logit(s, SV_BF16, V) : 0.0f;
+
+    count_values((const uint16_t*)s.vec, V, hist);
+    __syncthreads();
+
+    // ---- E1: thread t reads the 16-byte groups t + 1024 j (j < 8) of the
+    // table: conflict-free, and a dense range of values spreads over many
+    // threads.  Word w counts +w in its low half (rank 32768 + w) and -w in
+    // its high half (rank 32767 - w).  Only groups holding a count are
+    // looked at; jmask remembers them for the second pass.
+    uint32_t fl = 0, total = 0, nfin = 0, nent = 0, jmask = 0;
+    int maxr = -1;
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) {
+      const uint4 g = hist4[tid + 1024 * j];
+      if (!(g.x | g.y | g.z | g.w)) continue;
+      jmask |= 1u << j;
+      const uint32_t xs[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = xs[q];
+        if (!x) continue;
+        const uint32_t key = 4u * (tid + 1024u * j) + q;
+        total += (x & 0xFFFFu) + (x >> 16);
+        uint32_t lo, hi;
+        fl |= split_counts(x, key, &lo, &hi);
+        nfin += lo + hi;
+        nent += (lo != 0) + (hi != 0);
+        if (lo) maxr = max(maxr, 32768 + (int)key);
+        if (hi) maxr = max(maxr, 32767 - (int)key);
+      }
     }
-    for (; i < nb; i += kThreads) hist_add8(hist, body[i]);
-    const int t0 = head + (nb << 3);
-    if (t0 + tid < V) hist_add(hist, vec[t0 + tid]);
-  }
-  __syncthreads();
-
-  // ---- E1: largest finite rank, non-finite flags, totals
-  int maxr = -1;
-  uint32_t fl = 0, total = 0, nfin = 0;
-  for (int i = 0; i < 64; ++i) {
-    const uint32_t c = rank_count(hist, tid, i);
-    if (!c) continue;
-    const int r = 64 * tid + i;
-    total += c;
-    if (r < kRankNegInf || r >= kRankPosInf) fl |= SV_ROW_NONFINITE_LOGIT;
-    else if (r > kRankNegInf) { maxr = r; nfin += c; }
-  }
-  {
-    const int w = tid >> 6, l = tid & 63;
-    const int mr = wave_max_i(maxr);
-    const uint32_t f = wave_or(fl);
-    const uint32_t t = wave_sum(total);
-    const uint32_t n = wave_sum(nfin);
-    if (l == 0) { sc.i[w] = mr; sc.u[w] = f; sc.u2[w] = t; sc.f[w] = __uint_as_float(n); }
+    // block: exclusive scan of entry counts (thread order), flags, totals, max
+    const uint32_t einc = wave_scan_u32<OpAddU32>(nent);
+    {
+      const uint32_t etot = wave_last_u32(einc);
+      const int wmax = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)maxr));
+      const uint32_t wor = wave_last_u32(wave_scan_u32<OpOrU32>(fl));
+      const uint32_t wtot = wave_last_u32(wave_scan_u32<OpAddU32>(total));
+      const uint32_t wfin = wave_last_u32(wave_scan_u32<OpAddU32>(nfin));
+      if (l == 0) {
+        sc.i[w] = wmax;
+        sc.u[w] = wor;
+        sc.u2[w] = wtot;
+        sc.u4[w] = wfin;
+        sc.u3[w] = etot;
+      }
+    }
     __syncthreads();
     int MR = -1;
-    uint32_t F = 0, TT = 0, N = 0;
+    uint32_t F = 0, TT = 0, N = 0, ebefore = 0, ND = 0;
     for (int k = 0; k < kWaves; ++k) {
       MR = max(MR, sc.i[k]);
       F |= sc.u[k];
       TT += sc.u2[k];
-      N += __float_as_uint(sc.f[k]);
+      N += sc.u4[k];
+      if (k < w) ebefore += sc.u3[k];
+      ND += sc.u3[k];
     }
     __syncthreads();
-    maxr = MR;
-    fl = F;
-    total = TT;
-    nfin = N;
-  }
-  if (total != (uint32_t)V) {
-    // a 16-bit count wrapped: redo this vector exactly on the generic path,
-    // reusing the histogram memory for its 256 fp64 bins
-    generic_stats(s, SV_BF16, V, reinterpret_cast<double*>(hist), sc, p.recs + blockIdx.x);
-    return;
-  }
-  uint32_t status = fl;
-  if (nfin == 0) status |= SV_ROW_NO_FINITE;
-  const float m = maxr >= 0 ? bf16f(rank_key(maxr)) : -INFINITY;
-  if (status || !s.T_ok) {
-    if (tid == 0) write_record(s, SV_BF16, V, m, -INFINITY, 0.0, status, p.recs + blockIdx.x);
-    return;
-  }
+    if (TT != (uint32_t)V || (F & kFlagWrap) || ND > (uint32_t)kListCap) {
+      // a 16-bit count wrapped (or too many distinct values to list): redo
+      // the vector exactly on the generic path, borrowing the table
+      generic_stats(s, SV_BF16, V, reinterpret_cast<double*>(hist), sc, rec);
+      __syncthreads();
+      for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
+      __syncthreads();
+      continue;
+    }
+    uint32_t status = F & SV_ROW_NONFINITE_LOGIT;
+    if (N == 0) status |= SV_ROW_NO_FINITE;
+    const float m = MR >= 0 ? bf16f(rank_key(MR)) : -INFINITY;
+    const bool stats_ok = !status && s.T_ok;
 
-  // ---- E2: per-thread mass of its 64 ranks, fp64, in descending rank order
-  const double T = (double)s.T, md = (double)m;
-  double mass = 0.0;
-  for (int i = 63; i >= 0; --i) {
-    const int r = 64 * tid + i;
-    if (r <= kRankNegInf || r > maxr) continue;
-    const uint32_t c = rank_count(hist, tid, i);
-    if (!c) continue;
-    mass += (double)c * exp(((double)bf16f(rank_key(r)) - md) / T);
-  }
-  // suffix scan over threads in descending order: excl = mass of higher ranks
-  const int w = tid >> 6, l = tid & 63;
-  double suf = mass;
+    // ---- E2: second pass over the same groups: list entries (rank << 16 |
+    // count) at this thread's scanned offset, and the table cleared for the
+    // next vector.
+    {
+      uint32_t o = ebefore + (einc - nent);
+#pragma unroll 1
+      for (int j = 0; j < 8; ++j) {
+        if (!((jmask >> j) & 1u)) continue;
+        const uint4 g = hist4[tid + 1024 * j];
+        hist4[tid + 1024 * j] = make_uint4(0u, 0u, 0u, 0u);
+        if (!stats_ok) continue;
+        const uint32_t xs[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_down(suf, o, 64);
-    if (l + o < 64) suf += t;
-  }
-  if (l == 0) sc.d[w] = suf;  // wave total
-  __syncthreads();
-  double higher = 0.0, S = 0.0;
-  for (int k = kWaves - 1; k >= 0; --k) {
-    if (k > w) higher += sc.d[k];
-    S += sc.d[k];
-  }
-  const double excl = higher + (suf - mass);
-
-  float tau = -INFINITY;
-  double kept = S;
-  if (s.P < 1.0) {
-    const double target = s.P * S;
-    if (tid == 0) { sc.bi0 = -1; sc.bd1 = S; }
-    __syncthreads();
-    if (mass > 0.0 && excl < target && excl + mass >= target) {
-      double cum = excl;
-      int tr = -1;
-      double kz = S;
-      for (int i = 63; i >= 0; --i) {
-        const int r = 64 * tid + i;
-        if (r <= kRankNegInf || r > maxr) continue;
-        const uint32_t c = rank_count(hist, tid, i);
-        if (!c) continue;
-        const double g = (double)c * exp(((double)bf16f(rank_key(r)) - md) / T);
-        if (!(cum < target)) break;
-        tr = r;
-        cum += g;
-        kz = cum;
-        if (cum >= target) break;
+        for (int q = 0; q < 4; ++q) {
+          if (!xs[q]) continue;
+          const uint32_t key = 4u * (tid + 1024u * j) + q;
+          uint32_t lo, hi;
+          split_counts(xs[q], key, &lo, &hi);
+          if (lo) list[o++] = ((uint32_t)(32768 + (int)key) << 16) | lo;
+          if (hi) list[o++] = ((uint32_t)(32767 - (int)key) << 16) | hi;
+        }
       }
-      sc.bi0 = tr;
-      sc.bd1 = kz;
+    }
+    if (!stats_ok) {
+      if (tid == 0) write_record(s, V, m, -INFINITY, 0.0, status, zx, rec);
+      __syncthreads();
+      continue;
     }
     __syncthreads();
-    if (sc.bi0 >= 0) {
-      tau = bf16f(rank_key(sc.bi0));
-      kept = sc.bd1;
+
+    // ---- E3: mass of each listed value, count * exp((v - m)/T), as a 64-bit
+    // fixed-point number (scale 2^45; a vector's total stays below 2^63);
+    // integer sums are exact in any order, so the results do not depend on
+    // the schedule.  Coarse bins by rank >> 8 for the top-p search.
+    const float c2 = (float)(1.4426950408889634 / (double)s.T);
+    for (uint32_t e = tid; e < ND; e += kThreads) {
+      const uint32_t ent = list[e];
+      const uint32_t r = ent >> 16;
+      const double mass = (double)(ent & 0xFFFFu) * weight(bf16f(rank_key((int)r)), m, c2);
+      const uint64_t fx = (uint64_t)(mass * kFixScale + 0.5);
+      if (fx) atomicAdd((unsigned long long*)&bins1[r >> 8], (unsigned long long)fx);
     }
+    __syncthreads();
+
+    // ---- E4: wave 0 walks the 256 coarse bins from the top: total S, and
+    // the bin where the mass above reaches top_p * S.
+    if (w == 0) {
+      // lane l holds bins 255-4l .. 252-4l (descending)
+      uint64_t b[4];
+      double part = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b[q] = bins1[255 - 4 * l - q];
+        bins1[255 - 4 * l - q] = 0;
+        part += (double)b[q];
+      }
+      const double incl = wave_scan_add_f64(part);   // lanes ascending = bins descending
+      const double S_fix = wave_last_f64(incl);
+      double above = incl - part;                    // mass of all higher bins
+      if (l == 0) { sc.bd0 = S_fix; sc.bi0 = -1; }
+      if (s.P < 1.0) {
+        const double target = s.P * S_fix;
+        if (above < target && above + part >= target) {
+          double cum = above;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (cum + (double)b[q] >= target && b[q]) {
+              sc.bi0 = 255 - 4 * l - q;
+              sc.bd1 = cum;
+              break;
+            }
+            cum += (double)b[q];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const double S_fix = sc.bd0;
+    float tau = -INFINITY;
+    double kept_fix = S_fix;
+    if (s.P < 1.0 && sc.bi0 >= 0) {
+      // level 2: the values of the crossing bin, each in its own slot
+      const int b1 = sc.bi0;
+      for (uint32_t e = tid; e < ND; e += kThreads) {
+        const uint32_t ent = list[e];
+        const uint32_t r = ent >> 16;
+        if ((int)(r >> 8) != b1) continue;
+        const double mass = (double)(ent & 0xFFFFu) * weight(bf16f(rank_key((int)r)), m, c2);
+        bins2[r & 255u] = (uint64_t)(mass * kFixScale + 0.5);
+      }
+      __syncthreads();
+      if (w == 0) {
+        uint64_t b[4];
+        double part = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b[q] = bins2[255 - 4 * l - q];
+          bins2[255 - 4 * l - q] = 0;
+          part += (double)b[q];
+        }
+        const double incl = wave_scan_add_f64(part);
+        const double above = sc.bd1 + (incl - part);
+        const double target = s.P * S_fix;
+        if (l == 0) sc.bu0 = 0xFFFFFFFFu;
+        if (above < target && above + part >= target) {
+          double cum = above;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (b[q] && cum + (double)b[q] >= target) {
+              sc.bu0 = (uint32_t)(b1 << 8) | (uint32_t)(255 - 4 * l - q);
+              sc.bd0 = cum + (double)b[q];
+              break;
+            }
+            cum += (double)b[q];
+          }
+        }
+      }
+      __syncthreads();
+      if (sc.bu0 != 0xFFFFFFFFu) {
+        tau = bf16f(rank_key((int)sc.bu0));
+        kept_fix = sc.bd0;
+      }
+    }
+    if (tid == 0) write_record(s, V, m, tau, kept_fix * (1.0 / kFixScale), 0, zx, rec);
+    __syncthreads();  // scratch and list are reused by the next vector
   }
-  if (tid == 0) write_record(s, SV_BF16, V, m, tau, kept, 0, p.recs + blockIdx.x);
 }
 
 }  // namespace
 
-hipError_t launch_stats(const StatsParams& p, int dtype, hipStream_t s, Timer* t) {
-  const unsigned grid = (unsigned)p.B * (unsigned)slots_per_row(p.K);
-  if (grid == 0) return hipSuccess;
+hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_t s, Timer* t) {
+  const unsigned nslots = (unsigned)p.B * (unsigned)slots_per_row(p.K);
+  if (nslots == 0) return hipSuccess;
   if (dtype == SV_BF16) {
+    const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
+    const unsigned grid = nslots < cus ? nslots : cus;
     TimedScope ts(t, "stats_bf16", s);
     hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kThreads), 0, s, p);
   } else {
     TimedScope ts(t, "stats_generic", s);
-    hipLaunchKernelGGL(stats_generic_kernel, dim3(grid), dim3(kThreads), 0, s, p, dtype);
+    hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kThreads), 0, s, p, dtype);
   }
   return hipGetLastError();
 }
