@@ -330,8 +330,12 @@ __device__ __forceinline__ void hist_add8(uint32_t* hist, const uint4& d) {
   hist_add(hist, d.w & 0xFFFFu); hist_add(hist, d.w >> 16);
 }
 
-// Streams one vector into the count table.
-__device__ void count_values(const uint16_t* __restrict__ vec, int V, uint32_t* hist) {
+// Streams one vector into the count table.  Batches of 4 x 16 bytes per
+// thread; the next batch is loaded before the current one is counted.  Every
+// load is unconditional (indices past the end are clamped, their counts
+// skipped) so the compiler's wait counts let the prefetch stay in flight.
+__device__ __forceinline__ void count_values(const uint16_t* __restrict__ vec, int V,
+                                             uint32_t* hist) {
   const int tid = threadIdx.x;
   const uintptr_t addr = (uintptr_t)vec;
   int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) >> 1);
@@ -339,36 +343,28 @@ __device__ void count_values(const uint16_t* __restrict__ vec, int V, uint32_t* 
   if (tid < head) hist_add(hist, vec[tid]);
   const uint4* body = (const uint4*)(vec + head);
   const int nb = (V - head) >> 3;
-  // batches of 4 x 16 bytes per thread, the next batch's loads issued
-  // before the current batch's atomics
-  int i = tid;
-  bool have = i + 3 * kThreads < nb;
-  uint4 a0, a1, a2, a3;
-  if (have) {
-    a0 = body[i];
-    a1 = body[i + kThreads];
-    a2 = body[i + 2 * kThreads];
-    a3 = body[i + 3 * kThreads];
-  }
-  while (have) {
-    const int j = i + 4 * kThreads;
-    const bool next = j + 3 * kThreads < nb;
-    uint4 b0, b1, b2, b3;
-    if (next) {
-      b0 = body[j];
-      b1 = body[j + kThreads];
-      b2 = body[j + 2 * kThreads];
-      b3 = body[j + 3 * kThreads];
+  const int last = nb - 1;
+  const int nbatch = (nb + 4 * kThreads - 1) / (4 * kThreads);
+  if (nbatch > 0) {
+    int i = tid;
+    uint4 a0 = body[min(i, last)];
+    uint4 a1 = body[min(i + kThreads, last)];
+    uint4 a2 = body[min(i + 2 * kThreads, last)];
+    uint4 a3 = body[min(i + 3 * kThreads, last)];
+    for (int k = 0; k < nbatch; ++k) {
+      const int j = (k + 1 < nbatch) ? i + 4 * kThreads : i;
+      const uint4 b0 = body[min(j, last)];
+      const uint4 b1 = body[min(j + kThreads, last)];
+      const uint4 b2 = body[min(j + 2 * kThreads, last)];
+      const uint4 b3 = body[min(j + 3 * kThreads, last)];
+      if (i < nb) hist_add8(hist, a0);
+      if (i + kThreads < nb) hist_add8(hist, a1);
+      if (i + 2 * kThreads < nb) hist_add8(hist, a2);
+      if (i + 3 * kThreads < nb) hist_add8(hist, a3);
+      a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+      i += 4 * kThreads;
     }
-    hist_add8(hist, a0);
-    hist_add8(hist, a1);
-    hist_add8(hist, a2);
-    hist_add8(hist, a3);
-    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
-    i = j;
-    have = next;
   }
-  for (; i < nb; i += kThreads) hist_add8(hist, body[i]);
   const int t0 = head + (nb << 3);
   if (t0 + tid < V) hist_add(hist, vec[t0 + tid]);
 }
