@@ -33,21 +33,63 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=2, help="input batches rotated between steps")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_bf16_b256_k6_v151936_traffic.txt")
+STATS_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_11_amd", "csrc", "stats.hip")
+
+
+def copy_calibration():
+    """A plain elementwise copy of known size: 1 GiB read, 1 GiB written per
+    launch.  Its FETCH_SIZE / WRITE_SIZE readings scale the counters of the
+    kernels measured the same way."""
+    import torch
+    src = torch.arange(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    assert int(dst[12345]) == -12345
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "launches": 3}))
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the stats kernel from the committed counter
+    summary, or None when the kernel source has changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(line.split("=", 1) for line in f.read().splitlines()
+                          if "=" in line and not line.startswith("#"))
+        with open(STATS_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("stats_source_sha256", "").strip() != digest:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (rows are "
               "independent, so more GPUs would each run this same step on their own rows)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
-    if args.steps + args.warmup + 20 > 680:
-        print("at most 660 steps: each rollback shortens every sequence by up to k",
-              file=sys.stderr)
+    if 2 * args.steps + args.warmup > 680:
+        print("at most 2*steps + warmup = 680: each rollback shortens every sequence by up "
+              "to k", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -110,9 +152,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel durations, measured live with HIP events on the same stream
+    # per-kernel durations: a second pass of the same K steps with HIP events
+    # recorded around every launch, on the stream the kernels run on
     sv.timing_enable(dev, True)
-    for _ in range(min(args.steps, 20)):
+    for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     kt = sv.timing_read(dev)
@@ -151,7 +194,7 @@ def main():
         "wall_s": wall,
         "roofline": {"bound": "hbm", "kernel": "stats_bf16", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
     }
 
     if not args.no_cpu_baseline:

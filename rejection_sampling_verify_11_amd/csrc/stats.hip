@@ -170,17 +170,18 @@ __device__ __forceinline__ double weight(float z, float m, float c2) {
   return (double)__builtin_amdgcn_exp2f((z - m) * c2);
 }
 
-// Writes the record, including p'(x) of the slot's draft token.
-__device__ void write_record(const Slot& s, int V, float m, float tau, double kept,
-                             uint32_t status, float zx, VecRec* rec) {
+// Writes the record, including p'(x) of the slot's draft token (token -1:
+// none; T_ok false: the temperature is invalid and no mass is formed).
+__device__ void write_record(int token, float T, bool T_ok, int V, float m, float tau,
+                             double kept, uint32_t status, float zx, VecRec* rec) {
   double px = 0.0;
-  if (s.token >= 0) {
-    if (s.token >= V) {
+  if (token >= 0) {
+    if (token >= V) {
       status |= SV_ROW_BAD_TOKEN;
-    } else if (!status && s.T_ok && kept > 0.0 && zx >= tau) {
-      px = weight(zx, m, (float)(1.4426950408889634 / (double)s.T)) / kept;
+    } else if (!status && T_ok && kept > 0.0 && zx >= tau) {
+      px = weight(zx, m, (float)(1.4426950408889634 / (double)T)) / kept;
     }
-  } else if (s.token < -1) {
+  } else if (token < -1) {
     status |= SV_ROW_BAD_TOKEN;
   }
   VecRec r;
@@ -205,15 +206,19 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // All threads of the block call this.  hist256 is LDS of 256 doubles.  Kept
 // out of line: it is the rare path of the bf16 kernel and must not add to
-// that kernel's register budget.
-__device__ __attribute__((noinline)) void generic_stats(const Slot& s, int dtype, int V, double* hist256,
-                              Scratch& sc, VecRec* rec) {
+// that kernel's register budget.  The slot arrives as plain values so that
+// the caller keeps nothing in memory for the call.
+__device__ __attribute__((noinline)) void generic_stats(const void* vec, int token, float T,
+                                                        double P, int dtype, int V,
+                                                        double* hist256, Scratch& sc,
+                                                        VecRec* rec) {
   const int tid = threadIdx.x;
+  const bool T_ok = T > 0.0f && isfinite(T);
   // pass 1: largest finite value, NaN / +inf, any finite entry
   float mx = -INFINITY;
   uint32_t fl = 0, nfin = 0;
   for (int64_t j = tid; j < V; j += kThreads) {
-    const float z = load_logit(s.vec, dtype, j);
+    const float z = load_logit(vec, dtype, j);
     if (isnan(z) || z == INFINITY) fl |= SV_ROW_NONFINITE_LOGIT;
     else if (z > -INFINITY) { nfin = 1; mx = fmaxf(mx, z); }
   }
@@ -226,24 +231,25 @@ __device__ __attribute__((noinline)) void generic_stats(const Slot& s, int dtype
   uint32_t flags = 0;
   for (int i = 0; i < kWaves; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
   __syncthreads();
-  const float zx = token_logit(s, dtype, V);
+  const float zx = (token >= 0 && token < V) ? load_logit(vec, dtype, token)
+                                               : __uint_as_float(0x7FC00000u);
   uint32_t status = flags & SV_ROW_NONFINITE_LOGIT;
   if (!(flags & 0x80000000u)) status |= SV_ROW_NO_FINITE;
-  if (status || !s.T_ok) {
-    if (tid == 0) write_record(s, V, m, -INFINITY, 0.0, status, zx, rec);
+  if (status || !T_ok) {
+    if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, 0.0, status, zx, rec);
     return;
   }
-  const float c2 = (float)(1.4426950408889634 / (double)s.T);
+  const float c2 = (float)(1.4426950408889634 / (double)T);
   // pass 2: normaliser S
   double acc = 0.0;
-  for (int64_t j = tid; j < V; j += kThreads) acc += weight(load_logit(s.vec, dtype, j), m, c2);
+  for (int64_t j = tid; j < V; j += kThreads) acc += weight(load_logit(vec, dtype, j), m, c2);
   const double S = block_sum_d(acc, sc);
-  if (!(s.P < 1.0)) {
-    if (tid == 0) write_record(s, V, m, -INFINITY, S, 0, zx, rec);
+  if (!(P < 1.0)) {
+    if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, S, 0, zx, rec);
     return;
   }
   // passes 3-6: radix select of the threshold key, 8 bits at a time
-  const double target = s.P * S;
+  const double target = P * S;
   uint32_t prefix = 0;
   double kept = S;
   double above = 0.0;
@@ -253,7 +259,7 @@ __device__ __attribute__((noinline)) void generic_stats(const Slot& s, int dtype
     for (int i = tid; i < 256; i += kThreads) hist256[i] = 0.0;
     __syncthreads();
     for (int64_t j = tid; j < V; j += kThreads) {
-      const float z = load_logit(s.vec, dtype, j);
+      const float z = load_logit(vec, dtype, j);
       if (!(z > -INFINITY)) continue;
       const uint32_t k = order_key(z);
       if ((k & hmask) != (prefix & hmask)) continue;
@@ -282,7 +288,7 @@ __device__ __attribute__((noinline)) void generic_stats(const Slot& s, int dtype
     kept = sc.bd1;
     __syncthreads();
   }
-  if (tid == 0) write_record(s, V, m, key_value(prefix), kept, 0, zx, rec);
+  if (tid == 0) write_record(token, T, T_ok, V, m, key_value(prefix), kept, 0, zx, rec);
 }
 
 __global__ __launch_bounds__(kThreads) void stats_generic_kernel(StatsParams p, int dtype) {
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void stats_generic_kernel(StatsParams p, 
   __shared__ Scratch sc;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
-  generic_stats(s, dtype, p.V, hist256, sc, p.recs + blockIdx.x);
+  generic_stats(s.vec, s.token, s.T, s.P, dtype, p.V, hist256, sc, p.recs + blockIdx.x);
 }
 
 // ---------------------------------------------------------------- bf16 path
@@ -451,7 +457,8 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(StatsParams p) {
     if (TT != (uint32_t)V || (F & kFlagWrap) || ND > (uint32_t)kListCap) {
       // a 16-bit count wrapped (or too many distinct values to list): redo
       // the vector exactly on the generic path, borrowing the table
-      generic_stats(s, SV_BF16, V, reinterpret_cast<double*>(hist), sc, rec);
+      generic_stats(s.vec, s.token, s.T, s.P, SV_BF16, V, reinterpret_cast<double*>(hist),
+                    sc, rec);
       __syncthreads();
       for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
       __syncthreads();
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(StatsParams p) {
       }
     }
     if (!stats_ok) {
-      if (tid == 0) write_record(s, V, m, -INFINITY, 0.0, status, zx, rec);
+      if (tid == 0) write_record(s.token, s.T, s.T_ok, V, m, -INFINITY, 0.0, status, zx, rec);
       __syncthreads();
       continue;
     }
@@ -585,7 +592,8 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(StatsParams p) {
         kept_fix = sc.bd0;
       }
     }
-    if (tid == 0) write_record(s, V, m, tau, kept_fix * (1.0 / kFixScale), 0, zx, rec);
+    if (tid == 0)
+      write_record(s.token, s.T, s.T_ok, V, m, tau, kept_fix * (1.0 / kFixScale), 0, zx, rec);
     __syncthreads();  // scratch and list are reused by the next vector
   }
 }
