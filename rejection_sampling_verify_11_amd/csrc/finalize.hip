@@ -230,7 +230,7 @@ __device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, i
   d.vec = (const char*)base + vec_index * stride * (dtype == SV_BF16 ? 2 : 4);
   d.m = rec.m;
   d.tau = rec.tau;
-  d.c2 = (float)(1.4426950408889634 / (double)T);
+  d.c2 = log2e_over_T(T);
   d.inv = rec.inv_kept;
   return d;
 }

@@ -9,26 +9,24 @@
 // tie-closed: keep j iff the mass of strictly larger logits is below top_p,
 // i.e. keep {j : z_j >= tau} for the lowest kept value tau.
 //
-// bf16 path.  A bf16 logit has only 2^16 possible values, so an exact count
-// of each value determines everything: m is the largest value present, the
+// bf16 path.  A bf16 logit takes few distinct values, so an exact count of
+// each value determines everything: m is the largest value present, the
 // normaliser is sum_v count(v) exp((v - m)/T), and the top-p threshold is
 // found by walking values downwards until the mass reaches top_p * S.  The
-// streaming loop therefore does integer work only (one LDS atomic per
-// logit) and the exp()s are taken once per distinct value.  Two 16-bit
-// counts share an LDS word: the low 15 bits of the value select the word,
-// the sign bit the half.  A count can only wrap if 65536 or more logits of
-// one vector are bit-identical; the sum of all stored counts then differs
-// from V, which sends that vector down the generic path.
+// streaming loop does integer work only (one LDS atomic per logit) and the
+// exp()s are taken once per distinct value.
 //
-// The kernel is persistent: one 1024-thread workgroup per CU (the 132 KB
-// count table fills the CU's LDS) walks its share of the vectors.  Per
-// vector: stream the logits into the table; each thread reads and clears
-// its 32 words (the table is then ready for the next vector); the distinct
-// values are compacted into a list in ascending order; masses are formed
-// per list entry (fp32 exp2, fp64 sums) and scanned; the thread whose run
-// holds top_p * S resolves the threshold exactly.
+// The count table covers a window of magnitudes, [2^-24, 2^16): 40 exponent
+// rows of 128 mantissas, one 32-bit word per magnitude holding the count of
+// +v in its low half and of -v in its high half (20 KB).  Zeros and -inf are
+// counted in registers; NaN and +inf mark the row as an error.  Any other
+// logit outside the window, or a count that wraps its 16 bits (65536 equal
+// logits), sends the vector down the generic path.  The small table lets
+// four workgroups share a CU, so one workgroup's epilogue (no memory traffic)
+// overlaps the others' streaming; vectors are handed out by a ticket
+// counter.  LDS atomics, not HBM, bound the streaming loop.
 //
-// Generic path (fp32 logits, or a bf16 vector whose counts wrapped): passes
+// Generic path (fp32 logits, or a bf16 vector the table cannot hold): passes
 // over the vector in global memory: max, fp64 sum, then a 4-pass radix select
 // on 32-bit order-preserving keys with fp64 mass histograms.
 #include <math.h>
@@ -39,28 +37,8 @@
 namespace sv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kHistWords = 32768;
-// Fixed-point scale of value masses: a mass is at most 65535 (count) and a
-// vector's total at most V < 2^18, so sums stay below 2^63; one unit is
-// 2^-45 of the largest value's weight.
-constexpr double kFixScale = 35184372088832.0;  // 2^45
-// Distinct finite values listed per vector; a vector with more (none of the
-// workloads comes close: they hold 270..2900) takes the generic path.  Sized
-// to what is left of the CU's 160 KB of LDS.
-constexpr int kListCap = 7000;
+constexpr int kGenThreads = 1024;  // generic kernel: one workgroup per vector
 
-
-// Rank order of bf16 values: rank r in [0, 65536).  r >= 32768 holds the
-// non-negative key r - 32768; r < 32768 holds the negative key
-// 0x8000 | (32767 - r).  Ranks [128, 65407] are finite, 127 is -inf, 65408 is
-// +inf, the rest are NaN.
-constexpr uint32_t kFlagWrap = 1u << 30;  // internal: a count passed 16 bits
-
-__device__ __forceinline__ uint32_t rank_key(int r) {
-  return r >= 32768 ? (uint32_t)(r - 32768) : (0x8000u | (uint32_t)(32767 - r));
-}
 __device__ __forceinline__ float bf16f(uint32_t key) { return __uint_as_float(key << 16); }
 
 // ---------------------------------------------------------------- reductions
@@ -69,11 +47,6 @@ template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
   return v;
 }
 __device__ __forceinline__ float wave_max_f(float v) {
@@ -87,26 +60,23 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   return v;
 }
 
+template <int NW>
 struct Scratch {
-  double d[kWaves];
-  int i[kWaves];
-  uint32_t u[kWaves];
-  uint32_t u2[kWaves];
-  uint32_t u3[kWaves];
-  uint32_t u4[kWaves];
-  float f[kWaves];
+  double d[NW];
+  uint32_t u[NW];
+  float f[NW];
   double bd0, bd1;
-  int bi0;
   uint32_t bu0;
 };
 
-__device__ double block_sum_d(double v, Scratch& s) {
+template <int NT>
+__device__ double block_sum_d(double v, Scratch<NT / 64>& s) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (l == 0) s.d[w] = v;
   __syncthreads();
   double t = 0.0;
-  for (int i = 0; i < kWaves; ++i) t += s.d[i];
+  for (int i = 0; i < NT / 64; ++i) t += s.d[i];
   __syncthreads();
   return t;
 }
@@ -158,12 +128,6 @@ __device__ __forceinline__ float load_logit(const void* vec, int dtype, int64_t 
   return ((const float*)vec)[j];
 }
 
-// The slot's draft-token logit (NaN when there is none or it is out of range).
-__device__ __forceinline__ float token_logit(const Slot& s, int dtype, int V) {
-  if (s.token < 0 || s.token >= V) return __uint_as_float(0x7FC00000u);
-  return load_logit(s.vec, dtype, s.token);
-}
-
 // Weight exp((z - m) / T) of one value, formed as the finalize kernel forms
 // it: exp2 of an fp32 argument, c2 = log2(e) / T.  (z - m) is exact for bf16.
 __device__ __forceinline__ double weight(float z, float m, float c2) {
@@ -179,7 +143,7 @@ __device__ void write_record(int token, float T, bool T_ok, int V, float m, floa
     if (token >= V) {
       status |= SV_ROW_BAD_TOKEN;
     } else if (!status && T_ok && kept > 0.0 && zx >= tau) {
-      px = weight(zx, m, (float)(1.4426950408889634 / (double)T)) / kept;
+      px = weight(zx, m, log2e_over_T(T)) / kept;
     }
   } else if (token < -1) {
     status |= SV_ROW_BAD_TOKEN;
@@ -204,20 +168,18 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// All threads of the block call this.  hist256 is LDS of 256 doubles.  Kept
-// out of line: it is the rare path of the bf16 kernel and must not add to
-// that kernel's register budget.  The slot arrives as plain values so that
-// the caller keeps nothing in memory for the call.
-__device__ __attribute__((noinline)) void generic_stats(const void* vec, int token, float T,
-                                                        double P, int dtype, int V,
-                                                        double* hist256, Scratch& sc,
-                                                        VecRec* rec) {
+// All NT threads of the block call this.  hist256 is LDS of 256 doubles.
+// The bf16 kernel reaches it only for a vector its count table cannot hold.
+template <int NT>
+__device__ __forceinline__ void generic_stats(const void* vec, int token, float T, double P,
+                                              int dtype, int V, double* hist256,
+                                              Scratch<NT / 64>& sc, VecRec* rec) {
   const int tid = threadIdx.x;
   const bool T_ok = T > 0.0f && isfinite(T);
   // pass 1: largest finite value, NaN / +inf, any finite entry
   float mx = -INFINITY;
   uint32_t fl = 0, nfin = 0;
-  for (int64_t j = tid; j < V; j += kThreads) {
+  for (int64_t j = tid; j < V; j += NT) {
     const float z = load_logit(vec, dtype, j);
     if (isnan(z) || z == INFINITY) fl |= SV_ROW_NONFINITE_LOGIT;
     else if (z > -INFINITY) { nfin = 1; mx = fmaxf(mx, z); }
@@ -229,7 +191,7 @@ __device__ __attribute__((noinline)) void generic_stats(const void* vec, int tok
   __syncthreads();
   float m = -INFINITY;
   uint32_t flags = 0;
-  for (int i = 0; i < kWaves; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
+  for (int i = 0; i < NT / 64; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
   __syncthreads();
   const float zx = (token >= 0 && token < V) ? load_logit(vec, dtype, token)
                                                : __uint_as_float(0x7FC00000u);
@@ -239,11 +201,11 @@ __device__ __attribute__((noinline)) void generic_stats(const void* vec, int tok
     if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, 0.0, status, zx, rec);
     return;
   }
-  const float c2 = (float)(1.4426950408889634 / (double)T);
+  const float c2 = log2e_over_T(T);
   // pass 2: normaliser S
   double acc = 0.0;
-  for (int64_t j = tid; j < V; j += kThreads) acc += weight(load_logit(vec, dtype, j), m, c2);
-  const double S = block_sum_d(acc, sc);
+  for (int64_t j = tid; j < V; j += NT) acc += weight(load_logit(vec, dtype, j), m, c2);
+  const double S = block_sum_d<NT>(acc, sc);
   if (!(P < 1.0)) {
     if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, S, 0, zx, rec);
     return;
@@ -256,9 +218,9 @@ __device__ __attribute__((noinline)) void generic_stats(const void* vec, int tok
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = tid; i < 256; i += kThreads) hist256[i] = 0.0;
+    for (int i = tid; i < 256; i += NT) hist256[i] = 0.0;
     __syncthreads();
-    for (int64_t j = tid; j < V; j += kThreads) {
+    for (int64_t j = tid; j < V; j += NT) {
       const float z = load_logit(vec, dtype, j);
       if (!(z > -INFINITY)) continue;
       const uint32_t k = order_key(z);
@@ -291,312 +253,476 @@ __device__ __attribute__((noinline)) void generic_stats(const void* vec, int tok
   if (tid == 0) write_record(token, T, T_ok, V, m, key_value(prefix), kept, 0, zx, rec);
 }
 
-__global__ __launch_bounds__(kThreads) void stats_generic_kernel(StatsParams p, int dtype) {
+__global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams p, int dtype) {
   __shared__ double hist256[256];
-  __shared__ Scratch sc;
+  __shared__ Scratch<kGenThreads / 64> sc;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
-  generic_stats(s.vec, s.token, s.T, s.P, dtype, p.V, hist256, sc, p.recs + blockIdx.x);
+  generic_stats<kGenThreads>(s.vec, s.token, s.T, s.P, dtype, p.V, hist256, sc,
+                             p.recs + blockIdx.x);
 }
 
 // ---------------------------------------------------------------- bf16 path
 
-// Splits one table word into the counts of +key (lo) and -key (hi): -0 is
-// folded into +0, -inf carries no mass, +inf and NaN are errors.  Returns
-// flag bits.
-__device__ __forceinline__ uint32_t split_counts(uint32_t x, uint32_t key, uint32_t* lo,
-                                                 uint32_t* hi) {
-  uint32_t l = x & 0xFFFFu, h = x >> 16, fl = 0;
-  if (key == 0) {
-    l += h;
-    h = 0;
-    if (l > 0xFFFFu) { fl |= kFlagWrap; l = 0; }
-  }
-  if (key >= 0x7F80u) {
-    if (l) fl |= SV_ROW_NONFINITE_LOGIT;
-    if (h && key > 0x7F80u) fl |= SV_ROW_NONFINITE_LOGIT;
-    l = 0;
-    h = 0;
-  }
-  *lo = l;
-  *hi = h;
-  return fl;
+constexpr int kT = 256;                  // threads per workgroup
+constexpr int kWv = kT / 64;             // waves per workgroup
+constexpr int kWgPerCu = 3;              // workgroups sharing a CU
+constexpr int kBatch = 4;                // 16-byte loads per thread per batch
+constexpr uint32_t kE0 = 103;            // lowest exponent field in the window (2^-24)
+constexpr int kNE = 40;                  // exponent rows: magnitudes below 2^16
+constexpr uint32_t kBase = kE0 << 7;     // magnitude bits of the window's first word
+constexpr int kWords = kNE * 128;        // 5120 words, 20 KB
+constexpr int kGroups = kWords / 4;      // 16-byte groups of the table
+constexpr int kGpt = kGroups / kT;       // groups per thread
+constexpr int kBins = kGroups / 64;      // bins of 256 magnitudes, per sign
+constexpr int kRankBins = 2 * kBins + 1; // -bins, zero, +bins
+constexpr int kZeroBin = kBins;          // rank bin of the value 0
+static_assert(kGroups % kT == 0 && kGpt * kWv <= kBins * 2, "table tiling");
+static_assert(kBins == kWv * kGpt, "one (wave, row) per bin");
+
+// The streaming loop counts into two copies of the table, lanes of even and
+// odd index into copy 0 and 1.  The logits of one vector take few distinct
+// values (a few hundred, a few dozen of them hot), and an LDS atomic
+// instruction serialises its lanes that hit one address; two copies half as
+// many bank rows apart halve that.  The first epilogue pass merges copy 1
+// into copy 0 and clears copy 1.
+constexpr int kCopies = 2;
+constexpr int kCopyWords = kWords + 16;  // copy 1 starts 16 banks over
+static_assert((kCopyWords * 4) % 16 == 0, "copies are 16-byte aligned");
+
+constexpr uint32_t kFallback = 1u << 30;  // internal: the table cannot hold the vector
+
+// Rank bin of magnitude bin b: +values above zero, -values below.
+__device__ __forceinline__ int pos_bin(int b) { return kZeroBin + 1 + b; }
+__device__ __forceinline__ int neg_bin(int b) { return kZeroBin - 1 - b; }
+
+// Counts logit k of a 16-byte group known to lie in the window.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t k) {
+  const uint32_t word = (k & 0x7FFFu) - kBase;
+  const uint32_t inc = 1u << ((k >> 11) & 16u);
+  __hip_atomic_fetch_add(hist + word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Window test of both logits of a 32-bit word as arithmetic (no branches):
+// the exponent bits less the window's first, unsigned, so that exponents
+// below the window wrap high.  The word lies in the window iff the larger of
+// the two is below kWords (the window is whole exponent rows).
+__device__ __forceinline__ uint32_t window_excess(uint32_t x) {
+  const uint32_t lo = (x & 0x7F80u) - kBase;
+  const uint32_t hi = ((x >> 16) & 0x7F80u) - kBase;
+  return max(lo, hi);
 }
 
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t key16) {
-  const uint32_t word = key16 & 0x7FFFu;
-  const uint32_t inc = 1u << ((key16 >> 11) & 16u);
-  __hip_atomic_fetch_add(hist + word, inc, __ATOMIC_RELAXED,
+// Registers of the out-of-window logits seen by one thread.
+struct Side {
+  uint32_t nzero = 0, nninf = 0, flags = 0;
+};
+
+// Counts logit k when `valid`: in the window into the table, else into the
+// thread's side counters (zero, -inf) or flags (NaN / +inf: error; any other
+// value: fallback).  No branches: the atomic always runs, adding 0 to a word
+// of the thread's own (`spare`) when there is nothing to count.
+__device__ __forceinline__ void count_slow(uint32_t* hist, uint32_t k, bool valid, uint32_t spare,
+                                          Side& sd) {
+  const uint32_t mag = k & 0x7FFFu;
+  const uint32_t word = mag - kBase;
+  const bool inw = valid && word < (uint32_t)kWords;
+  const uint32_t inc = inw ? 1u << ((k >> 11) & 16u) : 0u;
+  __hip_atomic_fetch_add(hist + (inw ? word : spare), inc, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
+  const bool out = valid && !inw;
+  sd.nzero += (out && mag == 0u) ? 1u : 0u;
+  sd.nninf += (out && k == 0xFF80u) ? 1u : 0u;
+  sd.flags |= (out && mag >= 0x7F80u && k != 0xFF80u) ? (uint32_t)SV_ROW_NONFINITE_LOGIT : 0u;
+  sd.flags |= (out && mag != 0u && mag < 0x7F80u) ? kFallback : 0u;
 }
-__device__ __forceinline__ void hist_add8(uint32_t* hist, const uint4& d) {
+
+__device__ __forceinline__ void count_group_fast(uint32_t* hist, const uint4& d) {
   hist_add(hist, d.x & 0xFFFFu); hist_add(hist, d.x >> 16);
   hist_add(hist, d.y & 0xFFFFu); hist_add(hist, d.y >> 16);
   hist_add(hist, d.z & 0xFFFFu); hist_add(hist, d.z >> 16);
   hist_add(hist, d.w & 0xFFFFu); hist_add(hist, d.w >> 16);
 }
-
-// Streams one vector into the count table.  Batches of 4 x 16 bytes per
-// thread; the next batch is loaded before the current one is counted.  Every
-// load is unconditional (indices past the end are clamped, their counts
-// skipped) so the compiler's wait counts let the prefetch stay in flight.
-__device__ __forceinline__ void count_values(const uint16_t* __restrict__ vec, int V,
-                                             uint32_t* hist) {
-  const int tid = threadIdx.x;
-  const uintptr_t addr = (uintptr_t)vec;
-  int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) >> 1);
-  if (head > V) head = V;
-  if (tid < head) hist_add(hist, vec[tid]);
-  const uint4* body = (const uint4*)(vec + head);
-  const int nb = (V - head) >> 3;
-  const int last = nb - 1;
-  const int nbatch = (nb + 4 * kThreads - 1) / (4 * kThreads);
-  if (nbatch > 0) {
-    int i = tid;
-    uint4 a0 = body[min(i, last)];
-    uint4 a1 = body[min(i + kThreads, last)];
-    uint4 a2 = body[min(i + 2 * kThreads, last)];
-    uint4 a3 = body[min(i + 3 * kThreads, last)];
-    for (int k = 0; k < nbatch; ++k) {
-      const int j = (k + 1 < nbatch) ? i + 4 * kThreads : i;
-      const uint4 b0 = body[min(j, last)];
-      const uint4 b1 = body[min(j + kThreads, last)];
-      const uint4 b2 = body[min(j + 2 * kThreads, last)];
-      const uint4 b3 = body[min(j + 3 * kThreads, last)];
-      if (i < nb) hist_add8(hist, a0);
-      if (i + kThreads < nb) hist_add8(hist, a1);
-      if (i + 2 * kThreads < nb) hist_add8(hist, a2);
-      if (i + 3 * kThreads < nb) hist_add8(hist, a3);
-      a0 = b0; a1 = b1; a2 = b2; a3 = b3;
-      i += 4 * kThreads;
-    }
-  }
-  const int t0 = head + (nb << 3);
-  if (t0 + tid < V) hist_add(hist, vec[t0 + tid]);
+__device__ __forceinline__ void count_group_slow(uint32_t* hist, const uint4& d, bool valid,
+                                                uint32_t spare, Side& sd) {
+  count_slow(hist, d.x & 0xFFFFu, valid, spare, sd); count_slow(hist, d.x >> 16, valid, spare, sd);
+  count_slow(hist, d.y & 0xFFFFu, valid, spare, sd); count_slow(hist, d.y >> 16, valid, spare, sd);
+  count_slow(hist, d.z & 0xFFFFu, valid, spare, sd); count_slow(hist, d.z >> 16, valid, spare, sd);
+  count_slow(hist, d.w & 0xFFFFu, valid, spare, sd); count_slow(hist, d.w >> 16, valid, spare, sd);
 }
 
-__global__ __launch_bounds__(kThreads) void stats_bf16_kernel(StatsParams p) {
-  __shared__ __align__(16) uint32_t hist[kHistWords];
-  __shared__ uint32_t list[kListCap];
-  __shared__ uint64_t bins1[256];   // fixed-point mass per (rank >> 8)
-  __shared__ uint64_t bins2[256];   // fixed-point mass per rank inside the crossing bin
-  __shared__ Scratch sc;
+// A full batch holding a logit outside the window (rare).  Out of line, with
+// everything passed by value, so that its register needs do not weigh on the
+// streaming loop.
+static_assert(kBatch == 4, "count_batch_slow takes four groups");
+__device__ __attribute__((noinline)) Side count_batch_slow(uint32_t* hist, uint4 d0, uint4 d1,
+                                                           uint4 d2, uint4 d3, uint32_t spare,
+                                                           Side sd) {
+  count_group_slow(hist, d0, true, spare, sd);
+  count_group_slow(hist, d1, true, spare, sd);
+  count_group_slow(hist, d2, true, spare, sd);
+  count_group_slow(hist, d3, true, spare, sd);
+  return sd;
+}
+
+// Loads one batch: groups i, i + kT, ... of a body with nb > 0; an index
+// past the end is clamped to the last group (loaded, not counted).
+__device__ __forceinline__ void load_batch(uint4 (&d)[kBatch], const uint4* body, int i, int nb) {
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s) d[s] = body[min(i + s * kT, nb - 1)];
+}
+
+// Streams one vector into the table.  Full batches go through the fast path
+// unless a logit of the batch lies outside the window (a wave-uniform test);
+// the last, partial batch and the unaligned head and tail always go through
+// the slow path.  Batch k is counted while batch k + 1 loads.
+__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist, Side& sd) {
+  const int tid = threadIdx.x;
+  const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
+  int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
+  if (head > V) head = V;
+  const uint4* body = (const uint4*)(vec + head);
+  const int nb = (V - head) >> 3;
+  const int t0 = head + (nb << 3);
+  // head and tail logits (a lane without one loads logit 0 and counts nothing)
+  const bool has_head = tid < head, has_tail = t0 + tid < V;
+  const uint32_t xh = vec[has_head ? tid : 0];
+  const uint32_t xt = vec[has_tail ? t0 + tid : 0];
+  if (nb > 0) {
+    const int step = kBatch * kT;
+    const int nfull = nb / step;
+    const bool part = nfull * step < nb;
+    uint4 a[kBatch];
+    load_batch(a, body, tid, nb);
+    int i = tid;
+    for (int k = 0; k < nfull; ++k) {
+      uint4 n[kBatch];
+      load_batch(n, body, (k + 1 < nfull || part) ? i + step : i, nb);
+      uint32_t ex = 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        ex = max(ex, max(max(window_excess(a[q].x), window_excess(a[q].y)),
+                         max(window_excess(a[q].z), window_excess(a[q].w))));
+      if (!__any(ex >= (uint32_t)kWords)) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) count_group_fast(hist, a[q]);
+      } else {
+        sd = count_batch_slow(hist, a[0], a[1], a[2], a[3], spare, sd);
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) a[q] = n[q];
+      i += step;
+    }
+    if (part) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) count_group_slow(hist, a[q], i + q * kT < nb, spare, sd);
+    }
+  }
+  count_slow(hist, xh, has_head, spare, sd);
+  count_slow(hist, xt, has_tail, spare, sd);
+}
+
+// Whether the call uses slot v (reads k_per_row only when it is given).
+__device__ __forceinline__ bool slot_needed(const StatsParams& p, int v) {
+  const int per = slots_per_row(p.K);
+  const int b = v / per, j = v % per;
+  const int kb = p.k_per_row ? p.k_per_row[b] : p.K;
+  if (kb < 1 || kb > p.K) return false;
+  if (j <= p.K) return j <= kb && p.mode != 1;
+  return j - p.K - 1 < kb;
+}
+
+// Next used slot from the ticket counter (nslots or more: none left).
+__device__ __forceinline__ int take_ticket(const StatsParams& p, int nslots) {
+  int v;
+  do {
+    v = (int)atomicAdd(p.ticket, 1u);
+  } while (v < nslots && !slot_needed(p, v));
+  return v;
+}
+
+// A used slot's vector and parameters (the fields of slot_of).  The vector
+// address is arithmetic; the loads are issued together and nothing branches
+// on them.
+struct SlotP {
+  const uint16_t* vec;
+  int token;
+  float T;
+  double P;
+};
+
+__device__ __forceinline__ SlotP slot_params(const StatsParams& p, int v) {
+  const int K = p.K, per = slots_per_row(K);
+  const int b = v / per, j = v % per;
+  const bool draft_side = j > K;
+  const int i = draft_side ? j - K - 1 : j;
+  SlotP s;
+  s.vec = draft_side ? (const uint16_t*)p.draft + ((int64_t)b * K + i) * p.d_stride
+                     : (const uint16_t*)p.target + ((int64_t)b * (K + 1) + i) * p.t_stride;
+  // pointers that may be NULL are swapped for a valid dummy before loading
+  const float* Tp = p.temperature + b;
+  const int32_t* tokp = p.tokens ? p.tokens + (int64_t)b * K + min(i, K - 1) : (const int32_t*)Tp;
+  const int32_t* kbp = p.k_per_row ? p.k_per_row + b : (const int32_t*)Tp;
+  const float* Pp = p.top_p ? p.top_p + b : Tp;
+  const int tok = *tokp, kbl = *kbp;
+  const float T = *Tp, Pl = *Pp;
+  const int kb = p.k_per_row ? kbl : K;
+  s.token = (p.mode == 1 || (!draft_side && i >= kb)) ? -1 : tok;
+  s.T = T;
+  double P = p.top_p ? (double)Pl : 1.0;
+  if (!(P > 0.0)) P = 1.0;  // invalid top-p is flagged by the finalize kernel
+  if (draft_side && (p.flags & SV_FLAG_TOPP_TARGET_ONLY)) P = 1.0;
+  s.P = P;
+  return s;
+}
+
+struct Bf16Shared {
+  int wmaxpos[kWv], wminneg[kWv];
+  uint32_t wtot[kWv], wzero[kWv], wninf[kWv], wflag[kWv], wwrap[kWv];
+  int next;
+};
+
+// Level 2 of the top-p search, run by one wave: the 256 magnitudes of bin b
+// of one sign, walked from the largest value down.  `above` is the mass of
+// all larger values.  Returns the threshold value and the kept mass through
+// it (wave-uniform).
+__device__ __forceinline__ void crossing_value(const uint4* hist4, int b, bool pos, double above,
+                                               double target, float m, float c2, float* tau,
+                                               double* kept) {
+  const int l = threadIdx.x & 63;
+  // lanes ascending = values descending: +values from the top magnitude
+  // down, -values from the bottom magnitude up
+  const int grp = b * 64 + (pos ? 63 - l : l);
+  const uint4 g = hist4[grp];
+  const uint32_t xs[4] = {pos ? g.w : g.x, pos ? g.z : g.y, pos ? g.y : g.z, pos ? g.x : g.w};
+  double mass[4];
+  uint32_t keys[4];
+  double part = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = 4u * (uint32_t)grp + (uint32_t)(pos ? 3 - i : i);
+    const uint32_t c = pos ? (xs[i] & 0xFFFFu) : (xs[i] >> 16);
+    keys[i] = (word + kBase) | (pos ? 0u : 0x8000u);
+    mass[i] = c ? (double)c * weight(bf16f(keys[i]), m, c2) : 0.0;
+    part += mass[i];
+  }
+  const double incl = wave_scan_add_f64(part);
+  const uint64_t hit = __ballot(part > 0.0 && above + incl >= target);
+  const uint64_t any = __ballot(part > 0.0);
+  // the caller's bin has mass, so some lane has; lane 0 if rounding says not
+  const int L = hit ? __builtin_ctzll(hit) : any ? 63 - __builtin_clzll(any) : 0;
+  // in lane L: the first value whose inclusive mass reaches the target (the
+  // last present value if rounding left the target just out of reach)
+  double cum = above + (incl - part);
+  uint32_t sel = 0xFFFFFFFFu;
+  double sel_kept = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (mass[i] > 0.0) {
+      cum += mass[i];
+      if (sel == 0xFFFFFFFFu && cum >= target) { sel = keys[i]; sel_kept = cum; }
+    }
+  }
+  if (sel == 0xFFFFFFFFu) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (mass[i] > 0.0) sel = keys[i];
+    sel_kept = cum;
+  }
+  const uint32_t key = (uint32_t)__builtin_amdgcn_readlane((int)sel, L);
+  const uint64_t kb = (uint64_t)__double_as_longlong(sel_kept);
+  const uint32_t klo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kb, L);
+  const uint32_t khi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kb >> 32), L);
+  *tau = bf16f(key);
+  *kept = __longlong_as_double((long long)(((uint64_t)khi << 32) | klo));
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int L) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, L);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), L);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p) {
+  __shared__ __align__(16) uint32_t hist[kCopies * kCopyWords];
+  __shared__ double bins[kRankBins];
+  __shared__ Bf16Shared sh;
+  __shared__ double hist256[256];       // generic path
+  __shared__ Scratch<kWv> sc;           // generic path
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int V = p.V;
   const int nslots = p.B * slots_per_row(p.K);
   uint4* hist4 = reinterpret_cast<uint4*>(hist);
 
-  for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
-  if (tid < 256) { bins1[tid] = 0; bins2[tid] = 0; }
+  for (int i = tid; i < kCopies * kCopyWords; i += kT) hist[i] = 0;
+  uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
+  const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
+  if (tid == 0) sh.next = take_ticket(p, nslots);
   __syncthreads();
+  int v = sh.next;
+  if (v >= nslots) return;
+  SlotP cur = slot_params(p, v);
 
-  for (int v = blockIdx.x; v < nslots; v += gridDim.x) {
-    const Slot s = slot_of(p, SV_BF16, v);
-    if (!s.needed) continue;
+  for (;;) {
+    __syncthreads();  // every thread has read sh.next
+    if (tid == 0) sh.next = take_ticket(p, nslots);
+    const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
-    const float zx = tid == 0 ? token_logit(s, SV_BF16, V) : 0.0f;
+    // the draft token's logit, loaded by every thread from one address
+    const bool has_zx = cur.token >= 0 && cur.token < V;
+    const uint32_t zbits = cur.vec[has_zx ? cur.token : 0];
 
-    count_values((const uint16_t*)s.vec, V, hist);
-    __syncthreads();
+    Side sd;
+    stream_vector(cur.vec, V, hcopy, sd);
+    {
+      const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nzero));
+      const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nninf));
+      const uint32_t f = wave_last_u32(wave_scan_u32<OpOrU32>(sd.flags));
+      if (l == 0) { sh.wzero[w] = z; sh.wninf[w] = n; sh.wflag[w] = f; }
+    }
+    __syncthreads();  // B1: table complete
+    const int vn = sh.next;
+    const bool has_next = vn < nslots;
+    const SlotP nxt = slot_params(p, has_next ? vn : v);  // loads in flight meanwhile
 
-    // ---- E1: thread t reads the 16-byte groups t + 1024 j (j < 8) of the
-    // table: conflict-free, and a dense range of values spreads over many
-    // threads.  Word w counts +w in its low half (rank 32768 + w) and -w in
-    // its high half (rank 32767 - w).  Only groups holding a count are
-    // looked at; jmask remembers them for the second pass.
-    uint32_t fl = 0, total = 0, nfin = 0, nent = 0, jmask = 0;
-    int maxr = -1;
+    // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
+    // and clears copy 1; largest +magnitude, smallest -magnitude present,
+    // total count, and whether a merged count passed 16 bits
+    uint32_t gmask = 0, total = 0, wrap = 0;
+    int maxpos = -1, minneg = 0x7FFFFFFF;
 #pragma unroll 1
-    for (int j = 0; j < 8; ++j) {
-      const uint4 g = hist4[tid + 1024 * j];
-      if (!(g.x | g.y | g.z | g.w)) continue;
-      jmask |= 1u << j;
-      const uint32_t xs[4] = {g.x, g.y, g.z, g.w};
+    for (int j = 0; j < kGpt; ++j) {
+      const int g = tid + kT * j;
+      const uint4 d0 = hist4[g], d1 = copy1[g];
+      const uint32_t a0[4] = {d0.x, d0.y, d0.z, d0.w};
+      const uint32_t a1[4] = {d1.x, d1.y, d1.z, d1.w};
+      uint32_t xs[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t x = xs[q];
-        if (!x) continue;
-        const uint32_t key = 4u * (tid + 1024u * j) + q;
-        total += (x & 0xFFFFu) + (x >> 16);
-        uint32_t lo, hi;
-        fl |= split_counts(x, key, &lo, &hi);
-        nfin += lo + hi;
-        nent += (lo != 0) + (hi != 0);
-        if (lo) maxr = max(maxr, 32768 + (int)key);
-        if (hi) maxr = max(maxr, 32767 - (int)key);
+        const uint32_t lo = (a0[q] & 0xFFFFu) + (a1[q] & 0xFFFFu);
+        const uint32_t hi = (a0[q] >> 16) + (a1[q] >> 16);
+        wrap |= (lo | hi) >> 16;
+        xs[q] = (hi << 16) | (lo & 0xFFFFu);
+        const int word = 4 * g + q;
+        total += lo + hi;
+        if (lo) maxpos = max(maxpos, word);
+        if (hi) minneg = min(minneg, word);
       }
+      if (d1.x | d1.y | d1.z | d1.w) {
+        hist4[g] = make_uint4(xs[0], xs[1], xs[2], xs[3]);
+        reinterpret_cast<uint4*>(hist + kCopyWords)[g] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      if (xs[0] | xs[1] | xs[2] | xs[3]) gmask |= 1u << j;
     }
-    // block: exclusive scan of entry counts (thread order), flags, totals, max
-    const uint32_t einc = wave_scan_u32<OpAddU32>(nent);
     {
-      const uint32_t etot = wave_last_u32(einc);
-      const int wmax = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)maxr));
-      const uint32_t wor = wave_last_u32(wave_scan_u32<OpOrU32>(fl));
-      const uint32_t wtot = wave_last_u32(wave_scan_u32<OpAddU32>(total));
-      const uint32_t wfin = wave_last_u32(wave_scan_u32<OpAddU32>(nfin));
-      if (l == 0) {
-        sc.i[w] = wmax;
-        sc.u[w] = wor;
-        sc.u2[w] = wtot;
-        sc.u4[w] = wfin;
-        sc.u3[w] = etot;
-      }
+      const int a = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)maxpos));
+      const int b = (int)wave_last_u32(wave_scan_u32<OpMinI32>((uint32_t)minneg));
+      const uint32_t t = wave_last_u32(wave_scan_u32<OpAddU32>(total));
+      const uint32_t x = wave_last_u32(wave_scan_u32<OpOrU32>(wrap));
+      if (l == 0) { sh.wmaxpos[w] = a; sh.wminneg[w] = b; sh.wtot[w] = t; sh.wwrap[w] = x; }
     }
-    __syncthreads();
-    int MR = -1;
-    uint32_t F = 0, TT = 0, N = 0, ebefore = 0, ND = 0;
-    for (int k = 0; k < kWaves; ++k) {
-      MR = max(MR, sc.i[k]);
-      F |= sc.u[k];
-      TT += sc.u2[k];
-      N += sc.u4[k];
-      if (k < w) ebefore += sc.u3[k];
-      ND += sc.u3[k];
+    __syncthreads();  // B2
+    int MP = -1, MN = 0x7FFFFFFF;
+    uint32_t TT = 0, Z = 0, NI = 0, FL = 0, WR = 0;
+#pragma unroll
+    for (int k = 0; k < kWv; ++k) {
+      MP = max(MP, sh.wmaxpos[k]);
+      MN = min(MN, sh.wminneg[k]);
+      TT += sh.wtot[k];
+      Z += sh.wzero[k];
+      NI += sh.wninf[k];
+      FL |= sh.wflag[k];
+      WR |= sh.wwrap[k];
     }
-    __syncthreads();
-    if (TT != (uint32_t)V || (F & kFlagWrap) || ND > (uint32_t)kListCap) {
-      // a 16-bit count wrapped (or too many distinct values to list): redo
-      // the vector exactly on the generic path, borrowing the table
-      generic_stats(s.vec, s.token, s.T, s.P, SV_BF16, V, reinterpret_cast<double*>(hist),
-                    sc, rec);
-      __syncthreads();
-      for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
-      __syncthreads();
-      continue;
-    }
-    uint32_t status = F & SV_ROW_NONFINITE_LOGIT;
-    if (N == 0) status |= SV_ROW_NO_FINITE;
-    const float m = MR >= 0 ? bf16f(rank_key(MR)) : -INFINITY;
-    const bool stats_ok = !status && s.T_ok;
+    uint32_t status = FL & SV_ROW_NONFINITE_LOGIT;
+    // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
+    // count past 65535), or a logit outside the window: the generic path
+    // redoes the vector
+    const bool fallback = !status && ((FL & kFallback) || WR || TT + Z + NI != (uint32_t)V);
+    if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
+    const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
+                  : Z > 0   ? 0.0f
+                  : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
+                                    : -INFINITY;
+    const bool stats_ok = !fallback && !status && T_ok;
+    const float c2 = log2e_over_T(cur.T);
 
-    // ---- E2: second pass over the same groups: list entries (rank << 16 |
-    // count) at this thread's scanned offset, and the table cleared for the
-    // next vector.
-    {
-      uint32_t o = ebefore + (einc - nent);
+    // ---- E2: masses of the values of each (wave, row) bin: wave w with row
+    // j owns magnitude bin w + kWv j of both signs
+    if (stats_ok) {
 #pragma unroll 1
-      for (int j = 0; j < 8; ++j) {
-        if (!((jmask >> j) & 1u)) continue;
-        const uint4 g = hist4[tid + 1024 * j];
-        hist4[tid + 1024 * j] = make_uint4(0u, 0u, 0u, 0u);
-        if (!stats_ok) continue;
-        const uint32_t xs[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (!xs[q]) continue;
-          const uint32_t key = 4u * (tid + 1024u * j) + q;
-          uint32_t lo, hi;
-          split_counts(xs[q], key, &lo, &hi);
-          if (lo) list[o++] = ((uint32_t)(32768 + (int)key) << 16) | lo;
-          if (hi) list[o++] = ((uint32_t)(32767 - (int)key) << 16) | hi;
-        }
-      }
-    }
-    if (!stats_ok) {
-      if (tid == 0) write_record(s.token, s.T, s.T_ok, V, m, -INFINITY, 0.0, status, zx, rec);
-      __syncthreads();
-      continue;
-    }
-    __syncthreads();
-
-    // ---- E3: mass of each listed value, count * exp((v - m)/T), as a 64-bit
-    // fixed-point number (scale 2^45; a vector's total stays below 2^63);
-    // integer sums are exact in any order, so the results do not depend on
-    // the schedule.  Coarse bins by rank >> 8 for the top-p search.
-    const float c2 = (float)(1.4426950408889634 / (double)s.T);
-    for (uint32_t e = tid; e < ND; e += kThreads) {
-      const uint32_t ent = list[e];
-      const uint32_t r = ent >> 16;
-      const double mass = (double)(ent & 0xFFFFu) * weight(bf16f(rank_key((int)r)), m, c2);
-      const uint64_t fx = (uint64_t)(mass * kFixScale + 0.5);
-      if (fx) atomicAdd((unsigned long long*)&bins1[r >> 8], (unsigned long long)fx);
-    }
-    __syncthreads();
-
-    // ---- E4: wave 0 walks the 256 coarse bins from the top: total S, and
-    // the bin where the mass above reaches top_p * S.
-    if (w == 0) {
-      // lane l holds bins 255-4l .. 252-4l (descending)
-      uint64_t b[4];
-      double part = 0.0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        b[q] = bins1[255 - 4 * l - q];
-        bins1[255 - 4 * l - q] = 0;
-        part += (double)b[q];
-      }
-      const double incl = wave_scan_add_f64(part);   // lanes ascending = bins descending
-      const double S_fix = wave_last_f64(incl);
-      double above = incl - part;                    // mass of all higher bins
-      if (l == 0) { sc.bd0 = S_fix; sc.bi0 = -1; }
-      if (s.P < 1.0) {
-        const double target = s.P * S_fix;
-        if (above < target && above + part >= target) {
-          double cum = above;
+      for (int j = 0; j < kGpt; ++j) {
+        const int g = tid + kT * j;
+        const int b = w + kWv * j;
+        double mp = 0.0, mn = 0.0;
+        if ((gmask >> j) & 1u) {
+          const uint4 d = hist4[g];
+          const uint32_t xs[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (cum + (double)b[q] >= target && b[q]) {
-              sc.bi0 = 255 - 4 * l - q;
-              sc.bd1 = cum;
-              break;
-            }
-            cum += (double)b[q];
+            const uint32_t key = 4u * (uint32_t)g + (uint32_t)q + kBase;
+            const uint32_t lo = xs[q] & 0xFFFFu, hi = xs[q] >> 16;
+            if (lo) mp += (double)lo * weight(bf16f(key), m, c2);
+            if (hi) mn += (double)hi * weight(bf16f(key | 0x8000u), m, c2);
           }
         }
-      }
-    }
-    __syncthreads();
-    const double S_fix = sc.bd0;
-    float tau = -INFINITY;
-    double kept_fix = S_fix;
-    if (s.P < 1.0 && sc.bi0 >= 0) {
-      // level 2: the values of the crossing bin, each in its own slot
-      const int b1 = sc.bi0;
-      for (uint32_t e = tid; e < ND; e += kThreads) {
-        const uint32_t ent = list[e];
-        const uint32_t r = ent >> 16;
-        if ((int)(r >> 8) != b1) continue;
-        const double mass = (double)(ent & 0xFFFFu) * weight(bf16f(rank_key((int)r)), m, c2);
-        bins2[r & 255u] = (uint64_t)(mass * kFixScale + 0.5);
-      }
-      __syncthreads();
-      if (w == 0) {
-        uint64_t b[4];
-        double part = 0.0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          b[q] = bins2[255 - 4 * l - q];
-          bins2[255 - 4 * l - q] = 0;
-          part += (double)b[q];
+        if (__ballot((gmask >> j) & 1u)) {
+          mp = wave_last_f64(wave_scan_add_f64(mp));
+          mn = wave_last_f64(wave_scan_add_f64(mn));
         }
+        if (l == 0) { bins[pos_bin(b)] = mp; bins[neg_bin(b)] = mn; }
+      }
+      if (tid == 0) bins[kZeroBin] = Z ? (double)Z * weight(0.0f, m, c2) : 0.0;
+    }
+    __syncthreads();  // B3: bins written
+
+    // ---- wave 0: S and the top-p threshold in two levels, then the record
+    if (w == 0 && !fallback) {
+      double S = 0.0, kept = 0.0;
+      float tau = -INFINITY;
+      if (stats_ok) {
+        // lane l holds rank bin kRankBins - 1 - l (values descending)
+        const int R = kRankBins - 1 - l;
+        const double part = R >= 0 ? bins[R] : 0.0;
         const double incl = wave_scan_add_f64(part);
-        const double above = sc.bd1 + (incl - part);
-        const double target = s.P * S_fix;
-        if (l == 0) sc.bu0 = 0xFFFFFFFFu;
-        if (above < target && above + part >= target) {
-          double cum = above;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (b[q] && cum + (double)b[q] >= target) {
-              sc.bu0 = (uint32_t)(b1 << 8) | (uint32_t)(255 - 4 * l - q);
-              sc.bd0 = cum + (double)b[q];
-              break;
-            }
-            cum += (double)b[q];
+        S = wave_last_f64(incl);
+        kept = S;
+        if (cur.P < 1.0) {
+          const double target = cur.P * S;
+          const uint64_t hit = __ballot(part > 0.0 && incl >= target);
+          const uint64_t any = __ballot(part > 0.0);
+          // S > 0 (the maximum has weight 1), so some lane has mass
+          const int L = hit ? __builtin_ctzll(hit) : any ? 63 - __builtin_clzll(any) : 0;
+          const int RL = kRankBins - 1 - L;
+          const double above = readlane_f64(incl - part, L);
+          if (RL == kZeroBin) {
+            tau = 0.0f;
+            kept = above + readlane_f64(part, L);
+          } else if (RL > kZeroBin) {
+            crossing_value(hist4, RL - kZeroBin - 1, true, above, target, m, c2, &tau, &kept);
+          } else if (RL >= 0) {
+            crossing_value(hist4, kZeroBin - 1 - RL, false, above, target, m, c2, &tau, &kept);
           }
         }
       }
-      __syncthreads();
-      if (sc.bu0 != 0xFFFFFFFFu) {
-        tau = bf16f(rank_key((int)sc.bu0));
-        kept_fix = sc.bd0;
-      }
+      if (tid == 0)
+        write_record(cur.token, cur.T, T_ok, V, m, tau, kept, status,
+                     has_zx ? bf16f(zbits) : __uint_as_float(0x7FC00000u), rec);
     }
-    if (tid == 0)
-      write_record(s.token, s.T, s.T_ok, V, m, tau, kept_fix * (1.0 / kFixScale), 0, zx, rec);
-    __syncthreads();  // scratch and list are reused by the next vector
+    if (fallback) {
+      generic_stats<kT>(cur.vec, cur.token, cur.T, cur.P, SV_BF16, V, hist256, sc, rec);
+    }
+    __syncthreads();  // B4: the table is no longer read
+#pragma unroll 1
+    for (int j = 0; j < kGpt; ++j)
+      if ((gmask >> j) & 1u) hist4[tid + kT * j] = make_uint4(0u, 0u, 0u, 0u);
+    if (!has_next) break;
+    v = vn;
+    cur = nxt;
   }
 }
+
+__global__ void stats_ticket_reset_kernel(uint32_t* ticket) { *ticket = 0u; }
 
 }  // namespace
 
@@ -605,12 +731,14 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
   if (nslots == 0) return hipSuccess;
   if (dtype == SV_BF16) {
     const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
-    const unsigned grid = nslots < cus ? nslots : cus;
+    const unsigned want = cus * (unsigned)kWgPerCu;
+    const unsigned grid = nslots < want ? nslots : want;
+    hipLaunchKernelGGL(stats_ticket_reset_kernel, dim3(1), dim3(1), 0, s, p.ticket);
     TimedScope ts(t, "stats_bf16", s);
-    hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, p);
   } else {
     TimedScope ts(t, "stats_generic", s);
-    hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kThreads), 0, s, p, dtype);
+    hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kGenThreads), 0, s, p, dtype);
   }
   return hipGetLastError();
 }

@@ -10,6 +10,15 @@
 
 namespace sv {
 
+// log2(e) / T, the factor that turns (z - m) into an exp2 argument, as fp32.
+// A positive T so small that the factor overflows fp32 is given the largest
+// finite float instead: (m - m) * c2 stays 0 (weight 1 for the maximum) and
+// every smaller logit still gets weight 0, as in exact arithmetic.
+__device__ __forceinline__ float log2e_over_T(float T) {
+  const double c = 1.4426950408889634 / (double)T;
+  return c < 3.4028234663852886e38 ? (float)c : 3.4028234663852886e38f;
+}
+
 // Per-vector statistics written by the stats kernels and read by the
 // finalize kernel.  One record per (row, side, position) slot.
 struct VecRec {
@@ -60,6 +69,7 @@ struct StatsParams {
   uint32_t flags;
   int32_t mode;  // 0 verification (all slots), 1 draft sampling (draft slots only)
   VecRec* recs;
+  uint32_t* ticket;  // vector counter of the persistent bf16 kernel (workspace)
 };
 
 struct FinalizeParams {

@@ -45,6 +45,12 @@ struct OpMaxI32 {
     return (uint32_t)max((int)a, (int)b);
   }
 };
+struct OpMinI32 {
+  __device__ static uint32_t ident() { return 0x7FFFFFFFu; }  // INT_MAX
+  __device__ static uint32_t f(uint32_t a, uint32_t b) {
+    return (uint32_t)min((int)a, (int)b);
+  }
+};
 struct OpOrU32 {
   __device__ static uint32_t ident() { return 0u; }
   __device__ static uint32_t f(uint32_t a, uint32_t b) { return a | b; }
