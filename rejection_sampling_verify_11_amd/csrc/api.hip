@@ -83,12 +83,14 @@ constexpr int32_t kMaxVSampled = SV_MAX_V_SAMPLED;  // inverse-CDF segment table
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-vector records, then the ticket counter of the bf16 stats kernel.
+// Per-vector records, then the queue counters of the bf16 stats kernel.
 size_t recs_bytes(int32_t B, int32_t K) {
   return align_up((size_t)B * sv::slots_per_row(K) * sizeof(sv::VecRec), 256);
 }
 
-size_t sample_ws(int32_t B, int32_t K) { return recs_bytes(B, K) + 256; }
+size_t sample_ws(int32_t B, int32_t K) {
+  return recs_bytes(B, K) + align_up(sv::stats_ticket_bytes(), 256);
+}
 
 size_t greedy_ws(int32_t B, int32_t K, int32_t V) {
   return align_up((size_t)B * (2 * (size_t)K + 1) * sv::greedy_chunks(V) * sizeof(sv::ArgmaxPart), 256);
@@ -204,7 +206,7 @@ static sv::StatsParams stats_params(const sv_verify_args* a, int mode) {
   p.flags = a->flags;
   p.mode = mode;
   p.recs = (sv::VecRec*)a->workspace;
-  p.ticket = (uint32_t*)((char*)a->workspace + recs_bytes(a->B, a->k_max));
+  p.tickets = (uint32_t*)((char*)a->workspace + recs_bytes(a->B, a->k_max));
   return p;
 }
 

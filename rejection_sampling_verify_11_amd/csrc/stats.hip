@@ -22,9 +22,9 @@
 // counted in registers; NaN and +inf mark the row as an error.  Any other
 // logit outside the window, or a count that wraps its 16 bits (65536 equal
 // logits), sends the vector down the generic path.  The small table lets
-// four workgroups share a CU, so one workgroup's epilogue (no memory traffic)
-// overlaps the others' streaming; vectors are handed out by a ticket
-// counter.  LDS atomics, not HBM, bound the streaming loop.
+// three workgroups share a CU, so one workgroup's epilogue (no memory traffic)
+// overlaps the others' streaming; vectors are handed out from queues
+// (below) so that the workgroups of a CU do not stay in step.
 //
 // Generic path (fp32 logits, or a bf16 vector the table cannot hold): passes
 // over the vector in global memory: max, fp64 sum, then a 4-pass radix select
@@ -431,11 +431,25 @@ __device__ __forceinline__ bool slot_needed(const StatsParams& p, int v) {
   return j - p.K - 1 < kb;
 }
 
-// Next used slot from the ticket counter (nslots or more: none left).
-__device__ __forceinline__ int take_ticket(const StatsParams& p, int nslots) {
+// Vectors are handed out dynamically: a workgroup that finishes early takes
+// the next vector, so the workgroups of a CU drift apart and one's epilogue
+// overlaps the others' streaming (a fixed schedule keeps them in step).  One
+// counter for all would queue hundreds of device-scope atomics on a single
+// address, so the vectors are split into kQueues interleaved queues (queue q
+// holds vectors q, q + kQueues, ...), each with its own counter 128 bytes
+// apart and served by the workgroups g with g % kQueues == q.  Ticket t of
+// queue q is vector q + kQueues t; workgroup g's first ticket is g / kQueues
+// (no atomic) and each counter starts at its queue's number of workgroups.
+constexpr int kQueues = 64;
+constexpr int kQueueStride = 32;  // uint32 words between counters
+
+__device__ __forceinline__ int queue_slot(int q, uint32_t t) { return q + kQueues * (int)t; }
+
+// Next used slot of queue q from its counter (nslots or more: none left).
+__device__ __forceinline__ int take_ticket(const StatsParams& p, int q, int nslots) {
   int v;
   do {
-    v = (int)atomicAdd(p.ticket, 1u);
+    v = queue_slot(q, atomicAdd(p.tickets + q * kQueueStride, 1u));
   } while (v < nslots && !slot_needed(p, v));
   return v;
 }
@@ -557,15 +571,19 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   for (int i = tid; i < kCopies * kCopyWords; i += kT) hist[i] = 0;
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
-  if (tid == 0) sh.next = take_ticket(p, nslots);
-  __syncthreads();
-  int v = sh.next;
-  if (v >= nslots) return;
+  const int queue = (int)(blockIdx.x % kQueues);
+  int v = queue_slot(queue, blockIdx.x / kQueues);
+  if (v >= nslots || !slot_needed(p, v)) {
+    if (tid == 0) sh.next = take_ticket(p, queue, nslots);
+    __syncthreads();
+    v = sh.next;
+    if (v >= nslots) return;
+  }
   SlotP cur = slot_params(p, v);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
-    if (tid == 0) sh.next = take_ticket(p, nslots);
+    if (tid == 0) sh.next = take_ticket(p, queue, nslots);
     const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
     // the draft token's logit, loaded by every thread from one address
@@ -722,18 +740,29 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   }
 }
 
-__global__ void stats_ticket_reset_kernel(uint32_t* ticket) { *ticket = 0u; }
+// Counter q starts at the number of workgroups serving queue q (their first
+// tickets are taken without it).
+__global__ void stats_queue_reset_kernel(uint32_t* tickets, uint32_t grid) {
+  const uint32_t q = threadIdx.x;
+  if (q < (uint32_t)kQueues)
+    tickets[q * kQueueStride] = grid > q ? (grid - q + kQueues - 1) / kQueues : 0u;
+}
 
 }  // namespace
+
+size_t stats_ticket_bytes() { return (size_t)kQueues * kQueueStride * sizeof(uint32_t); }
 
 hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_t s, Timer* t) {
   const unsigned nslots = (unsigned)p.B * (unsigned)slots_per_row(p.K);
   if (nslots == 0) return hipSuccess;
   if (dtype == SV_BF16) {
     const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
-    const unsigned want = cus * (unsigned)kWgPerCu;
+    // every queue needs a workgroup: at least kQueues of them (or one per
+    // vector); extra workgroups simply wait for a free CU
+    unsigned want = cus * (unsigned)kWgPerCu;
+    if (want < (unsigned)kQueues) want = (unsigned)kQueues;
     const unsigned grid = nslots < want ? nslots : want;
-    hipLaunchKernelGGL(stats_ticket_reset_kernel, dim3(1), dim3(1), 0, s, p.ticket);
+    hipLaunchKernelGGL(stats_queue_reset_kernel, dim3(1), dim3(kQueues), 0, s, p.tickets, grid);
     TimedScope ts(t, "stats_bf16", s);
     hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, p);
   } else {

@@ -69,8 +69,11 @@ struct StatsParams {
   uint32_t flags;
   int32_t mode;  // 0 verification (all slots), 1 draft sampling (draft slots only)
   VecRec* recs;
-  uint32_t* ticket;  // vector counter of the persistent bf16 kernel (workspace)
+  uint32_t* tickets;  // queue counters of the bf16 kernel (workspace, after the records)
 };
+
+// Bytes of workspace the bf16 stats kernel keeps its queue counters in.
+size_t stats_ticket_bytes();
 
 struct FinalizeParams {
   const void* target;
