@@ -20,6 +20,7 @@
 
 #include "philox.h"
 #include "sv_internal.h"
+#include "wave_ops.h"
 
 namespace sv {
 namespace {
@@ -34,6 +35,7 @@ struct Dist {
   const void* vec;
   float m, tau, c2;  // c2 = log2(e) / T
   double inv;
+  float invf;        // inv as fp32 (the bf16 fast path)
 };
 
 // Loads 8 consecutive logits starting at j0 (elements >= V read as -inf).
@@ -70,6 +72,13 @@ __device__ __forceinline__ double prob(const Dist& d, float z) {
   return (double)__builtin_amdgcn_exp2f((z - d.m) * d.c2) * d.inv;
 }
 
+// The same probability in fp32: exp2 is an fp32 operation anyway, and the
+// residual max(0, p' - q') of two such values is within a few ulp of p' and
+// q'; sums are still taken in fp64.
+__device__ __forceinline__ float prob_f(const Dist& d, float z) {
+  return z >= d.tau ? __builtin_amdgcn_exp2f((z - d.m) * d.c2) * d.invf : 0.0f;
+}
+
 // r_j for the 8 logits at j0: residual max(0, p' - q') (mode 0) or p' (mode 1).
 __device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int dtype,
                                    int64_t j0, int V, bool aligned, double r[8]) {
@@ -101,12 +110,183 @@ __device__ __forceinline__ bool is_aligned16(const void* p) {
   return (((uintptr_t)p) & 15u) == 0;
 }
 
+// ---- bf16 fast path: 16-byte aligned vectors with V a multiple of 8.
+// Groups of kGroupTok tokens; in group G wave w owns the kSegTok contiguous
+// tokens G kGroupTok + kSegTok w + [0, kSegTok) (one segment), lane l the
+// 8-token chunks at 512 s + 8 l (s < kCps), so every wave load is 1 KB
+// contiguous.  Pass 1 loads group G + 1 while it sums group G.
+constexpr int kCps = 2;                    // chunks per lane per segment
+constexpr int kSegTok = 512 * kCps;
+constexpr int kGroupTok = kWaves * kSegTok;
+
+// MODE 0: residual max(0, p' - q'); MODE 1: p' alone.
+template <int MODE>
+struct Chunks {
+  uint4 p[kCps];
+  uint4 q[MODE == 0 ? kCps : 1];
+};
+
+// Loads the chunks of this lane in segment `seg` (chunk indices past the last
+// clamp to it; their values are masked by the caller).
+template <int MODE>
+__device__ __forceinline__ void load_segment(Chunks<MODE>& c, const uint16_t* P, const uint16_t* Q,
+                                             int seg, int nchunks) {
+  const int l = threadIdx.x & 63;
+  const int c0 = seg * (kSegTok / 8) + l;
+#pragma unroll
+  for (int s = 0; s < kCps; ++s) {
+    const int ci = min(c0 + 64 * s, nchunks - 1);
+    c.p[s] = *(const uint4*)(P + 8 * (int64_t)ci);
+    if (MODE == 0) c.q[s] = *(const uint4*)(Q + 8 * (int64_t)ci);
+  }
+}
+
+// r of the 8 tokens of chunk s (0 where the chunk lies past the end).
+template <int MODE>
+__device__ __forceinline__ void chunk_r(const Dist& Pd, const Dist& Qd, const Chunks<MODE>& c, int s,
+                                        bool valid, double r[8]) {
+  const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float zp = __uint_as_float(t & 1 ? (pw[t >> 1] & 0xFFFF0000u) : (pw[t >> 1] << 16));
+    float v = prob_f(Pd, zp);
+    if (MODE == 0) {
+      const uint32_t qw = t < 2 ? c.q[s].x : t < 4 ? c.q[s].y : t < 6 ? c.q[s].z : c.q[s].w;
+      const float zq = __uint_as_float(t & 1 ? (qw & 0xFFFF0000u) : (qw << 16));
+      v = fmaxf(v - prob_f(Qd, zq), 0.0f);
+    }
+    r[t] = valid ? (double)v : 0.0;
+  }
+}
+
+// Sum of r over the chunks of this lane in segment seg, summed over the wave
+// and stored as the segment's mass.
+template <int MODE>
+__device__ __forceinline__ void segment_sum(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
+                                            int seg, int nchunks, double* segs) {
+  const int l = threadIdx.x & 63;
+  double ls = 0.0;
+#pragma unroll
+  for (int s = 0; s < kCps; ++s) {
+    double r[8];
+    chunk_r<MODE>(P, Q, c, s, seg * (kSegTok / 8) + l + 64 * s < nchunks, r);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ls += r[t];
+  }
+  ls = wave_last_f64(wave_scan_add_f64(ls));
+  if (l == 0) segs[seg] = ls;
+}
+
+// One inverse-CDF draw with this layout: returns y, -1 if R is 0 (the
+// caller then retries on p' alone, for MODE 0) or the distribution is empty.
+template <int MODE>
+__device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch& sc) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const uint16_t* Pv = (const uint16_t*)P.vec;
+  const uint16_t* Qv = (const uint16_t*)Q.vec;
+  const int nchunks = V / 8;
+  const int ngroups = (V + kGroupTok - 1) / kGroupTok;
+  const int nseg = ngroups * kWaves;
+  // pass 1: segment sums; group G + 1 loads while group G is summed, in two
+  // register sets taken in turn (a copy would wait for the loads)
+  {
+    Chunks<MODE> ca, cb;
+    load_segment<MODE>(ca, Pv, Qv, w, nchunks);
+    for (int G = 0; G < ngroups; G += 2) {
+      load_segment<MODE>(cb, Pv, Qv, min(G + 1, ngroups - 1) * kWaves + w, nchunks);
+      segment_sum<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg);
+      if (G + 1 >= ngroups) break;
+      load_segment<MODE>(ca, Pv, Qv, min(G + 2, ngroups - 1) * kWaves + w, nchunks);
+      segment_sum<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg);
+    }
+  }
+  __syncthreads();
+  // exclusive scan over segments (token order), by wave 0
+  if (w == 0) {
+    double carry = 0.0;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+      const int i = s0 + l;
+      const double v = i < nseg ? sc.seg[i] : 0.0;
+      const double inc = wave_scan_add_f64(v);
+      if (i < nseg) sc.seg[i] = carry + (inc - v);
+      carry += wave_last_f64(inc);
+    }
+    if (l == 0) sc.R = carry;
+  }
+  __syncthreads();
+  const double R = sc.R;
+  if (!(R > 0.0)) {
+    __syncthreads();  // sc is reused by a retry
+    return -1;
+  }
+  const double target = u * R;
+  // the segment holding the crossing: the last segment whose exclusive prefix
+  // is <= target and whose mass is positive (or, at a rounding edge, the last
+  // segment with mass); then its tokens in order (s, then lane, then t)
+  if (w == 0) {
+    int best = -1, lastm = -1;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+      const int i = s0 + l;
+      const double ex = i < nseg ? sc.seg[i] : 0.0;
+      const double nx = i + 1 < nseg ? sc.seg[i + 1] : R;
+      const bool has = i < nseg && nx > ex;
+      if (has && ex <= target && nx > target) best = max(best, i);
+      if (has) lastm = max(lastm, i);
+    }
+    best = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)best));
+    lastm = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)lastm));
+    const int ss = best >= 0 ? best : lastm >= 0 ? lastm : 0;
+    Chunks<MODE> c;
+    load_segment<MODE>(c, Pv, Qv, ss, nchunks);
+    double running = sc.seg[ss];
+    int hit = 0x7FFFFFFF, lastpos = -1;
+#pragma unroll
+    for (int s = 0; s < kCps; ++s) {
+      const int ci = ss * (kSegTok / 8) + l + 64 * s;
+      double r[8];
+      chunk_r<MODE>(P, Q, c, s, ci < nchunks, r);
+      double ls = 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ls += r[t];
+      const double incl = wave_scan_add_f64(ls);
+      double cum = running + (incl - ls);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        cum += r[t];
+        if (r[t] > 0.0) {
+          lastpos = 8 * ci + t;
+          if (hit == 0x7FFFFFFF && cum > target) hit = 8 * ci + t;
+        }
+      }
+      running += wave_last_f64(incl);
+    }
+    hit = (int)wave_last_u32(wave_scan_u32<OpMinI32>((uint32_t)hit));
+    lastpos = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)lastpos));
+    if (l == 0) sc.y = hit != 0x7FFFFFFF ? hit : lastpos;
+  }
+  __syncthreads();
+  const int y = sc.y;
+  __syncthreads();  // sc is reused by the next call
+  return y;
+}
+
 // Inverse CDF over one position, all threads of the block participate.
 // mode 0: residual of (P, Q), falling back to P if it is identically zero;
 // mode 1: P alone.  Returns y (same value in every thread), or -1 if the
 // distribution is empty.  *zero_residual reports the fallback.
 __device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
                            CdfScratch& sc, bool* zero_residual) {
+  if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
+      (mode == 1 || is_aligned16(Q.vec))) {
+    *zero_residual = false;
+    if (mode == 0) {
+      const int y = inverse_cdf_bf16<0>(P, Q, V, u, sc);
+      if (y >= 0) return y;
+      // R == 0: the residual vanishes identically; draw from p' instead
+      *zero_residual = true;
+    }
+    return inverse_cdf_bf16<1>(P, P, V, u, sc);
+  }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = (V + kTile - 1) / kTile;
   const int nseg = ntiles * kWaves;
@@ -232,6 +412,7 @@ __device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, i
   d.tau = rec.tau;
   d.c2 = log2e_over_T(T);
   d.inv = rec.inv_kept;
+  d.invf = (float)rec.inv_kept;
   return d;
 }
 
@@ -248,7 +429,10 @@ __global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParam
   const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
   const int per = slots_per_row(K);
   const VecRec* recs = p.recs + (int64_t)b * per;
-  if (tid == 0) {
+  // Row header by wave 0, one lane per position: checks, ratios, uniforms;
+  // the first rejection is the lowest lane that rejects.
+  if (tid < 64) {
+    const int l = tid;
     uint32_t st = 0;
     const int kb = p.k_per_row ? p.k_per_row[b] : K;
     if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
@@ -256,49 +440,59 @@ __global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParam
     if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
     const float P = p.top_p ? p.top_p[b] : 1.0f;
     if (isnan(P) || P <= 0.0f) st |= SV_ROW_BAD_TOP_P;
-    int acc = 0;
+    double px = 0.0, qx = 0.0;
+    uint32_t lst = 0;
     if (!(st & SV_ROW_BAD_K)) {
-      for (int i = 0; i < kb; ++i) {
-        const int x = p.tokens[(int64_t)b * K + i];
-        if (x < 0 || x >= V) st |= SV_ROW_BAD_TOKEN;
+      if (l < kb) {
+        const int x = p.tokens[(int64_t)b * K + l];
+        if (x < 0 || x >= V) lst |= SV_ROW_BAD_TOKEN;
+        px = recs[l].px;
+        qx = recs[K + 1 + l].px;
+        lst |= recs[l].status | recs[K + 1 + l].status;
+      } else if (l == kb) {
+        lst |= recs[kb].status;
       }
-      for (int i = 0; i <= kb; ++i) st |= recs[i].status;
-      for (int i = 0; i < kb; ++i) st |= recs[K + 1 + i].status;
     }
+    st |= wave_last_u32(wave_scan_u32<OpOrU32>(lst));
+    int acc = 0;
     if (!st) {
-      // left-to-right chain with early stop
-      acc = kb;
-      for (int i = 0; i < kb; ++i) {
-        const double px = recs[i].px, qx = recs[K + 1 + i].px;
+      bool rej = false;
+      if (l < kb) {
         const double rho = qx > 0.0 ? px / qx : 0.0;
-        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 0, p.offset);
-        if (!(u < rho)) { acc = i; break; }
+        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)l, 0, p.offset);
+        rej = !(u < rho);
       }
-      for (int i = 0; i < K; ++i) {
-        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + i] = i < kb ? (float)recs[i].px : 0.0f;
-        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + i] = i < kb ? (float)recs[K + 1 + i].px : 0.0f;
+      const uint64_t rm = __ballot(rej);
+      acc = rm ? __builtin_ctzll(rm) : kb;
+      if (l < K) {
+        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + l] = l < kb ? (float)px : 0.0f;
+        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + l] = l < kb ? (float)qx : 0.0f;
       }
     } else {
-      for (int j = 0; j <= K; ++j) p.out_tokens[(int64_t)b * (K + 1) + j] = -1;
-      p.accepted[b] = -1;
-      if (p.num_emitted) p.num_emitted[b] = 0;
-      for (int i = 0; i < K; ++i) {
-        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + i] = NAN;
-        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + i] = NAN;
+      if (l <= K) p.out_tokens[(int64_t)b * (K + 1) + l] = -1;
+      if (l < K) {
+        if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + l] = NAN;
+        if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + l] = NAN;
       }
-      if (p.row_status) p.row_status[b] = (int32_t)st;
+      if (l == 0) {
+        p.accepted[b] = -1;
+        if (p.num_emitted) p.num_emitted[b] = 0;
+        if (p.row_status) p.row_status[b] = (int32_t)st;
+      }
     }
-    rs.kb = kb;
-    rs.acc = acc;
-    rs.go = st == 0;
-    rs.status = st;
-    rs.T = T;
-    rs.mode = acc < kb ? 0 : 1;
-    rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, p.offset);
+    if (l == 0) {
+      rs.kb = kb;
+      rs.acc = acc;
+      rs.go = st == 0;
+      rs.status = st;
+      rs.T = T;
+      rs.mode = acc < kb ? 0 : 1;
+      rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, p.offset);
+    }
   }
   __syncthreads();
   if (!rs.go) return;
-  const int kb = rs.kb, acc = rs.acc, mode = rs.mode;
+  const int acc = rs.acc, mode = rs.mode;
   const Dist P = make_dist(p.target, (int64_t)b * (K + 1) + acc, p.t_stride, p.dtype, recs[acc], rs.T);
   Dist Q = P;
   if (mode == 0) Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, recs[K + 1 + acc], rs.T);
