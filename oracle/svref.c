@@ -629,3 +629,45 @@ int svref_kv_rollback(const svref_rollback_args* a) {
   free(st); free(newlen); free(nrel);
   return 0;
 }
+
+/* ====================================================================== */
+/* Dynamic draft length                                                    */
+/* ====================================================================== */
+
+int svref_dynamic_k(const svref_dynk_args* a) {
+  if (!a || a->B < 0 || a->window < 1 || a->k_min < 1 || a->k_max < a->k_min ||
+      a->up_den <= 0 || a->down_den <= 0)
+    return -1;
+  if (a->B > 0 && (!a->accepted || !a->k_per_row || !a->state)) return -1;
+  const int32_t W = a->window;
+  for (int32_t b = 0; b < a->B; ++b) {
+    int32_t* st = a->state + (int64_t)b * (W + 4);
+    int32_t* slots = st + 4;
+    const int32_t k = a->k_per_row[b];
+    const int32_t acc = a->accepted[b];
+    if (acc < 0 || acc > k) continue; /* a row error: nothing to learn */
+    /* the round enters the window; when it is full the oldest round leaves */
+    if (st[0] < W) {
+      slots[(st[1] + st[0]) % W] = acc | (k << 16);
+      st[0] += 1;
+    } else {
+      const int32_t old = slots[st[1]];
+      st[2] -= old & 0xFFFF;
+      st[3] -= old >> 16;
+      slots[st[1]] = acc | (k << 16);
+      st[1] = (st[1] + 1) % W;
+    }
+    st[2] += acc;
+    st[3] += k;
+    int32_t next = k;
+    if (st[0] == W) {
+      const int64_t sa = st[2], sp = st[3];
+      if (sa * a->up_den > (int64_t)a->up_num * sp) next = k + 1;
+      else if (sa * a->down_den < (int64_t)a->down_num * sp) next = k - 1;
+    }
+    if (next > a->k_max) next = a->k_max;
+    if (next < a->k_min) next = a->k_min;
+    a->k_per_row[b] = next;
+  }
+  return 0;
+}

@@ -164,6 +164,29 @@ int svref_kv_rollback(const svref_rollback_args* a);
 
 #define SVREF_POISON_BF16 0xFFFFu
 
+/* ---------------------------------------------------------------------- */
+/* Dynamic draft length                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Per row, the last `window` rounds' (accepted, proposed) pairs.  Once the
+ * window is full, every round: the draft length goes up by one when the
+ * window's acceptance rate sum_acc / sum_prop is above up_num / up_den, down
+ * by one when it is below down_num / down_den, within [k_min, k_max]
+ * ([SSD] §3.2: raise k above 85 %, lower it below 70 %).  Rates are
+ * compared as integer cross products, so the decision is exact. */
+typedef struct {
+  int32_t B, window, k_min, k_max;
+  int32_t up_num, up_den, down_num, down_den;
+  const int32_t* accepted;  /* [B] this round's accepted count; a value
+                               outside [0, k] leaves the row unchanged     */
+  int32_t* k_per_row;       /* [B] in: k used this round; out: next k      */
+  int32_t* state;           /* [B][window + 4]: filled count, oldest slot,
+                               sum of accepted, sum of proposed, then one
+                               slot per round: accepted | proposed << 16   */
+} svref_dynk_args;
+
+int svref_dynamic_k(const svref_dynk_args* a);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,12 @@ class RollbackArgs(C.Structure):
     ]
 
 
+class DynkArgs(C.Structure):
+    _fields_ = [("B", C.c_int32), ("window", C.c_int32), ("k_min", C.c_int32), ("k_max", C.c_int32),
+                ("up_num", C.c_int32), ("up_den", C.c_int32), ("down_num", C.c_int32),
+                ("down_den", C.c_int32), ("accepted", _P), ("k_per_row", _P), ("state", _P)]
+
+
 _lib = None
 
 
@@ -77,6 +83,8 @@ def load_library(path):
     L.svref_draft_sample.restype = C.c_int
     L.svref_kv_rollback.argtypes = [C.POINTER(RollbackArgs)]
     L.svref_kv_rollback.restype = C.c_int
+    L.svref_dynamic_k.argtypes = [C.POINTER(DynkArgs)]
+    L.svref_dynamic_k.restype = C.c_int
     return L
 
 
@@ -288,3 +296,21 @@ def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
     if rc != 0:
         raise ValueError("svref_kv_rollback rejected its arguments")
     return st
+
+
+def dynk_state(B, window=64):
+    """A fresh controller state: every row's window empty."""
+    return np.zeros((B, window + 4), np.int32)
+
+
+def dynamic_k(accepted, k_per_row, state, window=64, k_min=2, k_max=8, up=(17, 20),
+              down=(7, 10)):
+    """One controller update, IN PLACE on k_per_row and state (numpy int32)."""
+    B = k_per_row.shape[0]
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    assert k_per_row.dtype == np.int32 and k_per_row.flags.c_contiguous
+    assert state.dtype == np.int32 and state.flags.c_contiguous and state.shape == (B, window + 4)
+    a = DynkArgs(B, window, k_min, k_max, up[0], up[1], down[0], down[1], _ptr(acc),
+                 _ptr(k_per_row), _ptr(state))
+    if lib().svref_dynamic_k(C.byref(a)) != 0:
+        raise ValueError("svref_dynamic_k rejected its arguments")

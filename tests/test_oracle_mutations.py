@@ -16,6 +16,7 @@ import tests.test_oracle_philox as T_philox
 import tests.test_oracle_statistics as T_stats
 import tests.test_oracle_greedy_rollback as T_gr
 import tests.test_oracle_softmax_topp as T_sm
+import tests.test_oracle_dynk as T_dk
 
 SRC = open(obuild.SRC).read()
 
@@ -65,6 +66,13 @@ MUTANTS = [
     ("softmax without the max shift divides by the wrong sum",
      "for (int32_t j = 0; j < V; ++j) p_out[j] /= S;", "for (int32_t j = 0; j < V; ++j) p_out[j] /= (S + 1e-3);",
      lambda o: T_sm.test_two_level_closed_form(o)),
+    ("controller raises k at exactly 85 %",
+     "if (sa * a->up_den > (int64_t)a->up_num * sp) next = k + 1;",
+     "if (sa * a->up_den >= (int64_t)a->up_num * sp) next = k + 1;",
+     lambda o: T_dk.test_thresholds_are_strict()),
+    ("controller acts before its window is full",
+     "if (st[0] == W) {\n      const int64_t sa", "if (st[0] >= W - 1) {\n      const int64_t sa",
+     lambda o: T_dk.test_all_accepted_climbs_to_k_max_after_the_window_fills()),
 ]
 
 
