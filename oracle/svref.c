@@ -645,7 +645,9 @@ int svref_dynamic_k(const svref_dynk_args* a) {
     int32_t* slots = st + 4;
     const int32_t k = a->k_per_row[b];
     const int32_t acc = a->accepted[b];
-    if (acc < 0 || acc > k) continue; /* a row error: nothing to learn */
+    /* a row error (accepted outside [0, k]) teaches nothing; a k that does
+     * not fit the 15-bit field of a slot is not a draft length either */
+    if (acc < 0 || acc > k || k > 0x7FFF) continue;
     /* the round enters the window; when it is full the oldest round leaves */
     if (st[0] < W) {
       slots[(st[1] + st[0]) % W] = acc | (k << 16);
