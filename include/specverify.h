@@ -129,6 +129,12 @@ typedef struct {
                                         ([SSD] §2.4; [FS] §5.1); sampled only */
   const float* top_p;                /* [B] in (0, 1]; NULL or >= 1 -> off     */
   uint64_t seed, offset;             /* Philox key word 0 / round counter      */
+  const uint64_t* offset_dev;        /* [1] device word, or NULL: when given,
+                                        the kernels read the round counter
+                                        from it as they run and `offset` is
+                                        ignored, so a captured graph draws
+                                        fresh numbers on every replay
+                                        (8-byte aligned, else SV_E_ARG)       */
   uint32_t flags;                    /* SV_FLAG_*                              */
 
   int32_t* out_tokens;               /* [B][k_max+1], -1 padded                */
@@ -229,6 +235,48 @@ sv_status sv_check_rollback_args(const sv_rollback_args* a);
  * table) are left unchanged and flagged.  With kv_pool, the slots
  * [new, old) of committed rows are poisoned in every layer and head. */
 sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s);
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic draft length and the on-device round                            */
+/* ------------------------------------------------------------------------ */
+
+/* Per-row controller of the draft length ([SSD] §3.2: raise k when the
+ * acceptance rate is above 85 %, lower it below 70 %).  Each row keeps the
+ * last `window` rounds' (accepted, proposed) pairs in `state`; once the window
+ * is full, every round k becomes k + 1 if sum_accepted * up_den > up_num *
+ * sum_proposed, else k - 1 if sum_accepted * down_den < down_num *
+ * sum_proposed, clamped to [k_min, k_max].  The comparisons are on integers,
+ * so the decision is exact.  Defaults that match the page: window 64,
+ * up 17/20, down 7/10, k in [2, 8], start at 5 (the caller's initial k). */
+typedef struct {
+  int32_t B, window, k_min, k_max;
+  int32_t up_num, up_den, down_num, down_den;
+  const int32_t* accepted;  /* [B] from a verify call; a value outside
+                               [0, k] (a flagged row), or k > 32767, leaves
+                               the row as is                                */
+  int32_t* k_per_row;       /* [B] in: k used this round; out: next round's
+                               k (usable directly as the next call's
+                               k_per_row)                                    */
+  int32_t* state;           /* [B][window + 4] int32, all zero before the
+                               first round: filled count, oldest slot, sum of
+                               accepted, sum of proposed, then one slot per
+                               round (accepted | proposed << 16)            */
+} sv_dynk_args;
+
+/* Host checks only: window in [1, 4096], 1 <= k_min <= k_max <= SV_MAX_K,
+ * positive denominators, non-NULL arrays when B > 0. */
+sv_status sv_check_dynk_args(const sv_dynk_args* a);
+
+/* One controller update for every row, on the stream (one thread per row). */
+sv_status sv_dynamic_k(sv_handle h, const sv_dynk_args* a, hipStream_t s);
+
+/* Adds delta to the device word *offset_dev on the stream (one thread): the
+ * end of a round for callers that keep the Philox round counter on the
+ * device (sv_verify_args.offset_dev), so that a captured round of draft
+ * sampling, verification, rollback and controller update replays without
+ * any host work.  Wraps modulo 2^64.  SV_E_ARG if offset_dev is NULL or not
+ * 8-byte aligned. */
+sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,8 @@ class VerifyArgs(C.Structure):
         ("target_logits", _P), ("target_vec_stride", C.c_int64),
         ("draft_logits", _P), ("draft_vec_stride", C.c_int64),
         ("draft_tokens", _P), ("k_per_row", _P), ("temperature", _P), ("top_p", _P),
-        ("seed", C.c_uint64), ("offset", C.c_uint64), ("flags", C.c_uint32),
+        ("seed", C.c_uint64), ("offset", C.c_uint64), ("offset_dev", _P),
+        ("flags", C.c_uint32),
         ("out_tokens", _P), ("accepted", _P), ("num_emitted", _P),
         ("p_at_draft", _P), ("q_at_draft", _P), ("row_status", _P),
         ("workspace", _P), ("workspace_bytes", C.c_size_t),
@@ -61,10 +62,20 @@ class RollbackArgs(C.Structure):
     ]
 
 
+class DynkArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("window", C.c_int32), ("k_min", C.c_int32), ("k_max", C.c_int32),
+        ("up_num", C.c_int32), ("up_den", C.c_int32), ("down_num", C.c_int32),
+        ("down_den", C.c_int32),
+        ("accepted", _P), ("k_per_row", _P), ("state", _P),
+    ]
+
+
 EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
-           "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback")
+           "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
+           "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset")
 
 _lib = None
 _lock = threading.Lock()
@@ -105,6 +116,12 @@ def library():
                 L.sv_check_rollback_args.restype = C.c_int
                 L.sv_kv_rollback.argtypes = [_P, C.POINTER(RollbackArgs), _P]
                 L.sv_kv_rollback.restype = C.c_int
+                L.sv_check_dynk_args.argtypes = [C.POINTER(DynkArgs)]
+                L.sv_check_dynk_args.restype = C.c_int
+                L.sv_dynamic_k.argtypes = [_P, C.POINTER(DynkArgs), _P]
+                L.sv_dynamic_k.restype = C.c_int
+                L.sv_advance_offset.argtypes = [_P, _P, C.c_uint64, _P]
+                L.sv_advance_offset.restype = C.c_int
                 _lib = L
     return _lib
 
@@ -234,7 +251,7 @@ class VerifyCall:
             a.draft_logits = _ptr(draft)
             a.draft_vec_stride = _vec_stride(draft, K, "draft")
             keep.append(draft)
-        if mode == "draft":
+        if mode == "draft" and draft_tokens is None:
             draft_tokens = torch.full((B, K), -1, dtype=torch.int32, device=dev)
         keep.append(_i32(draft_tokens, (B, K), "draft_tokens", dev))
         a.draft_tokens = _ptr(draft_tokens)
@@ -244,7 +261,15 @@ class VerifyCall:
         a.temperature = _ptr(temperature)
         keep.append(_f32(top_p, (B,), "top_p", dev))
         a.top_p = _ptr(top_p)
-        a.seed, a.offset, a.flags = int(seed), int(offset), int(flags)
+        a.seed, a.flags = int(seed), int(flags)
+        if isinstance(offset, torch.Tensor):
+            # the round counter lives on the device: read by the kernels at run time
+            if offset.dtype != torch.int64 or offset.numel() != 1 or offset.device != dev:
+                raise ValueError("a device offset must be a one-element int64 tensor on %s" % dev)
+            a.offset_dev = _ptr(offset)
+            keep.append(offset)
+        else:
+            a.offset = int(offset)
         self.outputs = {}
         if mode != "draft":
             o = self.outputs
@@ -365,3 +390,38 @@ def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
     call = RollbackCall(kv_len, accepted, page_table, page_size, k_max, k_per_row, free_pages,
                         free_top, kv_pool, num_pages, num_layers, kv_heads, head_dim)
     return call.run(stream)
+
+
+def advance_offset(offset, delta=1, stream=None):
+    """Adds delta to a device round counter (one-element int64 tensor), on the
+    stream (sv_advance_offset); the counter is read as an unsigned word."""
+    if offset.dtype != torch.int64 or offset.numel() != 1 or offset.device.type != "cuda":
+        raise ValueError("offset must be a one-element int64 tensor on a GPU")
+    dev = offset.device
+    rc = library().sv_advance_offset(handle(dev), _ptr(offset), int(delta) & (2**64 - 1),
+                                     _stream(dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError("sv_advance_offset", rc)
+    return offset
+
+
+def dynk_state(B, window=64, device="cuda"):
+    """A fresh controller state ([B][window + 4] int32 zeros) on the device."""
+    return torch.zeros((B, window + 4), dtype=torch.int32, device=device)
+
+
+def dynamic_k(accepted, k_per_row, state, window=64, k_min=2, k_max=8, up=(17, 20),
+              down=(7, 10), stream=None):
+    """One update of the dynamic draft-length controller (sv_dynamic_k), in
+    place on the device tensors k_per_row [B] and state [B, window + 4]."""
+    dev = k_per_row.device
+    B = k_per_row.shape[0] if k_per_row.dim() == 1 else -1
+    _i32(k_per_row, (B,), "k_per_row", dev)
+    _i32(accepted, (B,), "accepted", dev)
+    _i32(state, (B, window + 4), "state", dev)
+    a = DynkArgs(B, window, k_min, k_max, up[0], up[1], down[0], down[1], _ptr(accepted),
+                 _ptr(k_per_row), _ptr(state))
+    rc = library().sv_dynamic_k(handle(dev), C.byref(a), _stream(dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError("sv_dynamic_k", rc)
+    return k_per_row

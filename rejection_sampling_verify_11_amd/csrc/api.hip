@@ -171,6 +171,7 @@ sv_status sv_check_verify_args(const sv_verify_args* a, int mode) {
   if ((int64_t)a->B * (2 * a->k_max + 1) * sv::greedy_chunks(a->V) > 0x7FFFFFFFLL) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
   if (mode != 1 && a->V > kMaxVSampled) return SV_E_ARG;
+  if ((uintptr_t)a->offset_dev & 7) return SV_E_ARG;
   if (mode == 0) {
     if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
         !a->out_tokens || !a->accepted)
@@ -227,6 +228,7 @@ static sv::FinalizeParams finalize_params(const sv_verify_args* a) {
   f.flags = a->flags;
   f.seed = a->seed;
   f.offset = a->offset;
+  f.offset_dev = a->offset_dev;
   f.recs = (const sv::VecRec*)a->workspace;
   f.out_tokens = a->out_tokens;
   f.accepted = a->accepted;
@@ -330,6 +332,42 @@ sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) 
   p.row_status = a->row_status;
   p.recs = (sv::RollRec*)a->workspace;
   if (sv::launch_rollback(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_check_dynk_args(const sv_dynk_args* a) {
+  if (!a) return SV_E_ARG;
+  if (a->B < 0 || a->window < 1 || a->window > 4096 || a->k_min < 1 || a->k_max < a->k_min ||
+      a->k_max > SV_MAX_K || a->up_den <= 0 || a->down_den <= 0)
+    return SV_E_ARG;
+  if (a->B > 0 && (!a->accepted || !a->k_per_row || !a->state)) return SV_E_ARG;
+  return SV_OK;
+}
+
+sv_status sv_dynamic_k(sv_handle h, const sv_dynk_args* a, hipStream_t s) {
+  const sv_status st = sv_check_dynk_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::DynkParams p;
+  p.B = a->B;
+  p.W = a->window;
+  p.k_min = a->k_min;
+  p.k_max = a->k_max;
+  p.up_num = a->up_num;
+  p.up_den = a->up_den;
+  p.down_num = a->down_num;
+  p.down_den = a->down_den;
+  p.accepted = a->accepted;
+  p.k_per_row = a->k_per_row;
+  p.state = a->state;
+  if (sv::launch_dynk(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, hipStream_t s) {
+  if (!h || !offset_dev || ((uintptr_t)offset_dev & 7)) return SV_E_ARG;
+  if (sv::launch_advance_offset(offset_dev, delta, s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
 }
 

@@ -106,6 +106,12 @@ struct CdfScratch {
   double base;
 };
 
+// The Philox round counter of this call: the device word when one is given
+// (read as the kernel runs, for captured rounds), else the host value.
+__device__ __forceinline__ uint64_t round_offset(const FinalizeParams& p) {
+  return p.offset_dev ? *p.offset_dev : p.offset;
+}
+
 __device__ __forceinline__ bool is_aligned16(const void* p) {
   return (((uintptr_t)p) & 15u) == 0;
 }
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParam
       bool rej = false;
       if (l < kb) {
         const double rho = qx > 0.0 ? px / qx : 0.0;
-        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)l, 0, p.offset);
+        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)l, 0, round_offset(p));
         rej = !(u < rho);
       }
       const uint64_t rm = __ballot(rej);
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParam
       rs.status = st;
       rs.T = T;
       rs.mode = acc < kb ? 0 : 1;
-      rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, p.offset);
+      rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, round_offset(p));
     }
   }
   __syncthreads();
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(FinalizeParams p
   if (!go) return;
   const Dist Q = make_dist(p.draft, (int64_t)b * K + i, p.d_stride, p.dtype, recs[K + 1 + i], Ts);
   bool zero = false;
-  const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 2, p.offset);
+  const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 2, round_offset(p));
   const int y = inverse_cdf(Q, Q, 1, p.dtype, p.V, u, sc, &zero);
   if (tid == 0) p.draft_out[(int64_t)b * K + i] = y;
 }

@@ -86,6 +86,7 @@ struct FinalizeParams {
   int32_t B, K, V, dtype;
   uint32_t flags;
   uint64_t seed, offset;
+  const uint64_t* offset_dev;  // when non-null, the round counter is read here
   const VecRec* recs;
   int32_t* out_tokens;
   int32_t* accepted;
@@ -126,6 +127,13 @@ struct RollbackParams {
   RollRec* recs;
 };
 
+struct DynkParams {
+  int32_t B, W, k_min, k_max, up_num, up_den, down_num, down_den;
+  const int32_t* accepted;
+  int32_t* k_per_row;
+  int32_t* state;
+};
+
 // Optional event bracketing of each launch (see sv_timing_enable).
 class Timer {
  public:
@@ -151,5 +159,7 @@ hipError_t launch_finalize_sample(const FinalizeParams& p, hipStream_t s, Timer*
 hipError_t launch_draft_sample(const FinalizeParams& p, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
+hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t);
+hipError_t launch_advance_offset(uint64_t* offset_dev, uint64_t delta, hipStream_t s, Timer* t);
 
 }  // namespace sv

@@ -54,7 +54,8 @@ def _c_layout(struct, fields):
 
 
 @pytest.mark.parametrize("cls,cname", [(_abi.VerifyArgs, "sv_verify_args"),
-                                       (_abi.RollbackArgs, "sv_rollback_args")])
+                                       (_abi.RollbackArgs, "sv_rollback_args"),
+                                       (_abi.DynkArgs, "sv_dynk_args")])
 def test_argument_block_layout_matches_header(cls, cname):
     fields = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -158,6 +159,30 @@ def test_rollback_validation():
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG  # stack without height
     a.page_size = 0
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG
+
+
+def test_dynk_validation():
+    L = _abi.library()
+    a = _abi.DynkArgs(4, 64, 2, 8, 17, 20, 7, 10, 0x10000, 0x10000, 0x10000)
+    assert L.sv_check_dynk_args(C.byref(a)) == _abi.SV_OK
+    for field, bad in [("window", 0), ("window", 4097), ("k_min", 0), ("k_max", 1),
+                       ("k_max", _abi.SV_MAX_K + 1), ("up_den", 0), ("down_den", -1),
+                       ("B", -1), ("state", None)]:
+        b = _abi.DynkArgs.from_buffer_copy(a)
+        setattr(b, field, bad)
+        assert L.sv_check_dynk_args(C.byref(b)) == _abi.SV_E_ARG, field
+    a.B, a.accepted, a.k_per_row, a.state = 0, None, None, None
+    assert L.sv_check_dynk_args(C.byref(a)) == _abi.SV_OK  # nothing to do
+    assert L.sv_dynamic_k(None, C.byref(a), None) == _abi.SV_E_ARG  # no handle
+    assert L.sv_advance_offset(None, 0x10000, 1, None) == _abi.SV_E_ARG
+
+
+def test_device_offset_must_be_aligned():
+    a = good_args()
+    a.offset_dev = 0x10008
+    assert check(a) == _abi.SV_OK and check(a, 2) == _abi.SV_OK
+    a.offset_dev = 0x10004
+    assert check(a) == _abi.SV_E_ARG and check(a, 2) == _abi.SV_E_ARG
 
 
 def test_status_strings():
