@@ -97,8 +97,15 @@ __device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int d
   }
 }
 
+// Tokens per wave segment of the bf16 path (defined with that path below).
+constexpr int kCpsFast = 2;
+constexpr int kSegTokFast = 512 * kCpsFast;
+
 struct CdfScratch {
   double seg[kMaxSeg];
+  // bf16 path with a top-p cut: each wave's list of the tokens of its
+  // segment that can carry mass, plus one spare slot per lane
+  uint32_t list[kWaves][kSegTokFast + 64];
   double wsum[kWaves];
   double R;
   int sstar;
@@ -121,8 +128,8 @@ __device__ __forceinline__ bool is_aligned16(const void* p) {
 // tokens G kGroupTok + kSegTok w + [0, kSegTok) (one segment), lane l the
 // 8-token chunks at 512 s + 8 l (s < kCps), so every wave load is 1 KB
 // contiguous.  Pass 1 loads group G + 1 while it sums group G.
-constexpr int kCps = 2;                    // chunks per lane per segment
-constexpr int kSegTok = 512 * kCps;
+constexpr int kCps = kCpsFast;             // chunks per lane per segment
+constexpr int kSegTok = kSegTokFast;
 constexpr int kGroupTok = kWaves * kSegTok;
 
 // MODE 0: residual max(0, p' - q'); MODE 1: p' alone.
@@ -183,9 +190,57 @@ __device__ __forceinline__ void segment_sum(const Dist& P, const Dist& Q, const 
   if (l == 0) segs[seg] = ls;
 }
 
+// The same sum when p' has a top-p cut.  r is zero at every token below
+// tau_p (p' is zero there, so is max(0, p' - q')), and with a cut that is
+// most tokens.  The wave first lists the tokens at or above tau_p in LDS --
+// the raw p bits in the low half of an entry, q's in the high half -- by a
+// ballot and a lane prefix count (branch-free: a lane with nothing to list
+// writes its spare slot), then forms r on the list only.  The sum is over the
+// same fp32 values as segment_sum's, in another order.
+template <int MODE>
+__device__ __forceinline__ void segment_sum_listed(const Dist& P, const Dist& Q,
+                                                   const Chunks<MODE>& c, int seg, int nchunks,
+                                                   double* segs, uint32_t* list) {
+  const int l = threadIdx.x & 63;
+  uint32_t n = 0;  // list length (wave-uniform)
+#pragma unroll
+  for (int s = 0; s < kCps; ++s) {
+    const bool valid = seg * (kSegTok / 8) + l + 64 * s < nchunks;
+    const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
+    uint32_t qw[4] = {0u, 0u, 0u, 0u};
+    if (MODE == 0) {
+      qw[0] = c.q[s].x; qw[1] = c.q[s].y; qw[2] = c.q[s].z; qw[3] = c.q[s].w;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t word = pw[t >> 1];
+      const uint32_t hi = t & 1 ? word & 0xFFFF0000u : word << 16;  // p as fp32 bits
+      const bool keep = valid && __uint_as_float(hi) >= P.tau;
+      const uint64_t m = __ballot(keep);
+      const uint32_t pre =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      uint32_t e = hi >> 16;
+      if (MODE == 0) e |= t & 1 ? qw[t >> 1] & 0xFFFF0000u : qw[t >> 1] << 16;
+      list[keep ? n + pre : (uint32_t)(kSegTok + l)] = e;
+      n += (uint32_t)__builtin_popcountll(m);
+    }
+  }
+  double ls = 0.0;
+  for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+    const uint32_t i = i0 + (uint32_t)l;
+    const uint32_t e = list[i < n ? i : 0u];
+    float v = prob_f(P, __uint_as_float(e << 16));
+    if (MODE == 0) v = fmaxf(v - prob_f(Q, __uint_as_float(e & 0xFFFF0000u)), 0.0f);
+    ls += i < n ? (double)v : 0.0;
+  }
+  ls = wave_last_f64(wave_scan_add_f64(ls));
+  if (l == 0) segs[seg] = ls;
+}
+
 // One inverse-CDF draw with this layout: returns y, -1 if R is 0 (the
 // caller then retries on p' alone, for MODE 0) or the distribution is empty.
-template <int MODE>
+// LISTED: p' has a top-p cut and pass 1 works on listed tokens.
+template <int MODE, bool LISTED>
 __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch& sc) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
@@ -197,13 +252,16 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
   // register sets taken in turn (a copy would wait for the loads)
   {
     Chunks<MODE> ca, cb;
+    uint32_t* list = sc.list[w];
     load_segment<MODE>(ca, Pv, Qv, w, nchunks);
     for (int G = 0; G < ngroups; G += 2) {
       load_segment<MODE>(cb, Pv, Qv, min(G + 1, ngroups - 1) * kWaves + w, nchunks);
-      segment_sum<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg);
+      if (LISTED) segment_sum_listed<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg, list);
+      else segment_sum<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg);
       if (G + 1 >= ngroups) break;
       load_segment<MODE>(ca, Pv, Qv, min(G + 2, ngroups - 1) * kWaves + w, nchunks);
-      segment_sum<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg);
+      if (LISTED) segment_sum_listed<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg, list);
+      else segment_sum<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg);
     }
   }
   __syncthreads();
@@ -285,13 +343,15 @@ __device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, in
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
       (mode == 1 || is_aligned16(Q.vec))) {
     *zero_residual = false;
+    const bool cut = P.tau > -INFINITY;  // the same in every thread
     if (mode == 0) {
-      const int y = inverse_cdf_bf16<0>(P, Q, V, u, sc);
+      const int y = cut ? inverse_cdf_bf16<0, true>(P, Q, V, u, sc)
+                        : inverse_cdf_bf16<0, false>(P, Q, V, u, sc);
       if (y >= 0) return y;
       // R == 0: the residual vanishes identically; draw from p' instead
       *zero_residual = true;
     }
-    return inverse_cdf_bf16<1>(P, P, V, u, sc);
+    return cut ? inverse_cdf_bf16<1, true>(P, P, V, u, sc) : inverse_cdf_bf16<1, false>(P, P, V, u, sc);
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = (V + kTile - 1) / kTile;
