@@ -560,14 +560,18 @@ int svref_kv_rollback(const svref_rollback_args* a) {
     if (!st[b]) {
       /* Consistency of the table with the length, where the rollback acts:
        * every page holding a position in [new, old) is mapped (to a page of
-       * the pool), and the first entry past the old length is unmapped. */
+       * the pool), and, when pages are released, the first entry past the
+       * old length is unmapped.  Without a free stack the pages past the
+       * length stay mapped by design ([SD] §4.3), so that entry says
+       * nothing there. */
       int32_t nl = old - (k - acc);
       int32_t used = ceil_div(old, ps);
       for (int32_t pg = nl / ps; pg < used; ++pg) {
         int32_t e = a->page_table[(int64_t)b * MP + pg];
         if (e < 0 || (a->num_pages > 0 && e >= a->num_pages)) st[b] |= SVREF_ROW_BAD_PAGES;
       }
-      if (used < MP && a->page_table[(int64_t)b * MP + used] != -1) st[b] |= SVREF_ROW_BAD_PAGES;
+      if (a->free_pages && used < MP && a->page_table[(int64_t)b * MP + used] != -1)
+        st[b] |= SVREF_ROW_BAD_PAGES;
     }
     if (!st[b]) {
       newlen[b] = old - (k - acc);

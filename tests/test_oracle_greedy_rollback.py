@@ -148,6 +148,19 @@ def test_rollback_keep_pages_mode(oracle):
     assert np.all(st == 0)
     assert list(kv) == [29, 46, 17]
     assert np.array_equal(pt, pt0)
+    # the next round: row 0 keeps page 2 mapped past its length (29 tokens
+    # use pages 0-1), which is no inconsistency without a free stack
+    st = oracle.kv_rollback(kv, np.array([4, 1, 0], np.int32), pt, 16, 4)
+    assert np.all(st == 0)
+    assert list(kv) == [29, 43, 13]
+    assert np.array_equal(pt, pt0)
+    # with a free stack the same table is inconsistent for rows 0 and 2 (a
+    # page still mapped just past the length), not for row 1
+    free, top = np.full(8, -1, np.int32), np.array([0], np.int32)
+    kv2 = kv.copy()
+    st = oracle.kv_rollback(kv2, np.array([4, 4, 4], np.int32), pt.copy(), 16, 4,
+                            free_pages=free, free_top=top, free_capacity=8)
+    assert list(st) == [oracle.ROW_BAD_PAGES, 0, oracle.ROW_BAD_PAGES]
 
 
 def test_rollback_free_stack_overflow_rule(oracle):
@@ -178,11 +191,19 @@ def test_rollback_bad_rows_untouched(oracle):
     kv = lens.copy()
     acc = np.array([3, -1, 5, 1, 1], np.int32)
     kk = np.array([3, 3, 3, 3, 0], np.int32)
-    st = oracle.kv_rollback(kv, acc, pt, ps, 3, k_per_row=kk)
+    top0 = top.copy()
+    st = oracle.kv_rollback(kv, acc, pt, ps, 3, k_per_row=kk, free_pages=free, free_top=top,
+                            free_capacity=free.size)
     assert list(st) == [0, oracle.ROW_BAD_ACCEPTED, oracle.ROW_BAD_ACCEPTED,
                         oracle.ROW_BAD_PAGES, oracle.ROW_BAD_K]
     assert list(kv) == [9, 9, 9, 9, 9]
-    assert np.array_equal(pt, pt0)
+    assert np.array_equal(pt, pt0) and np.array_equal(top, top0)
+    # without a free stack, pages past the length are kept by design: row 3
+    # is consistent there
+    st = oracle.kv_rollback(kv, acc, pt, ps, 3, k_per_row=kk)
+    assert list(st) == [0, oracle.ROW_BAD_ACCEPTED, oracle.ROW_BAD_ACCEPTED, 0,
+                        oracle.ROW_BAD_K]
+    assert list(kv) == [9, 9, 9, 7, 9]
 
 
 def test_rollback_poisons_exactly_the_rejected_slots(oracle):
