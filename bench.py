@@ -11,6 +11,13 @@ contexts of 4096..8192 tokens, so that hundreds of steps can each shorten
 every sequence by up to k without running out of context).  Two input batches (2 GB together) alternate
 so that no step finds its logits in the 256 MB last-level cache.
 
+Beside the headline step, two more legs are timed and reported as extra
+keys: greedy verification at B=64, k=8, V=128256 (target logits only), and
+the on-device round at B=512, V=128256 with per-row temperatures and k from
+the dynamic controller (verification, page-table rollback, controller update
+and round-counter advance), replayed as a HIP graph and, for comparison,
+launched eagerly.
+
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 import argparse
@@ -30,11 +37,12 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=2, help="input batches rotated between steps")
-    ap.add_argument("--cpu-rows", type=int, default=128, help="rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the greedy and round legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -75,6 +83,95 @@ def recorded_traffic():
     if fields.get("stats_source_sha256", "").strip() != digest:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def timed(fn, n, dev):
+    """Mean milliseconds of fn() over n calls, by HIP events on the stream."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def greedy_leg(dev, n):
+    """Greedy verification (draft tokens given), B=64, k=8, V=128256 bf16."""
+    import rejection_sampling_verify_11_amd as sv
+    from rejection_sampling_verify_11_amd import workloads as W
+    B, K, V = 64, 8, 128256
+    zt, toks = W.workload3(0, device=dev, B=B, k=K, V=V)
+    call = sv.VerifyCall("greedy", zt, None, toks)
+    for _ in range(20):
+        call.run()
+    ms = timed(call.run, n, dev)
+    assert int((call.outputs["row_status"] != 0).sum()) == 0
+    target_bytes = B * (K + 1) * V * 2
+    return {"workload": "B=64 k=8 V=128256 bf16 greedy, draft = target argmax w.p. 0.85",
+            "ms_per_call": ms, "target_gbs": target_bytes / (ms * 1e-3) / 1e9,
+            "verified_positions_per_s": B * K / (ms * 1e-3),
+            "mean_accepted": call.outputs["accepted"].float().mean().item()}
+
+
+def round_leg(dev, n):
+    """The on-device round at B=512, k_max=8, V=128256: verification, rollback
+    over a preallocated page table (pages stay mapped), the dynamic-k
+    controller and the round counter.  Between rounds a torch add stands in
+    for the target model's k+1 KV writes; the logits and draft tokens stay
+    fixed."""
+    import torch
+    import rejection_sampling_verify_11_amd as sv
+    from rejection_sampling_verify_11_amd import workloads as W
+    B, K, V, ps = 512, 8, 128256, 16
+    rows = W.workload5_rows(0, B=B, device=dev)
+    k = torch.full((B,), 5, dtype=torch.int32, device=dev)
+    inp = W.workload5(0, rows, k, k_max=K, device=dev, V=V)
+    toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 0)
+    ctx_max = 4096 + 2 * (n + 40) * (K + 1)
+    MP = (ctx_max + ps - 1) // ps
+    page_table = torch.arange(B * MP, dtype=torch.int32, device=dev).view(B, MP)
+    kv_len = rows.kv_len0.to(dev).clone()
+    offset = torch.zeros(1, dtype=torch.int64, device=dev)
+    state = sv.dynk_state(B, 64, dev)
+    verify = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, None, k,
+                           seed=0, offset=offset)
+    acc = verify.outputs["accepted"]
+    roll = sv.RollbackCall(kv_len, acc, page_table, ps, K, k_per_row=k, num_pages=B * MP)
+
+    def one_round():
+        kv_len.add_(k).add_(1)     # the target forward's k + 1 speculative writes
+        verify.run()
+        roll.run()
+        sv.dynamic_k(acc, k, state)
+        sv.advance_offset(offset)
+
+    for _ in range(20):
+        one_round()
+    torch.cuda.synchronize()
+    eager_ms = timed(one_round, n, dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_round()
+    for _ in range(20):
+        g.replay()
+    graph_ms = timed(g.replay, n, dev)
+    assert int((roll.row_status != 0).sum()) == 0
+    assert int((verify.outputs["row_status"] != 0).sum()) == 0
+    # the controller's k over a further stretch of rounds (untimed)
+    k_sum = torch.zeros((), dtype=torch.int64, device=dev)
+    for _ in range(20):
+        k_sum += k.sum()
+        g.replay()
+    mean_k = k_sum.item() / (20 * B)
+    return {"workload": "B=512 k_b in [2, 8] from the controller (window 64) V=128256 bf16, "
+                        "T_b ~ U[0.1, 1], no top-p, page-table rollback",
+            "graph_ms_per_round": graph_ms, "eager_ms_per_round": eager_ms,
+            "mean_k": mean_k, "verified_positions_per_s": mean_k * B / (graph_ms * 1e-3),
+            "mean_accepted": acc.float().mean().item()}
 
 
 def main():
@@ -196,6 +293,10 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": recorded_traffic()},
     }
+
+    if not args.no_extra:
+        result["greedy"] = greedy_leg(dev, args.steps)
+        result["round"] = round_leg(dev, args.steps)
 
     if not args.no_cpu_baseline:
         from oracle import svref

@@ -69,7 +69,8 @@ typedef enum { SV_FP32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_ROW_BAD_PAGES       (1u << 6) /* page table inconsistent with kv_len:
                                             a page holding a rolled-back
                                             position unmapped (or past the
-                                            pool), or the entry just past the
+                                            pool), or, when pages are
+                                            released, the entry just past the
                                             old length mapped                 */
 #define SV_ROW_FREE_OVERFLOW   (1u << 7) /* released pages do not fit the stack  */
 #define SV_ROW_BAD_ACCEPTED    (1u << 8) /* accepted outside [0, k_b] (e.g. -1

@@ -43,8 +43,9 @@ __device__ Decision decide_row(const RollbackParams& p, int b) {
   else if (acc < 0 || acc > k || old - (k - acc) < 0) d.st |= SV_ROW_BAD_ACCEPTED;
   if (old < 0 || ceil_div(old, p.ps) > p.MP) d.st |= SV_ROW_BAD_PAGES;
   if (!d.st) {
-    // the pages holding the rolled-back positions must be mapped, and the
-    // first entry past the old length must be unmapped
+    // the pages holding the rolled-back positions must be mapped, and, when
+    // pages are released, the first entry past the old length must be
+    // unmapped (without a free stack pages past the length stay mapped)
     const int nl = old - (k - acc);
     const int used = ceil_div(old, p.ps);
     const int32_t* row = p.page_table + (int64_t)b * p.MP;
@@ -52,7 +53,7 @@ __device__ Decision decide_row(const RollbackParams& p, int b) {
       const int e = row[pg];
       if (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) d.st |= SV_ROW_BAD_PAGES;
     }
-    if (used < p.MP && row[used] != -1) d.st |= SV_ROW_BAD_PAGES;
+    if (p.free_pages && used < p.MP && row[used] != -1) d.st |= SV_ROW_BAD_PAGES;
   }
   if (!d.st) {
     d.new_len = old - (k - acc);

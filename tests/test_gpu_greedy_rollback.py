@@ -183,6 +183,28 @@ def test_rollback_keep_pages_overflow_and_bad_rows(oracle):
     assert ((st & sv.ROW_FREE_OVERFLOW) != 0).sum() > 0
 
 
+def test_rollback_keep_pages_over_rounds(oracle):
+    """Without a free stack pages past the length stay mapped; three rounds
+    in a row on the same table, each checked against the oracle's."""
+    rng = np.random.default_rng(8)
+    B, K, ps = 300, 6, 16
+    lens = (rng.integers(40, 400, B) + K + 1).astype(np.int32)
+    MP = int((lens.max() + ps - 1) // ps)
+    kv = W.paged_kv(torch.from_numpy(lens), ps, MP, seed=8)
+    o_len, o_pt = lens.copy(), kv.page_table.numpy().copy()
+    d_len, d_pt = torch.from_numpy(lens.copy()).to(DEV), kv.page_table.to(DEV)
+    for r in range(3):
+        kk = rng.integers(1, K + 1, B).astype(np.int32)
+        acc = np.array([rng.integers(0, k + 1) for k in kk], np.int32)
+        st = sv.kv_rollback(d_len, torch.from_numpy(acc).to(DEV), d_pt, ps, K,
+                            k_per_row=torch.from_numpy(kk).to(DEV))
+        o_st = oracle.kv_rollback(o_len, acc, o_pt, ps, K, k_per_row=kk)
+        assert np.all(o_st == 0), "round %d" % r
+        assert np.array_equal(st.cpu().numpy(), o_st)
+        assert np.array_equal(d_len.cpu().numpy(), o_len)
+        assert np.array_equal(d_pt.cpu().numpy(), o_pt)
+
+
 def test_rollback_full_size_pool_poison(oracle):
     """The workload's real pool: 32 layers x 8 KV heads x 128 dims bf16, page
     size 16 (2 MiB per page), 64 rows of 512..4096 tokens.  The oracle gives
