@@ -153,6 +153,12 @@ def round_leg(dev, n):
         one_round()
     torch.cuda.synchronize()
     eager_ms = timed(one_round, n, dev)
+    sv.timing_enable(dev, True)
+    for _ in range(20):
+        one_round()
+    torch.cuda.synchronize()
+    kt = sv.timing_read(dev)
+    sv.timing_enable(dev, False)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         one_round()
@@ -170,6 +176,7 @@ def round_leg(dev, n):
     return {"workload": "B=512 k_b in [2, 8] from the controller (window 64) V=128256 bf16, "
                         "T_b ~ U[0.1, 1], no top-p, page-table rollback",
             "graph_ms_per_round": graph_ms, "eager_ms_per_round": eager_ms,
+            "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "mean_k": mean_k, "verified_positions_per_s": mean_k * B / (graph_ms * 1e-3),
             "mean_accepted": acc.float().mean().item()}
 

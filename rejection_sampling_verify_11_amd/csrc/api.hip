@@ -83,13 +83,14 @@ constexpr int32_t kMaxVSampled = SV_MAX_V_SAMPLED;  // inverse-CDF segment table
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-vector records, then the queue counters of the bf16 stats kernel.
+// Per-vector records, then the queue counters, slot count and slot list of
+// the bf16 stats kernel.
 size_t recs_bytes(int32_t B, int32_t K) {
   return align_up((size_t)B * sv::slots_per_row(K) * sizeof(sv::VecRec), 256);
 }
 
 size_t sample_ws(int32_t B, int32_t K) {
-  return recs_bytes(B, K) + align_up(sv::stats_ticket_bytes(), 256);
+  return recs_bytes(B, K) + sv::stats_plan_bytes(B, K);
 }
 
 size_t greedy_ws(int32_t B, int32_t K, int32_t V) {
@@ -207,7 +208,11 @@ static sv::StatsParams stats_params(const sv_verify_args* a, int mode) {
   p.flags = a->flags;
   p.mode = mode;
   p.recs = (sv::VecRec*)a->workspace;
-  p.tickets = (uint32_t*)((char*)a->workspace + recs_bytes(a->B, a->k_max));
+  char* plan = (char*)a->workspace + recs_bytes(a->B, a->k_max);
+  p.tickets = (uint32_t*)plan;
+  p.slot_count = (int32_t*)(plan + align_up(sv::stats_ticket_bytes(), 256));
+  const bool listed = a->k_per_row != nullptr || mode == 1;
+  p.slot_list = listed ? p.slot_count + 64 : nullptr;
   return p;
 }
 

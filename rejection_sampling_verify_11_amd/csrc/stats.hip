@@ -275,8 +275,12 @@ constexpr int kWords = kNE * 128;        // 5120 words, 20 KB
 constexpr int kGroups = kWords / 4;      // 16-byte groups of the table
 constexpr int kGpt = kGroups / kT;       // groups per thread
 constexpr int kBins = kGroups / 64;      // bins of 256 magnitudes, per sign
-constexpr int kRankBins = 2 * kBins + 1; // -bins, zero, +bins
-constexpr int kZeroBin = kBins;          // rank bin of the value 0
+// Rank bins, in value order: the -magnitude bins (largest magnitude first),
+// the nonzero -values below the window, 0, the nonzero +values below the
+// window, then the +magnitude bins.
+constexpr int kRankBins = 2 * kBins + 3;
+constexpr int kZeroBin = kBins + 1;      // rank bin of the value 0
+constexpr int kTinyCap = 64;             // values below the window kept per vector
 static_assert(kGroups % kT == 0 && kGpt * kWv <= kBins * 2, "table tiling");
 static_assert(kBins == kWv * kGpt, "one (wave, row) per bin");
 
@@ -293,8 +297,8 @@ static_assert((kCopyWords * 4) % 16 == 0, "copies are 16-byte aligned");
 constexpr uint32_t kFallback = 1u << 30;  // internal: the table cannot hold the vector
 
 // Rank bin of magnitude bin b: +values above zero, -values below.
-__device__ __forceinline__ int pos_bin(int b) { return kZeroBin + 1 + b; }
-__device__ __forceinline__ int neg_bin(int b) { return kZeroBin - 1 - b; }
+__device__ __forceinline__ int pos_bin(int b) { return kZeroBin + 2 + b; }
+__device__ __forceinline__ int neg_bin(int b) { return kZeroBin - 2 - b; }
 
 // Counts logit k of a 16-byte group known to lie in the window.
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t k) {
@@ -318,11 +322,13 @@ struct Side {
 };
 
 // Counts logit k when `valid`: in the window into the table, else into the
-// thread's side counters (zero, -inf) or flags (NaN / +inf: error; any other
-// value: fallback).  No branches: the atomic always runs, adding 0 to a word
-// of the thread's own (`spare`) when there is nothing to count.
-__device__ __forceinline__ void count_slow(uint32_t* hist, uint32_t k, bool valid, uint32_t spare,
-                                          Side& sd) {
+// thread's side counters (zero, -inf), the vector's list of nonzero values
+// below the window (`tiny`: count, then up to kTinyCap raw values), or flags
+// (NaN / +inf: error; a finite value above the window or a full list:
+// fallback).  The table atomic always runs, adding 0 to a word of the
+// thread's own (`spare`) when there is nothing to count.
+__device__ __forceinline__ void count_slow(uint32_t* hist, uint32_t* tiny, uint32_t k, bool valid,
+                                          uint32_t spare, Side& sd) {
   const uint32_t mag = k & 0x7FFFu;
   const uint32_t word = mag - kBase;
   const bool inw = valid && word < (uint32_t)kWords;
@@ -333,7 +339,12 @@ __device__ __forceinline__ void count_slow(uint32_t* hist, uint32_t k, bool vali
   sd.nzero += (out && mag == 0u) ? 1u : 0u;
   sd.nninf += (out && k == 0xFF80u) ? 1u : 0u;
   sd.flags |= (out && mag >= 0x7F80u && k != 0xFF80u) ? (uint32_t)SV_ROW_NONFINITE_LOGIT : 0u;
-  sd.flags |= (out && mag != 0u && mag < 0x7F80u) ? kFallback : 0u;
+  sd.flags |= (out && mag >= kBase + (uint32_t)kWords && mag < 0x7F80u) ? kFallback : 0u;
+  if (out && mag != 0u && mag < kBase) {
+    const uint32_t i = __hip_atomic_fetch_add(tiny, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (i < (uint32_t)kTinyCap) tiny[1 + i] = k;
+    else sd.flags |= kFallback;
+  }
 }
 
 __device__ __forceinline__ void count_group_fast(uint32_t* hist, const uint4& d) {
@@ -342,25 +353,55 @@ __device__ __forceinline__ void count_group_fast(uint32_t* hist, const uint4& d)
   hist_add(hist, d.z & 0xFFFFu); hist_add(hist, d.z >> 16);
   hist_add(hist, d.w & 0xFFFFu); hist_add(hist, d.w >> 16);
 }
-__device__ __forceinline__ void count_group_slow(uint32_t* hist, const uint4& d, bool valid,
-                                                uint32_t spare, Side& sd) {
-  count_slow(hist, d.x & 0xFFFFu, valid, spare, sd); count_slow(hist, d.x >> 16, valid, spare, sd);
-  count_slow(hist, d.y & 0xFFFFu, valid, spare, sd); count_slow(hist, d.y >> 16, valid, spare, sd);
-  count_slow(hist, d.z & 0xFFFFu, valid, spare, sd); count_slow(hist, d.z >> 16, valid, spare, sd);
-  count_slow(hist, d.w & 0xFFFFu, valid, spare, sd); count_slow(hist, d.w >> 16, valid, spare, sd);
+
+// Counts logit k, known to lie in the window, when `valid`; otherwise adds
+// 0 to the thread's spare word (no branch).
+__device__ __forceinline__ void hist_add_masked(uint32_t* hist, uint32_t k, bool valid,
+                                                uint32_t spare) {
+  const uint32_t word = (k & 0x7FFFu) - kBase;
+  const uint32_t inc = valid ? 1u << ((k >> 11) & 16u) : 0u;
+  __hip_atomic_fetch_add(hist + (valid ? word : spare), inc, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void count_group_masked(uint32_t* hist, const uint4& d, bool valid,
+                                                  uint32_t spare) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hist_add_masked(hist, w[q] & 0xFFFFu, valid, spare);
+    hist_add_masked(hist, w[q] >> 16, valid, spare);
+  }
+}
+__device__ __forceinline__ void count_group_slow(uint32_t* hist, uint32_t* tiny, const uint4& d,
+                                                bool valid, uint32_t spare, Side& sd) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    count_slow(hist, tiny, w[q] & 0xFFFFu, valid, spare, sd);
+    count_slow(hist, tiny, w[q] >> 16, valid, spare, sd);
+  }
 }
 
-// A full batch holding a logit outside the window (rare).  Out of line, with
-// everything passed by value, so that its register needs do not weigh on the
-// streaming loop.
+// A batch holding a logit outside the window (rare); group q counts when
+// bit q of vmask is set.  Out of line, with everything passed by value, so
+// that its register needs do not weigh on the streaming loop.
 static_assert(kBatch == 4, "count_batch_slow takes four groups");
-__device__ __attribute__((noinline)) Side count_batch_slow(uint32_t* hist, uint4 d0, uint4 d1,
-                                                           uint4 d2, uint4 d3, uint32_t spare,
-                                                           Side sd) {
-  count_group_slow(hist, d0, true, spare, sd);
-  count_group_slow(hist, d1, true, spare, sd);
-  count_group_slow(hist, d2, true, spare, sd);
-  count_group_slow(hist, d3, true, spare, sd);
+__device__ __attribute__((noinline)) Side count_batch_slow(uint32_t* hist, uint32_t* tiny,
+                                                           uint4 d0, uint4 d1, uint4 d2, uint4 d3,
+                                                           uint32_t vmask, uint32_t spare, Side sd) {
+  count_group_slow(hist, tiny, d0, vmask & 1u, spare, sd);
+  count_group_slow(hist, tiny, d1, (vmask >> 1) & 1u, spare, sd);
+  count_group_slow(hist, tiny, d2, (vmask >> 2) & 1u, spare, sd);
+  count_group_slow(hist, tiny, d3, (vmask >> 3) & 1u, spare, sd);
+  return sd;
+}
+
+// The head and tail logits of a vector outside the window (rare), likewise.
+__device__ __attribute__((noinline)) Side count_pair_slow(uint32_t* hist, uint32_t* tiny,
+                                                          uint32_t xh, bool has_head, uint32_t xt,
+                                                          bool has_tail, uint32_t spare, Side sd) {
+  count_slow(hist, tiny, xh, has_head, spare, sd);
+  count_slow(hist, tiny, xt, has_tail, spare, sd);
   return sd;
 }
 
@@ -375,7 +416,8 @@ __device__ __forceinline__ void load_batch(uint4 (&d)[kBatch], const uint4* body
 // unless a logit of the batch lies outside the window (a wave-uniform test);
 // the last, partial batch and the unaligned head and tail always go through
 // the slow path.  Batch k is counted while batch k + 1 loads.
-__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist, Side& sd) {
+__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
+                                              uint32_t* tiny, Side& sd) {
   const int tid = threadIdx.x;
   const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
   int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
@@ -406,52 +448,62 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) count_group_fast(hist, a[q]);
       } else {
-        sd = count_batch_slow(hist, a[0], a[1], a[2], a[3], spare, sd);
+        sd = count_batch_slow(hist, tiny, a[0], a[1], a[2], a[3], 0xFu, spare, sd);
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) a[q] = n[q];
       i += step;
     }
     if (part) {
+      uint32_t vmask = 0, ex = 0;
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) count_group_slow(hist, a[q], i + q * kT < nb, spare, sd);
+      for (int q = 0; q < kBatch; ++q) {
+        const bool valid = i + q * kT < nb;
+        vmask |= valid ? 1u << q : 0u;
+        const uint32_t e = max(max(window_excess(a[q].x), window_excess(a[q].y)),
+                               max(window_excess(a[q].z), window_excess(a[q].w)));
+        ex = max(ex, valid ? e : 0u);
+      }
+      if (!__any(ex >= (uint32_t)kWords)) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) count_group_masked(hist, a[q], (vmask >> q) & 1u, spare);
+      } else {
+        sd = count_batch_slow(hist, tiny, a[0], a[1], a[2], a[3], vmask, spare, sd);
+      }
     }
   }
-  count_slow(hist, xh, has_head, spare, sd);
-  count_slow(hist, xt, has_tail, spare, sd);
-}
-
-// Whether the call uses slot v (reads k_per_row only when it is given).
-__device__ __forceinline__ bool slot_needed(const StatsParams& p, int v) {
-  const int per = slots_per_row(p.K);
-  const int b = v / per, j = v % per;
-  const int kb = p.k_per_row ? p.k_per_row[b] : p.K;
-  if (kb < 1 || kb > p.K) return false;
-  if (j <= p.K) return j <= kb && p.mode != 1;
-  return j - p.K - 1 < kb;
+  const uint32_t exh = has_head ? ((xh & 0x7F80u) - kBase) : 0u;
+  const uint32_t ext = has_tail ? ((xt & 0x7F80u) - kBase) : 0u;
+  if (!__any(max(exh, ext) >= (uint32_t)kWords)) {
+    hist_add_masked(hist, xh, has_head, spare);
+    hist_add_masked(hist, xt, has_tail, spare);
+  } else {
+    sd = count_pair_slow(hist, tiny, xh, has_head, xt, has_tail, spare, sd);
+  }
 }
 
 // Vectors are handed out dynamically: a workgroup that finishes early takes
 // the next vector, so the workgroups of a CU drift apart and one's epilogue
 // overlaps the others' streaming (a fixed schedule keeps them in step).  One
 // counter for all would queue hundreds of device-scope atomics on a single
-// address, so the vectors are split into kQueues interleaved queues (queue q
-// holds vectors q, q + kQueues, ...), each with its own counter 128 bytes
-// apart and served by the workgroups g with g % kQueues == q.  Ticket t of
-// queue q is vector q + kQueues t; workgroup g's first ticket is g / kQueues
-// (no atomic) and each counter starts at its queue's number of workgroups.
+// address, so the work items are split into kQueues interleaved queues
+// (queue q holds items q, q + kQueues, ...), each with its own counter 128
+// bytes apart and served by the workgroups g with g % kQueues == q.  Ticket
+// t of queue q is item q + kQueues t; workgroup g's first ticket is
+// g / kQueues (no atomic) and each counter starts at its queue's number of
+// workgroups.  Item i is slot i, or the i-th entry of the slot list when the
+// call uses only some slots: a skipped slot costs no ticket.
 constexpr int kQueues = 64;
 constexpr int kQueueStride = 32;  // uint32 words between counters
 
-__device__ __forceinline__ int queue_slot(int q, uint32_t t) { return q + kQueues * (int)t; }
+__device__ __forceinline__ int queue_item(int q, uint32_t t) { return q + kQueues * (int)t; }
 
-// Next used slot of queue q from its counter (nslots or more: none left).
-__device__ __forceinline__ int take_ticket(const StatsParams& p, int q, int nslots) {
-  int v;
-  do {
-    v = queue_slot(q, atomicAdd(p.tickets + q * kQueueStride, 1u));
-  } while (v < nslots && !slot_needed(p, v));
-  return v;
+__device__ __forceinline__ int take_ticket(const StatsParams& p, int q) {
+  return queue_item(q, atomicAdd(p.tickets + q * kQueueStride, 1u));
+}
+
+__device__ __forceinline__ int item_slot(const StatsParams& p, int item) {
+  return p.slot_list ? p.slot_list[item] : item;
 }
 
 // A used slot's vector and parameters (the fields of slot_of).  The vector
@@ -557,33 +609,63 @@ __device__ __forceinline__ double readlane_f64(double x, int L) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Level 2 of the top-p search when the crossing lies among the nonzero
+// values below the window (one sign), run by one wave on the vector's list
+// of them (n entries, n <= kTinyCap, one per lane).  Each lane forms the mass
+// of the listed values of its sign that are >= its own (equal values are one
+// value); the threshold is the largest value whose inclusive mass reaches
+// the target (the smallest present if rounding leaves the target just out
+// of reach), as in crossing_value.
+__device__ __forceinline__ void tiny_crossing(const uint32_t* tiny, uint32_t n, bool pos,
+                                              double above, double target, float m, float c2,
+                                              float* tau, double* kept) {
+  const int l = threadIdx.x & 63;
+  const bool in = (uint32_t)l < n;
+  const uint32_t k = tiny[1 + (in ? l : 0)];
+  const bool valid = in && (((k & 0x8000u) == 0u) == pos);
+  const float v = bf16f(k);
+  const double wt = valid ? weight(v, m, c2) : 0.0;
+  double ge = 0.0;
+  for (int j = 0; j < 64; ++j) {
+    const float vj = __shfl(v, j, 64);
+    const double wj = __shfl(wt, j, 64);
+    ge += vj >= v ? wj : 0.0;  // wj is 0 for lanes outside the bin
+  }
+  const uint64_t hit = __ballot(valid && above + ge >= target);
+  const float cand = hit ? (((hit >> l) & 1u) ? v : -INFINITY) : (valid ? -v : -INFINITY);
+  float best = wave_max_f(cand);
+  if (!hit) best = -best;
+  const uint64_t at = __ballot(valid && v == best);
+  const int L = at ? __builtin_ctzll(at) : 0;
+  *tau = best;
+  *kept = readlane_f64(above + ge, L);
+}
+
 __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p) {
   __shared__ __align__(16) uint32_t hist[kCopies * kCopyWords];
   __shared__ double bins[kRankBins];
   __shared__ Bf16Shared sh;
+  __shared__ uint32_t tiny[1 + kTinyCap];  // values below the window: count, then values
   __shared__ double hist256[256];       // generic path
   __shared__ Scratch<kWv> sc;           // generic path
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int V = p.V;
-  const int nslots = p.B * slots_per_row(p.K);
+  const int nitems = p.slot_list ? *p.slot_count : p.B * slots_per_row(p.K);
   uint4* hist4 = reinterpret_cast<uint4*>(hist);
 
+  // the first item; a workgroup without one has none later either
+  const int queue = (int)(blockIdx.x % kQueues);
+  if (queue_item(queue, blockIdx.x / kQueues) >= nitems) return;
+  int v = item_slot(p, queue_item(queue, blockIdx.x / kQueues));
   for (int i = tid; i < kCopies * kCopyWords; i += kT) hist[i] = 0;
+  if (tid == 0) tiny[0] = 0u;
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
-  const int queue = (int)(blockIdx.x % kQueues);
-  int v = queue_slot(queue, blockIdx.x / kQueues);
-  if (v >= nslots || !slot_needed(p, v)) {
-    if (tid == 0) sh.next = take_ticket(p, queue, nslots);
-    __syncthreads();
-    v = sh.next;
-    if (v >= nslots) return;
-  }
   SlotP cur = slot_params(p, v);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
-    if (tid == 0) sh.next = take_ticket(p, queue, nslots);
+    if (tid == 0) sh.next = take_ticket(p, queue);
     const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
     // the draft token's logit, loaded by every thread from one address
@@ -591,7 +673,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     const uint32_t zbits = cur.vec[has_zx ? cur.token : 0];
 
     Side sd;
-    stream_vector(cur.vec, V, hcopy, sd);
+    stream_vector(cur.vec, V, hcopy, tiny, sd);
     {
       const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nzero));
       const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nninf));
@@ -599,9 +681,10 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       if (l == 0) { sh.wzero[w] = z; sh.wninf[w] = n; sh.wflag[w] = f; }
     }
     __syncthreads();  // B1: table complete
-    const int vn = sh.next;
-    const bool has_next = vn < nslots;
-    const SlotP nxt = slot_params(p, has_next ? vn : v);  // loads in flight meanwhile
+    const int in = sh.next;
+    const bool has_next = in < nitems;
+    const int vn = has_next ? item_slot(p, in) : v;
+    const SlotP nxt = slot_params(p, vn);  // loads in flight meanwhile
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
     // and clears copy 1; largest +magnitude, smallest -magnitude present,
@@ -653,10 +736,14 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       WR |= sh.wwrap[k];
     }
     uint32_t status = FL & SV_ROW_NONFINITE_LOGIT;
+    const uint32_t NT = tiny[0];
     // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
-    // count past 65535), or a logit outside the window: the generic path
+    // count past 65535), a logit above the window, more values below it than
+    // the list holds, or no positive value in the window while some lie
+    // below it (the largest logit would be one of them): the generic path
     // redoes the vector
-    const bool fallback = !status && ((FL & kFallback) || WR || TT + Z + NI != (uint32_t)V);
+    const bool fallback = !status && ((FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V ||
+                                      (MP < 0 && NT > 0));
     if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
     const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
                   : Z > 0   ? 0.0f
@@ -691,6 +778,18 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
         if (l == 0) { bins[pos_bin(b)] = mp; bins[neg_bin(b)] = mn; }
       }
       if (tid == 0) bins[kZeroBin] = Z ? (double)Z * weight(0.0f, m, c2) : 0.0;
+      if (w == kWv - 1) {  // the listed values below the window, by sign
+        double tp = 0.0, tn = 0.0;
+        if (NT) {
+          const bool has = (uint32_t)l < NT;
+          const uint32_t k = tiny[1 + (has ? l : 0)];
+          const double wt = has ? weight(bf16f(k), m, c2) : 0.0;
+          const bool neg = (k & 0x8000u) != 0u;
+          tp = wave_last_f64(wave_scan_add_f64(neg ? 0.0 : wt));
+          tn = wave_last_f64(wave_scan_add_f64(neg ? wt : 0.0));
+        }
+        if (l == 0) { bins[kZeroBin + 1] = tp; bins[kZeroBin - 1] = tn; }
+      }
     }
     __syncthreads();  // B3: bins written
 
@@ -716,10 +815,12 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
           if (RL == kZeroBin) {
             tau = 0.0f;
             kept = above + readlane_f64(part, L);
+          } else if (RL == kZeroBin + 1 || RL == kZeroBin - 1) {
+            tiny_crossing(tiny, NT, RL > kZeroBin, above, target, m, c2, &tau, &kept);
           } else if (RL > kZeroBin) {
-            crossing_value(hist4, RL - kZeroBin - 1, true, above, target, m, c2, &tau, &kept);
+            crossing_value(hist4, RL - kZeroBin - 2, true, above, target, m, c2, &tau, &kept);
           } else if (RL >= 0) {
-            crossing_value(hist4, kZeroBin - 1 - RL, false, above, target, m, c2, &tau, &kept);
+            crossing_value(hist4, kZeroBin - 2 - RL, false, above, target, m, c2, &tau, &kept);
           }
         }
       }
@@ -731,6 +832,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       generic_stats<kT>(cur.vec, cur.token, cur.T, cur.P, SV_BF16, V, hist256, sc, rec);
     }
     __syncthreads();  // B4: the table is no longer read
+    if (tid == 0) tiny[0] = 0u;
 #pragma unroll 1
     for (int j = 0; j < kGpt; ++j)
       if ((gmask >> j) & 1u) hist4[tid + kT * j] = make_uint4(0u, 0u, 0u, 0u);
@@ -740,17 +842,61 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   }
 }
 
-// Counter q starts at the number of workgroups serving queue q (their first
-// tickets are taken without it).
-__global__ void stats_queue_reset_kernel(uint32_t* tickets, uint32_t grid) {
-  const uint32_t q = threadIdx.x;
-  if (q < (uint32_t)kQueues)
-    tickets[q * kQueueStride] = grid > q ? (grid - q + kQueues - 1) / kQueues : 0u;
+// Runs before the bf16 stats kernel, one workgroup.  Counter q starts at the
+// number of workgroups serving queue q (their first tickets are taken
+// without it).  With a slot list, rows are numbered in tiles of kPlanT: a
+// block-wide exclusive scan of each row's slot count gives its place in the
+// list, and the row writes its slots there in slot order (target positions
+// 0..k_b, then draft positions 0..k_b - 1; draft positions only when
+// sampling drafts).  A row with k_b outside [1, K] lists nothing.
+constexpr int kPlanT = 1024;
+
+__global__ __launch_bounds__(kPlanT) void stats_plan_kernel(StatsParams p, uint32_t grid) {
+  __shared__ uint32_t wsum[kPlanT / 64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  if (tid < kQueues)
+    p.tickets[tid * kQueueStride] = grid > (uint32_t)tid ? (grid - tid + kQueues - 1) / kQueues : 0u;
+  if (!p.slot_list) return;
+  const int K = p.K, per = slots_per_row(K);
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < p.B; b0 += kPlanT) {
+    const int b = b0 + tid;
+    const int kb = b < p.B ? (p.k_per_row ? p.k_per_row[b] : K) : 0;
+    const bool ok = b < p.B && kb >= 1 && kb <= K;
+    const uint32_t n = ok ? (p.mode == 1 ? (uint32_t)kb : 2u * (uint32_t)kb + 1u) : 0u;
+    const uint32_t incl = wave_scan_u32<OpAddU32>(n);
+    if (l == 63) wsum[w] = incl;
+    __syncthreads();
+    uint32_t before = carry, total = carry;
+#pragma unroll
+    for (int k = 0; k < kPlanT / 64; ++k) {
+      before += k < w ? wsum[k] : 0u;
+      total += wsum[k];
+    }
+    __syncthreads();  // wsum is rewritten by the next tile
+    int32_t* out = p.slot_list + before + (incl - n);
+    const int s0 = b * per;
+    if (ok) {
+      int o = 0;
+      if (p.mode != 1)
+        for (int j = 0; j <= kb; ++j) out[o++] = s0 + j;
+      for (int i = 0; i < kb; ++i) out[o++] = s0 + K + 1 + i;
+    }
+    carry = total;
+  }
+  if (tid == 0) *p.slot_count = (int32_t)carry;
 }
 
 }  // namespace
 
 size_t stats_ticket_bytes() { return (size_t)kQueues * kQueueStride * sizeof(uint32_t); }
+
+size_t stats_plan_bytes(int32_t B, int32_t K) {
+  const size_t nslots = (size_t)(B > 0 ? B : 0) * (size_t)slots_per_row(K);
+  const size_t tickets = (stats_ticket_bytes() + 255) / 256 * 256;
+  const size_t list = (64 * sizeof(int32_t) + nslots * sizeof(int32_t) + 255) / 256 * 256;
+  return tickets + list;
+}
 
 hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_t s, Timer* t) {
   const unsigned nslots = (unsigned)p.B * (unsigned)slots_per_row(p.K);
@@ -762,7 +908,10 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
     unsigned want = cus * (unsigned)kWgPerCu;
     if (want < (unsigned)kQueues) want = (unsigned)kQueues;
     const unsigned grid = nslots < want ? nslots : want;
-    hipLaunchKernelGGL(stats_queue_reset_kernel, dim3(1), dim3(kQueues), 0, s, p.tickets, grid);
+    {
+      TimedScope ts(t, "stats_plan", s);
+      hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
+    }
     TimedScope ts(t, "stats_bf16", s);
     hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, p);
   } else {

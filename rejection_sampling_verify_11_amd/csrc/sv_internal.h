@@ -69,10 +69,16 @@ struct StatsParams {
   uint32_t flags;
   int32_t mode;  // 0 verification (all slots), 1 draft sampling (draft slots only)
   VecRec* recs;
-  uint32_t* tickets;  // queue counters of the bf16 kernel (workspace, after the records)
+  uint32_t* tickets;     // queue counters of the bf16 kernel (workspace, after the records)
+  int32_t* slot_count;   // with slot_list: the number of listed slots
+  int32_t* slot_list;    // the slots the call uses, in order, when some rows
+                         // use fewer than all of theirs (k_per_row given, or
+                         // draft sampling); NULL: every slot, slot = item
 };
 
-// Bytes of workspace the bf16 stats kernel keeps its queue counters in.
+// Bytes of workspace the bf16 stats kernel keeps its queue counters, slot
+// count and slot list in (after the records).
+size_t stats_plan_bytes(int32_t B, int32_t K);
 size_t stats_ticket_bytes();
 
 struct FinalizeParams {

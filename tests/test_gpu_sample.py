@@ -210,6 +210,55 @@ def test_count_overflow_falls_back_exactly(oracle):
     assert rep.exact_rows == B
 
 
+def test_values_below_the_count_window(oracle):
+    """Nonzero logits below 2^-24 in magnitude (a few per vector in
+    N(0, 3^2) logits) are listed beside the count table: scattered ones with
+    both signs, exact ties among them, zeros next to them, top-p thresholds
+    that fall inside the listed values of either sign, and more of them than
+    the list holds (the generic path then redoes the vector)."""
+    V, K = 4096, 3
+    g = torch.Generator().manual_seed(21)
+    tiny_pos = [2.0 ** -30, 2.0 ** -27, 2.0 ** -27, 3 * 2.0 ** -40, 2.0 ** -100, 2.0 ** -130]
+    tiny_neg = [-t for t in tiny_pos]
+    rows = []
+    # row 0: N(0, 3^2) with scattered tiny values and zeros
+    z = torch.randn((K + 1, V), generator=g) * 3
+    for i in range(K + 1):
+        idx = torch.randperm(V, generator=g)[:12]
+        z[i, idx[:6]] = torch.tensor(tiny_pos)
+        z[i, idx[6:]] = torch.tensor(tiny_neg)
+        z[i, torch.randperm(V, generator=g)[:3]] = 0.0
+    rows.append(z)
+    # rows 1, 2: the top-p crossing among the positive / the negative tiny
+    # values: one value 2^-10 in the window, the listed ones, the rest at -8
+    for sign in (1.0, -1.0):
+        z = torch.full((K + 1, V), -8.0)
+        for i in range(K + 1):
+            idx = torch.randperm(V, generator=g)[:40]
+            z[i, idx[0]] = 2.0 ** -10
+            vals = torch.tensor([sign * 2.0 ** -(30 + (j % 13)) for j in range(39)])
+            z[i, idx[1:]] = vals  # ties: j and j + 13 share a value
+        rows.append(z)
+    # row 3: more listed values than the list holds
+    z = torch.randn((K + 1, V), generator=g)
+    z[:, :100] = 2.0 ** -60
+    z[:, 100:180] = -(2.0 ** -33)
+    rows.append(z)
+    zt = torch.stack(rows)
+    B = zt.shape[0]
+    zd = zt[:, :K].clone()
+    zd[:, :, ::7] = zd[:, :, ::7] * 0.5
+    P = torch.tensor([0.9, 0.5, 0.5, 0.9])
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.ones(B), P)
+    rep = Report()
+    for r in range(6):
+        toks = oracle_tokens(oracle, inp, 3, r)
+        rep.merge(check_round(oracle, inp, toks, 3, r))
+    print("below-window:", rep)
+    assert rep.exact_rows + rep.flagged_rows == rep.rows
+    assert rep.exact_rows >= rep.rows - 2
+
+
 def test_degenerate_distributions(oracle):
     V = 4096
     g = torch.Generator().manual_seed(4)
