@@ -101,6 +101,7 @@ def timed(fn, n, dev):
 
 def greedy_leg(dev, n):
     """Greedy verification (draft tokens given), B=64, k=8, V=128256 bf16."""
+    import torch
     import rejection_sampling_verify_11_amd as sv
     from rejection_sampling_verify_11_amd import workloads as W
     B, K, V = 64, 8, 128256
@@ -109,10 +110,17 @@ def greedy_leg(dev, n):
     for _ in range(20):
         call.run()
     ms = timed(call.run, n, dev)
+    sv.timing_enable(dev, True)
+    for _ in range(20):
+        call.run()
+    torch.cuda.synchronize()
+    kt = sv.timing_read(dev)
+    sv.timing_enable(dev, False)
     assert int((call.outputs["row_status"] != 0).sum()) == 0
     target_bytes = B * (K + 1) * V * 2
     return {"workload": "B=64 k=8 V=128256 bf16 greedy, draft = target argmax w.p. 0.85",
             "ms_per_call": ms, "target_gbs": target_bytes / (ms * 1e-3) / 1e9,
+            "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "verified_positions_per_s": B * K / (ms * 1e-3),
             "mean_accepted": call.outputs["accepted"].float().mean().item()}
 

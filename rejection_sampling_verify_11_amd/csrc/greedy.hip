@@ -6,8 +6,10 @@
 //
 // Kernel 1 splits every vector into chunks of kGreedyChunk logits, one
 // workgroup of 256 threads per chunk, and writes (max value, first index,
-// flags) per chunk.  Kernel 2 (one workgroup per row) folds the chunks of
-// each position and makes the row's decision.
+// flags) per chunk; a thread issues all its 16-byte loads before comparing.
+// Kernel 2 runs one wave per row: lane i folds the chunks of position i
+// (target, and draft when draft logits are given), and a ballot finds the
+// first mismatch.
 #include <math.h>
 
 #include "sv_internal.h"
@@ -17,6 +19,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = kGreedyChunk / kThreads;  // 64 logits
+constexpr int kLoads = kPerThread / 8;               // 16-byte loads per thread
 
 // (v, i) beats (bv, bi): larger value, or equal value with a lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -49,16 +52,32 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
   if (p.dtype == SV_BF16 && aligned) {
     const uint16_t* base = (const uint16_t*)vec + c0;
     const int n8 = n >> 3;
-    // thread t reads 16-byte groups t, t+256, ... : increasing index order
-    for (int g = tid; g < n8; g += kThreads) {
-      const uint4 d = *(const uint4*)(base + 8 * g);
-      const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+    // thread t reads 16-byte groups t, t+256, ... : increasing index order;
+    // all loads first (indices past the end clamp to group 0 and are skipped)
+    uint4 d[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) d[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (n8 > 0) {  // a chunk shorter than one group has only its tail loop
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int g = tid + kThreads * j;
+        d[j] = *(const uint4*)(base + 8 * (g < n8 ? g : 0));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int g = tid + kThreads * j;
+      const bool valid = g < n8;
+      const uint32_t w[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float z = __uint_as_float(t & 1 ? (w[t >> 1] & 0xFFFF0000u) : (w[t >> 1] << 16));
-        if (isnan(z) || z == INFINITY) fl |= SV_ROW_NONFINITE_LOGIT;
-        else if (z > -INFINITY) fl |= kSawFinite;
-        if (z > bv || (bi < 0 && z == -INFINITY)) { bv = z; bi = (int)(c0 + 8 * g + t); }
+        const bool bad = isnan(z) || z == INFINITY;
+        fl |= valid && bad ? (uint32_t)SV_ROW_NONFINITE_LOGIT : 0u;
+        fl |= valid && !bad && z > -INFINITY ? kSawFinite : 0u;
+        const bool take = valid && (z > bv || (bi < 0 && z == -INFINITY));
+        bv = take ? z : bv;
+        bi = take ? (int)(c0 + 8 * g + t) : bi;
       }
     }
     for (int j = (n8 << 3) + tid; j < n; j += kThreads) {
@@ -105,70 +124,68 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
   }
 }
 
-__device__ int fold_argmax(const GreedyParams& p, int v, uint32_t* status) {
-  const int nch = greedy_chunks(p.V);
+// Folds the chunk results of vector v: (value, first index) and flags.
+__device__ __forceinline__ int fold_argmax(const GreedyParams& p, int v, int nch, uint32_t* fl) {
   float bv = -INFINITY;
   int bi = -1;
-  uint32_t fl = 0;
-  for (int c = 0; c < nch; ++c) {
-    const ArgmaxPart r = p.parts[(int64_t)v * nch + c];
-    fl |= r.status;
-    if (better(r.value, r.index, bv, bi)) { bv = r.value; bi = r.index; }
+  const ArgmaxPart* r = p.parts + (int64_t)v * nch;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    ArgmaxPart q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = r[min(c0 + u, nch - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u >= nch) break;
+      *fl |= q[u].status;
+      if (better(q[u].value, q[u].index, bv, bi)) { bv = q[u].value; bi = q[u].index; }
+    }
   }
-  uint32_t st = fl & SV_ROW_NONFINITE_LOGIT;
-  if (!(fl & kSawFinite)) st |= SV_ROW_NO_FINITE;
-  *status |= st;
   return bi;
 }
 
-__global__ void greedy_finalize_kernel(GreedyParams p) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row; lane i owns position i.
+__global__ __launch_bounds__(256) void greedy_finalize_kernel(GreedyParams p) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
   if (b >= p.B) return;
-  const int K = p.K;
+  const int K = p.K, nch = greedy_chunks(p.V);
   const int kb = p.k_per_row ? p.k_per_row[b] : K;
-  uint32_t st = 0;
-  int32_t* out = p.out_tokens + (int64_t)b * (K + 1);
-  if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
-  int acc = 0, y = -1;
-  if (!st) {
-    const int nvec_t = p.B * (K + 1);
-    // first pass: status of every vector the row uses
-    for (int i = 0; i < kb; ++i) {
+  const bool kok = kb >= 1 && kb <= K;
+  uint32_t st = kok ? 0u : (uint32_t)SV_ROW_BAD_K;
+  int g = -1, x = -1;
+  if (kok) {
+    uint32_t fl = 0;
+    if (l <= kb) {
+      uint32_t f = 0;
+      g = fold_argmax(p, b * (K + 1) + l, nch, &f);
+      fl |= f & SV_ROW_NONFINITE_LOGIT;
+      if (!(f & kSawFinite)) fl |= SV_ROW_NO_FINITE;
+    }
+    if (l < kb) {
       if (p.draft) {
-        fold_argmax(p, nvec_t + b * K + i, &st);
+        uint32_t f = 0;
+        x = fold_argmax(p, p.B * (K + 1) + b * K + l, nch, &f);
+        fl |= f & SV_ROW_NONFINITE_LOGIT;
+        if (!(f & kSawFinite)) fl |= SV_ROW_NO_FINITE;
       } else {
-        const int x = p.tokens[(int64_t)b * K + i];
-        if (x < 0 || x >= p.V) st |= SV_ROW_BAD_TOKEN;
+        x = p.tokens[(int64_t)b * K + l];
+        if (x < 0 || x >= p.V) fl |= SV_ROW_BAD_TOKEN;
       }
     }
-    for (int i = 0; i <= kb; ++i) fold_argmax(p, b * (K + 1) + i, &st);
-    if (!st) {
-      acc = kb;
-      for (int i = 0; i < kb; ++i) {
-        uint32_t dummy = 0;
-        const int x = p.draft ? fold_argmax(p, nvec_t + b * K + i, &dummy)
-                              : p.tokens[(int64_t)b * K + i];
-        const int g = fold_argmax(p, b * (K + 1) + i, &dummy);
-        if (x != g) { acc = i; y = g; break; }
-        out[i] = x;
-      }
-      if (acc == kb) {
-        uint32_t dummy = 0;
-        y = fold_argmax(p, b * (K + 1) + kb, &dummy);
-      }
-    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+    st = fl;
   }
-  if (st) {
-    for (int j = 0; j <= K; ++j) out[j] = -1;
-    p.accepted[b] = -1;
-    if (p.num_emitted) p.num_emitted[b] = 0;
-  } else {
-    out[acc] = y;
-    for (int j = acc + 1; j <= K; ++j) out[j] = -1;
-    p.accepted[b] = acc;
-    if (p.num_emitted) p.num_emitted[b] = acc + 1;
+  const uint64_t miss = __ballot(kok && l < kb && x != g);
+  const int acc = miss ? __builtin_ctzll(miss) : kb;
+  const int y = __shfl(g, (acc >= 0 && acc < 64) ? acc : 0, 64);
+  int32_t* out = p.out_tokens + (int64_t)b * (K + 1);
+  if (l <= K) out[l] = st ? -1 : l < acc ? x : l == acc ? y : -1;
+  if (l == 0) {
+    p.accepted[b] = st ? -1 : acc;
+    if (p.num_emitted) p.num_emitted[b] = st ? 0 : acc + 1;
+    if (p.row_status) p.row_status[b] = (int32_t)st;
   }
-  if (p.row_status) p.row_status[b] = (int32_t)st;
 }
 
 }  // namespace
@@ -185,7 +202,7 @@ hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t) {
   if (e != hipSuccess) return e;
   {
     TimedScope ts(t, "greedy_finalize", s);
-    hipLaunchKernelGGL(greedy_finalize_kernel, dim3((p.B + 63) / 64), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(greedy_finalize_kernel, dim3((p.B + 3) / 4), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -491,8 +491,9 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
 // bytes apart and served by the workgroups g with g % kQueues == q.  Ticket
 // t of queue q is item q + kQueues t; workgroup g's first ticket is
 // g / kQueues (no atomic) and each counter starts at its queue's number of
-// workgroups.  Item i is slot i, or the i-th entry of the slot list when the
-// call uses only some slots: a skipped slot costs no ticket.
+// workgroups.  Item i maps to a slot by item_slot, or is the i-th entry of
+// the slot list when the call uses only some slots: a skipped slot costs no
+// ticket.
 constexpr int kQueues = 64;
 constexpr int kQueueStride = 32;  // uint32 words between counters
 
@@ -502,8 +503,17 @@ __device__ __forceinline__ int take_ticket(const StatsParams& p, int q) {
   return queue_item(q, atomicAdd(p.tickets + q * kQueueStride, 1u));
 }
 
+// Without a list, items run position-major: the bonus position of every
+// row, then target and draft position K-1 of every row, ..., position 0
+// last.  Vectors streamed side by side then belong to different rows, which
+// measured ~3 % faster than the slot order (rows' vectors adjacent).
 __device__ __forceinline__ int item_slot(const StatsParams& p, int item) {
-  return p.slot_list ? p.slot_list[item] : item;
+  if (p.slot_list) return p.slot_list[item];
+  const int B = p.B, K = p.K, per = slots_per_row(K);
+  if (item < B) return item * per + K;
+  const int i = item - B, q = i / (2 * B), r = i - q * 2 * B;
+  const int pos = K - 1 - q;
+  return r < B ? r * per + pos : (r - B) * per + K + 1 + pos;
 }
 
 // A used slot's vector and parameters (the fields of slot_of).  The vector
