@@ -172,21 +172,38 @@ __device__ __forceinline__ void chunk_r(const Dist& Pd, const Dist& Qd, const Ch
   }
 }
 
-// Sum of r over the chunks of this lane in segment seg, summed over the wave
-// and stored as the segment's mass.
-template <int MODE>
-__device__ __forceinline__ void segment_sum(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
-                                            int seg, int nchunks, double* segs) {
+// Pass 1 of one segment: the sum of r over the chunks of this lane, summed
+// over the wave and stored as the segment's mass.  This version is for p'
+// without a top-p cut (tau_p = -inf, so no test on the p side), with a cut
+// on q' only when CQ.  A lane sums its 16 tokens in fp32
+// before the fp64 wave sum: the token probabilities are fp32 values anyway,
+// and the located segment is re-derived token by token in fp64.
+template <int MODE, bool CQ>
+__device__ __forceinline__ void segment_sum_uncut(const Dist& P, const Dist& Q,
+                                                  const Chunks<MODE>& c, int seg, int nchunks,
+                                                  double* segs) {
   const int l = threadIdx.x & 63;
-  double ls = 0.0;
+  float lf = 0.0f;
 #pragma unroll
   for (int s = 0; s < kCps; ++s) {
-    double r[8];
-    chunk_r<MODE>(P, Q, c, s, seg * (kSegTok / 8) + l + 64 * s < nchunks, r);
+    const bool valid = seg * (kSegTok / 8) + l + 64 * s < nchunks;
+    const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
+    float cs = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) ls += r[t];
+    for (int t = 0; t < 8; ++t) {
+      const float zp = __uint_as_float(t & 1 ? (pw[t >> 1] & 0xFFFF0000u) : (pw[t >> 1] << 16));
+      float v = __builtin_amdgcn_exp2f((zp - P.m) * P.c2) * P.invf;
+      if (MODE == 0) {
+        const uint32_t qw = t < 2 ? c.q[s].x : t < 4 ? c.q[s].y : t < 6 ? c.q[s].z : c.q[s].w;
+        const float zq = __uint_as_float(t & 1 ? (qw & 0xFFFF0000u) : (qw << 16));
+        const float qv = CQ ? prob_f(Q, zq) : __builtin_amdgcn_exp2f((zq - Q.m) * Q.c2) * Q.invf;
+        v = fmaxf(v - qv, 0.0f);
+      }
+      cs += v;
+    }
+    lf += valid ? cs : 0.0f;
   }
-  ls = wave_last_f64(wave_scan_add_f64(ls));
+  const double ls = wave_last_f64(wave_scan_add_f64((double)lf));
   if (l == 0) segs[seg] = ls;
 }
 
@@ -237,10 +254,20 @@ __device__ __forceinline__ void segment_sum_listed(const Dist& P, const Dist& Q,
   if (l == 0) segs[seg] = ls;
 }
 
+// Pass-1 variants: 0 listed tokens (p' has a top-p cut), 1 no cut on either
+// side, 2 a cut on q' only.
+enum { kPassListed = 0, kPassUncut = 1, kPassCutQ = 2 };
+
+template <int MODE, int PASS>
+__device__ __forceinline__ void pass1_segment(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
+                                              int seg, int nchunks, double* segs, uint32_t* list) {
+  if (PASS == kPassListed) segment_sum_listed<MODE>(P, Q, c, seg, nchunks, segs, list);
+  else segment_sum_uncut<MODE, PASS == kPassCutQ>(P, Q, c, seg, nchunks, segs);
+}
+
 // One inverse-CDF draw with this layout: returns y, -1 if R is 0 (the
 // caller then retries on p' alone, for MODE 0) or the distribution is empty.
-// LISTED: p' has a top-p cut and pass 1 works on listed tokens.
-template <int MODE, bool LISTED>
+template <int MODE, int PASS>
 __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch& sc) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
@@ -256,12 +283,10 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
     load_segment<MODE>(ca, Pv, Qv, w, nchunks);
     for (int G = 0; G < ngroups; G += 2) {
       load_segment<MODE>(cb, Pv, Qv, min(G + 1, ngroups - 1) * kWaves + w, nchunks);
-      if (LISTED) segment_sum_listed<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg, list);
-      else segment_sum<MODE>(P, Q, ca, G * kWaves + w, nchunks, sc.seg);
+      pass1_segment<MODE, PASS>(P, Q, ca, G * kWaves + w, nchunks, sc.seg, list);
       if (G + 1 >= ngroups) break;
       load_segment<MODE>(ca, Pv, Qv, min(G + 2, ngroups - 1) * kWaves + w, nchunks);
-      if (LISTED) segment_sum_listed<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg, list);
-      else segment_sum<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg);
+      pass1_segment<MODE, PASS>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg, list);
     }
   }
   __syncthreads();
@@ -343,15 +368,18 @@ __device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, in
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
       (mode == 1 || is_aligned16(Q.vec))) {
     *zero_residual = false;
-    const bool cut = P.tau > -INFINITY;  // the same in every thread
+    // the same in every thread
+    const bool cutp = P.tau > -INFINITY, cutq = Q.tau > -INFINITY;
     if (mode == 0) {
-      const int y = cut ? inverse_cdf_bf16<0, true>(P, Q, V, u, sc)
-                        : inverse_cdf_bf16<0, false>(P, Q, V, u, sc);
+      const int y = cutp ? inverse_cdf_bf16<0, kPassListed>(P, Q, V, u, sc)
+                  : cutq ? inverse_cdf_bf16<0, kPassCutQ>(P, Q, V, u, sc)
+                         : inverse_cdf_bf16<0, kPassUncut>(P, Q, V, u, sc);
       if (y >= 0) return y;
       // R == 0: the residual vanishes identically; draw from p' instead
       *zero_residual = true;
     }
-    return cut ? inverse_cdf_bf16<1, true>(P, P, V, u, sc) : inverse_cdf_bf16<1, false>(P, P, V, u, sc);
+    return cutp ? inverse_cdf_bf16<1, kPassListed>(P, P, V, u, sc)
+                : inverse_cdf_bf16<1, kPassUncut>(P, P, V, u, sc);
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = (V + kTile - 1) / kTile;
