@@ -26,6 +26,33 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
 }
 
+// Order keys of the two bf16 logits of a 32-bit word, per 16-bit half:
+// h | 0x8000 for a +value, ~h for a -value, so that a larger float has a
+// larger unsigned key (-inf 0x007F, -0 0x7FFF, +0 0x8000, +inf 0xFF80; a
+// +NaN lies above +inf, a -NaN below -inf).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 order_keys(uint32_t w) {
+  const s16x2 h = __builtin_bit_cast(s16x2, w);
+  const s16x2 neg = h >> (short)15;  // all ones in a half that holds a -value
+  const uint32_t m = __builtin_bit_cast(uint32_t, neg) & 0x7FFF7FFFu;
+  return __builtin_bit_cast(u16x2, w ^ m ^ 0x80008000u);
+}
+__device__ __forceinline__ uint32_t key_of(uint32_t h) {  // one half
+  return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ float value_of_key(uint32_t k) {
+  const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return __uint_as_float(h << 16);
+}
+// Keys of equal floats: the two zeros are one value.
+__device__ __forceinline__ bool same_value(uint32_t k, uint32_t kmax) {
+  const bool zero = kmax == 0x8000u || kmax == 0x7FFFu;
+  return zero ? (k == 0x8000u || k == 0x7FFFu) : k == kmax;
+}
+constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyPosInf = 0xFF80u;
+
 __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p) {
   const int nch = greedy_chunks(p.V);
   const int nvec_t = p.B * (p.K + 1);
@@ -41,15 +68,73 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
   const char* vec = draft_side
       ? (const char*)p.draft + ((int64_t)b * p.K + pos) * p.d_stride * esz
       : (const char*)p.target + ((int64_t)b * (p.K + 1) + pos) * p.t_stride * esz;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int64_t c0 = (int64_t)c * kGreedyChunk;
   const int n = (int)min((int64_t)kGreedyChunk, (int64_t)p.V - c0);
+  __shared__ float sv_[kThreads / 64];
+  __shared__ int si_[kThreads / 64];
+  __shared__ uint32_t sf_[kThreads / 64];
 
   float bv = -INFINITY;
   int bi = -1;
   uint32_t fl = 0;
   const bool aligned = ((((uintptr_t)vec) + c0 * esz) & 15u) == 0;
-  if (p.dtype == SV_BF16 && aligned) {
+  if (p.dtype == SV_BF16 && aligned && n == kGreedyChunk) {
+    // Full bf16 chunk: the largest order key with packed 16-bit max/min over
+    // the thread's 64 logits, the chunk's largest key by a block max, then
+    // the first index holding it, searched only by the threads that hold it.
+    const uint16_t* base = (const uint16_t*)vec + c0;
+    uint4 d[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) d[j] = *(const uint4*)(base + 8 * (tid + kThreads * j));
+    u16x2 kmax = {0, 0}, kmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u16x2 k = order_keys(ws[q]);
+        kmax = __builtin_elementwise_max(kmax, k);
+        kmin = __builtin_elementwise_min(kmin, k);
+      }
+    }
+    uint32_t tmax = max((uint32_t)kmax.x, (uint32_t)kmax.y);
+    uint32_t tmin = min((uint32_t)kmin.x, (uint32_t)kmin.y);
+    const uint32_t t0 = tmax;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, o, 64));
+      tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, o, 64));
+    }
+    if (l == 0) { si_[w] = (int)tmax; sf_[w] = tmin; }
+    __syncthreads();
+    uint32_t cmax = 0, cmin = 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) {
+      cmax = max(cmax, (uint32_t)si_[k]);
+      cmin = min(cmin, sf_[k]);
+    }
+    __syncthreads();  // si_ and sf_ are reused below
+    // flags: +inf or a NaN above +inf, a NaN below -inf; a finite value
+    // exists if the largest key is finite
+    if (cmax >= kKeyPosInf || cmin < kKeyNegInf) fl |= SV_ROW_NONFINITE_LOGIT;
+    if (cmax > kKeyNegInf && cmax < kKeyPosInf) fl |= kSawFinite;
+    if (same_value(t0, cmax)) {  // this thread holds the chunk's largest value
+      int first = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t h = t & 1 ? ws[t >> 1] >> 16 : ws[t >> 1] & 0xFFFFu;
+          const int idx = (int)(c0 + 8 * (tid + kThreads * j) + t);
+          first = same_value(key_of(h), cmax) ? min(first, idx) : first;
+        }
+      }
+      bi = first;
+      bv = value_of_key(cmax);
+    }
+  } else if (p.dtype == SV_BF16 && aligned) {
     const uint16_t* base = (const uint16_t*)vec + c0;
     const int n8 = n >> 3;
     // thread t reads 16-byte groups t, t+256, ... : increasing index order;
@@ -68,10 +153,10 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
     for (int j = 0; j < kLoads; ++j) {
       const int g = tid + kThreads * j;
       const bool valid = g < n8;
-      const uint32_t w[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+      const uint32_t w4[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float z = __uint_as_float(t & 1 ? (w[t >> 1] & 0xFFFF0000u) : (w[t >> 1] << 16));
+        const float z = __uint_as_float(t & 1 ? (w4[t >> 1] & 0xFFFF0000u) : (w4[t >> 1] << 16));
         const bool bad = isnan(z) || z == INFINITY;
         fl |= valid && bad ? (uint32_t)SV_ROW_NONFINITE_LOGIT : 0u;
         fl |= valid && !bad && z > -INFINITY ? kSawFinite : 0u;
@@ -104,10 +189,6 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
     fl |= __shfl_xor(fl, o, 64);
     if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
-  __shared__ float sv_[kThreads / 64];
-  __shared__ int si_[kThreads / 64];
-  __shared__ uint32_t sf_[kThreads / 64];
-  const int w = tid >> 6, l = tid & 63;
   if (l == 0) { sv_[w] = bv; si_[w] = bi; sf_[w] = fl; }
   __syncthreads();
   if (tid == 0) {

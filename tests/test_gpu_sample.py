@@ -122,6 +122,23 @@ def test_workload5_ragged_per_row_temperature(oracle):
     assert rep.exact_rows >= rep.rows - 1
 
 
+def test_workload5_full_batch_sampled_rows(oracle):
+    """The ragged workload at full size: B=512, k_b in [2, 8], V=128256 bf16,
+    per-row temperature and noise, no top-p, one call; 16 rows spread over
+    the batch are checked one by one."""
+    B = 512
+    rows = W.workload5_rows(0, B=B, device=DEV)
+    k = torch.randint(2, 9, (B,), generator=torch.Generator().manual_seed(9),
+                      dtype=torch.int32).to(DEV)
+    inp = W.workload5(0, rows, k, device=DEV)
+    toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 0)
+    sel = np.linspace(0, B - 1, 16).astype(np.int64)
+    rep = check_round(oracle, inp, toks.cpu().numpy(), 0, 0, rows=sel)
+    print("workload5 full:", rep)
+    assert rep.rows == 16 and rep.exact_rows + rep.flagged_rows == 16
+    assert rep.excused_mismatches <= 1
+
+
 @pytest.mark.parametrize("V,dtype,top_p,stride_pad", [
     (1, torch.bfloat16, None, 0),
     (5, torch.float32, 0.5, 0),
