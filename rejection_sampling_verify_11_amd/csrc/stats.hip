@@ -300,12 +300,6 @@ constexpr uint32_t kFallback = 1u << 30;  // internal: the table cannot hold the
 __device__ __forceinline__ int pos_bin(int b) { return kZeroBin + 2 + b; }
 __device__ __forceinline__ int neg_bin(int b) { return kZeroBin - 2 - b; }
 
-// Counts logit k of a 16-byte group known to lie in the window.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t k) {
-  const uint32_t word = (k & 0x7FFFu) - kBase;
-  const uint32_t inc = 1u << ((k >> 11) & 16u);
-  __hip_atomic_fetch_add(hist + word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 // Window test of both logits of a 32-bit word as arithmetic (no branches):
 // the exponent bits less the window's first, unsigned, so that exponents
 // below the window wrap high.  The word lies in the window iff the larger of
@@ -347,11 +341,40 @@ __device__ __forceinline__ void count_slow(uint32_t* hist, uint32_t* tiny, uint3
   }
 }
 
-__device__ __forceinline__ void count_group_fast(uint32_t* hist, const uint4& d) {
-  hist_add(hist, d.x & 0xFFFFu); hist_add(hist, d.x >> 16);
-  hist_add(hist, d.y & 0xFFFFu); hist_add(hist, d.y >> 16);
-  hist_add(hist, d.z & 0xFFFFu); hist_add(hist, d.z >> 16);
-  hist_add(hist, d.w & 0xFFFFu); hist_add(hist, d.w >> 16);
+// Counts both logits of a 32-bit word, known to lie in the window.  hbase
+// is the table shifted down by the window's first word, so a logit's word
+// is hbase + magnitude; the increment is 1 for a +value, 0x10000 for a
+// -value (4 VALU instructions per logit).
+__device__ __forceinline__ void count_word_fast(uint32_t* hbase, uint32_t w) {
+  const uint32_t mlo = w & 0x7FFFu, mhi = __builtin_amdgcn_ubfe(w, 16, 15);
+  const uint32_t slo = __builtin_amdgcn_ubfe(w, 15, 1), shi = w >> 31;
+  __hip_atomic_fetch_add(hbase + mlo, slo * 0xFFFFu + 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_add(hbase + mhi, shi * 0xFFFFu + 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void count_group_fast(uint32_t* hbase, const uint4& d) {
+  count_word_fast(hbase, d.x);
+  count_word_fast(hbase, d.y);
+  count_word_fast(hbase, d.z);
+  count_word_fast(hbase, d.w);
+}
+
+// Window test of a batch with packed 16-bit arithmetic: per half, the
+// exponent bits less the window's first, wrapping below it; the batch lies
+// in the window iff the largest of them is below kWords.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t batch_excess(const uint4 (&a)[kBatch]) {
+  const u16x2 base = {(unsigned short)kBase, (unsigned short)kBase};
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    const uint32_t w[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[t] & 0x7F807F80u) - base);
+  }
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // Counts logit k, known to lie in the window, when `valid`; otherwise adds
@@ -420,6 +443,7 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
                                               uint32_t* tiny, Side& sd) {
   const int tid = threadIdx.x;
   const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
+  uint32_t* hbase = hist - kBase;
   int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
   if (head > V) head = V;
   const uint4* body = (const uint4*)(vec + head);
@@ -439,14 +463,10 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
     for (int k = 0; k < nfull; ++k) {
       uint4 n[kBatch];
       load_batch(n, body, (k + 1 < nfull || part) ? i + step : i, nb);
-      uint32_t ex = 0;
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q)
-        ex = max(ex, max(max(window_excess(a[q].x), window_excess(a[q].y)),
-                         max(window_excess(a[q].z), window_excess(a[q].w))));
+      const uint32_t ex = batch_excess(a);
       if (!__any(ex >= (uint32_t)kWords)) {
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) count_group_fast(hist, a[q]);
+        for (int q = 0; q < kBatch; ++q) count_group_fast(hbase, a[q]);
       } else {
         sd = count_batch_slow(hist, tiny, a[0], a[1], a[2], a[3], 0xFu, spare, sd);
       }
