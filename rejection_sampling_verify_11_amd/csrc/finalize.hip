@@ -9,13 +9,17 @@
 //   ([SD] §2.2).
 //
 // The draw is an inverse CDF in token-index order: y = min{j : C_j > u R},
-// C the inclusive prefix of r, R its total.  The vector is read in tiles of
-// 1024 x 8 contiguous logits (one 16-byte load per thread for bf16); each
-// wave owns a segment of 512 consecutive tokens per tile.  Pass 1 sums r per
-// segment (fp64); a scan over segments finds the one holding u R; pass 2
-// re-derives that segment's 512 values, scans them across lanes and picks
-// the token.  Probabilities are exp2 of fp32 arguments (v_exp_f32) scaled by
-// fp64 normalisers; all sums are fp64.
+// C the inclusive prefix of r, R its total.  Pass 1 sums r per segment of
+// consecutive tokens; a scan over the segments finds the one holding u R;
+// pass 2 re-derives that segment's values token by token in fp64, scans
+// them across lanes and picks the token.  bf16 vectors that are 16-byte
+// aligned with V a multiple of 8 are read in groups of 16384 tokens, one
+// 1024-token segment per wave, with the next group's loads in flight; under
+// a top-p cut on p' pass 1 works on the listed tokens at or above tau_p
+// only.  Other vectors (fp32, unaligned, ragged V) are read in tiles of
+// 1024 x 8 logits with 512-token segments.  Probabilities are exp2 of fp32
+// arguments (v_exp_f32) times the 1/G normalisers; segment and prefix sums
+// are fp64.
 #include <math.h>
 
 #include "philox.h"
