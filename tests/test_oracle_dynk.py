@@ -72,3 +72,22 @@ def test_ring_sums_match_the_slots_over_a_long_run():
         assert np.array_equal(st[:, 3], (slots >> 16).sum(axis=1))
         assert np.all((k >= 2) & (k <= 8))
         assert np.all(st[:, 0] <= W) and np.all((st[:, 1] >= 0) & (st[:, 1] < W))
+
+
+def test_k_too_large_for_a_slot_is_not_a_draft_length():
+    # a slot stores proposed k in 15 bits; a larger k leaves the row alone
+    k = np.array([40000, 5], np.int32)
+    st = svref.dynk_state(2, 4)
+    for _ in range(6):
+        svref.dynamic_k(np.array([3, 5], np.int32), k, st, window=4)
+    assert k[0] == 40000 and np.all(st[0] == 0)
+    assert k[1] == 8 and st[1, 0] == 4
+
+
+def test_empty_batch_and_argument_checks():
+    k = np.zeros(0, np.int32)
+    st = svref.dynk_state(0, 4)
+    svref.dynamic_k(np.zeros(0, np.int32), k, st, window=4)
+    with pytest.raises(ValueError):
+        svref.dynamic_k(np.zeros(1, np.int32), np.ones(1, np.int32), svref.dynk_state(1, 4),
+                        window=4, k_min=5, k_max=4)
