@@ -11,12 +11,13 @@ contexts of 4096..8192 tokens, so that hundreds of steps can each shorten
 every sequence by up to k without running out of context).  Two input batches (2 GB together) alternate
 so that no step finds its logits in the 256 MB last-level cache.
 
-Beside the headline step, two more legs are timed and reported as extra
-keys: greedy verification at B=64, k=8, V=128256 (target logits only), and
-the on-device round at B=512, V=128256 with per-row temperatures and k from
-the dynamic controller (verification, page-table rollback, controller update
+Beside the headline step, more legs are timed and reported as extra keys:
+greedy verification at B=64, k=8, V=128256 (target logits only); the
+on-device round at B=512, V=128256 with per-row temperatures and k from the
+dynamic controller (verification, page-table rollback, controller update
 and round-counter advance), replayed as a HIP graph and, for comparison,
-launched eagerly.
+launched eagerly; and, on the bench batch, the draft-side sampler and
+verification with top-p on the target only.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -123,6 +124,40 @@ def greedy_leg(dev, n):
             "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "verified_positions_per_s": B * K / (ms * 1e-3),
             "mean_accepted": call.outputs["accepted"].float().mean().item()}
+
+
+def variant_legs(dev, sets, n):
+    """The bench batch through the two variants the verification step has:
+    the draft-side sampler (temperature, top-p, inverse CDF over all k
+    positions of every row, draw 2) and verification with top-p on the
+    target only.  Per-call times by HIP events."""
+    import torch
+    import rejection_sampling_verify_11_amd as sv
+    inp, toks, _ = sets[0]
+    B, K, V = inp.draft.shape
+    draft = sv.VerifyCall("draft", None, inp.draft, None, inp.temperature, inp.top_p, None,
+                          seed=0, offset=0)
+    tonly = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
+                          None, seed=0, offset=0, flags=sv.FLAG_TOPP_TARGET_ONLY)
+    out = {}
+    for name, call, nbytes in (("draft_sample", draft, B * K * V * 2),
+                               ("verify_topp_target_only", tonly, B * (2 * K + 1) * V * 2)):
+        for _ in range(20):
+            call.run()
+        ms = timed(call.run, n, dev)
+        sv.timing_enable(dev, True)
+        for _ in range(20):
+            call.run()
+        torch.cuda.synchronize()
+        kt = sv.timing_read(dev)
+        sv.timing_enable(dev, False)
+        assert int((call.outputs["row_status"] != 0).sum()) == 0
+        out[name] = {"ms_per_call": ms, "input_gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "kernels_ms": {k: v[1] / v[0] for k, v in kt.items()}}
+    out["draft_sample"]["drafted_tokens_per_s"] = B * K / (out["draft_sample"]["ms_per_call"] * 1e-3)
+    out["verify_topp_target_only"]["verified_positions_per_s"] = \
+        B * K / (out["verify_topp_target_only"]["ms_per_call"] * 1e-3)
+    return out
 
 
 def round_leg(dev, n):
@@ -312,6 +347,7 @@ def main():
     if not args.no_extra:
         result["greedy"] = greedy_leg(dev, args.steps)
         result["round"] = round_leg(dev, args.steps)
+        result.update(variant_legs(dev, sets, min(args.steps, 50)))
 
     if not args.no_cpu_baseline:
         from oracle import svref

@@ -251,7 +251,8 @@ sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
   if (sv::launch_stats(stats_params(a, 0), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
-  if (sv::launch_finalize_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_finalize_sample(finalize_params(a), h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
   return SV_OK;
 }
 
@@ -261,7 +262,8 @@ sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
   if (sv::launch_stats(stats_params(a, 1), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
-  if (sv::launch_draft_sample(finalize_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_draft_sample(finalize_params(a), h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
   return SV_OK;
 }
 

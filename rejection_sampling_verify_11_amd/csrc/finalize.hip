@@ -29,9 +29,10 @@
 namespace sv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kTile = kThreads * 8;   // logits per tile
+// Workgroups have NT = 1024 or 512 threads (a template parameter): 1024 when
+// the launch has about one workgroup per CU, 512 when it has two or more
+// per CU, so that two fit a CU (registers and LDS) and one's serial steps
+// (row header, scan, located segment) overlap the other's streaming.
 constexpr int kSeg = 512;             // logits per (tile, wave) segment
 constexpr int kMaxSeg = 4096;         // V <= 2^21 on this path
 
@@ -105,12 +106,13 @@ __device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int d
 constexpr int kCpsFast = 2;
 constexpr int kSegTokFast = 512 * kCpsFast;
 
+template <int NT>
 struct CdfScratch {
   double seg[kMaxSeg];
   // bf16 path with a top-p cut: each wave's list of the tokens of its
   // segment that can carry mass, plus one spare slot per lane
-  uint32_t list[kWaves][kSegTokFast + 64];
-  double wsum[kWaves];
+  uint32_t list[NT / 64][kSegTokFast + 64];
+  double wsum[NT / 64];
   double R;
   int sstar;
   int y;
@@ -128,13 +130,13 @@ __device__ __forceinline__ bool is_aligned16(const void* p) {
 }
 
 // ---- bf16 fast path: 16-byte aligned vectors with V a multiple of 8.
-// Groups of kGroupTok tokens; in group G wave w owns the kSegTok contiguous
-// tokens G kGroupTok + kSegTok w + [0, kSegTok) (one segment), lane l the
+// Groups of (NT / 64) kSegTok tokens; in group G wave w owns the kSegTok
+// contiguous tokens G (NT / 64) kSegTok + kSegTok w + [0, kSegTok) (one
+// segment), lane l the
 // 8-token chunks at 512 s + 8 l (s < kCps), so every wave load is 1 KB
 // contiguous.  Pass 1 loads group G + 1 while it sums group G.
 constexpr int kCps = kCpsFast;             // chunks per lane per segment
 constexpr int kSegTok = kSegTokFast;
-constexpr int kGroupTok = kWaves * kSegTok;
 
 // MODE 0: residual max(0, p' - q'); MODE 1: p' alone.
 template <int MODE>
@@ -271,8 +273,9 @@ __device__ __forceinline__ void pass1_segment(const Dist& P, const Dist& Q, cons
 
 // One inverse-CDF draw with this layout: returns y, -1 if R is 0 (the
 // caller then retries on p' alone, for MODE 0) or the distribution is empty.
-template <int MODE, int PASS>
-__device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch& sc) {
+template <int MODE, int PASS, int NT>
+__device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch<NT>& sc) {
+  constexpr int kWaves = NT / 64, kGroupTok = kWaves * kSegTok;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
   const uint16_t* Qv = (const uint16_t*)Q.vec;
@@ -367,23 +370,25 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
 // mode 0: residual of (P, Q), falling back to P if it is identically zero;
 // mode 1: P alone.  Returns y (same value in every thread), or -1 if the
 // distribution is empty.  *zero_residual reports the fallback.
+template <int NT>
 __device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
-                           CdfScratch& sc, bool* zero_residual) {
+                           CdfScratch<NT>& sc, bool* zero_residual) {
+  constexpr int kThreads = NT, kWaves = NT / 64, kTile = NT * 8;
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
       (mode == 1 || is_aligned16(Q.vec))) {
     *zero_residual = false;
     // the same in every thread
     const bool cutp = P.tau > -INFINITY, cutq = Q.tau > -INFINITY;
     if (mode == 0) {
-      const int y = cutp ? inverse_cdf_bf16<0, kPassListed>(P, Q, V, u, sc)
-                  : cutq ? inverse_cdf_bf16<0, kPassCutQ>(P, Q, V, u, sc)
-                         : inverse_cdf_bf16<0, kPassUncut>(P, Q, V, u, sc);
+      const int y = cutp ? inverse_cdf_bf16<0, kPassListed, NT>(P, Q, V, u, sc)
+                  : cutq ? inverse_cdf_bf16<0, kPassCutQ, NT>(P, Q, V, u, sc)
+                         : inverse_cdf_bf16<0, kPassUncut, NT>(P, Q, V, u, sc);
       if (y >= 0) return y;
       // R == 0: the residual vanishes identically; draw from p' instead
       *zero_residual = true;
     }
-    return cutp ? inverse_cdf_bf16<1, kPassListed>(P, P, V, u, sc)
-                : inverse_cdf_bf16<1, kPassUncut>(P, P, V, u, sc);
+    return cutp ? inverse_cdf_bf16<1, kPassListed, NT>(P, P, V, u, sc)
+                : inverse_cdf_bf16<1, kPassUncut, NT>(P, P, V, u, sc);
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = (V + kTile - 1) / kTile;
@@ -521,8 +526,9 @@ struct RowShared {
   double u1;
 };
 
-__global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParams p) {
-  __shared__ CdfScratch sc;
+template <int NT>
+__global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
+  __shared__ CdfScratch<NT> sc;
   __shared__ RowShared rs;
   const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
   const int per = slots_per_row(K);
@@ -608,8 +614,9 @@ __global__ __launch_bounds__(kThreads) void finalize_sample_kernel(FinalizeParam
 }
 
 // Draft sampling: one workgroup per (row, draft position).
-__global__ __launch_bounds__(kThreads) void draft_sample_kernel(FinalizeParams p) {
-  __shared__ CdfScratch sc;
+template <int NT>
+__global__ __launch_bounds__(NT) void draft_sample_kernel(FinalizeParams p) {
+  __shared__ CdfScratch<NT> sc;
   __shared__ int go;
   __shared__ float Ts;
   const int b = blockIdx.x / p.K, i = blockIdx.x % p.K, K = p.K, tid = threadIdx.x;
@@ -642,17 +649,30 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(FinalizeParams p
 
 }  // namespace
 
-hipError_t launch_finalize_sample(const FinalizeParams& p, hipStream_t s, Timer* t) {
+// 512-thread workgroups when there are at least two per CU.
+static bool use_half_blocks(unsigned nblocks, int num_cus) {
+  const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
+  return nblocks >= 2u * cus;
+}
+
+hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t) {
   if (p.B == 0) return hipSuccess;
   TimedScope ts(t, "finalize_sample", s);
-  hipLaunchKernelGGL(finalize_sample_kernel, dim3(p.B), dim3(kThreads), 0, s, p);
+  if (use_half_blocks((unsigned)p.B, num_cus))
+    hipLaunchKernelGGL(finalize_sample_kernel<512>, dim3(p.B), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(finalize_sample_kernel<1024>, dim3(p.B), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_draft_sample(const FinalizeParams& p, hipStream_t s, Timer* t) {
+hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t) {
   if (p.B == 0) return hipSuccess;
   TimedScope ts(t, "draft_sample", s);
-  hipLaunchKernelGGL(draft_sample_kernel, dim3((unsigned)p.B * (unsigned)p.K), dim3(kThreads), 0, s, p);
+  const unsigned n = (unsigned)p.B * (unsigned)p.K;
+  if (use_half_blocks(n, num_cus))
+    hipLaunchKernelGGL(draft_sample_kernel<512>, dim3(n), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(draft_sample_kernel<1024>, dim3(n), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 

@@ -161,8 +161,8 @@ struct TimedScope {
 
 // Launchers (each returns hipGetLastError() of its launch(es)).
 hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_t s, Timer* t);
-hipError_t launch_finalize_sample(const FinalizeParams& p, hipStream_t s, Timer* t);
-hipError_t launch_draft_sample(const FinalizeParams& p, hipStream_t s, Timer* t);
+hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
+hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
 hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t);
