@@ -526,9 +526,19 @@ __device__ __forceinline__ int take_ticket(const StatsParams& p, int q) {
 // Without a list, items run position-major: the bonus position of every
 // row, then target and draft position K-1 of every row, ..., position 0
 // last.  Vectors streamed side by side then belong to different rows, which
-// measured ~3 % faster than the slot order (rows' vectors adjacent).
-__device__ __forceinline__ int item_slot(const StatsParams& p, int item) {
-  if (p.slot_list) return p.slot_list[item];
+// measured ~3 % faster than the slot order (rows' vectors adjacent).  A
+// list (in row order) is visited as item * stride mod n with a stride
+// coprime to n, for the same effect.
+__device__ __forceinline__ uint32_t list_stride(uint32_t n) {
+  const uint32_t primes[4] = {1009u, 1013u, 1019u, 1021u};
+  uint32_t s = 1u;
+#pragma unroll
+  for (int i = 3; i >= 0; --i) s = n % primes[i] ? primes[i] : s;
+  return s;
+}
+
+__device__ __forceinline__ int item_slot(const StatsParams& p, int item, uint32_t n, uint32_t stride) {
+  if (p.slot_list) return p.slot_list[(uint32_t)(((uint64_t)item * stride) % n)];
   const int B = p.B, K = p.K, per = slots_per_row(K);
   if (item < B) return item * per + K;
   const int i = item - B, q = i / (2 * B), r = i - q * 2 * B;
@@ -686,7 +696,8 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   // the first item; a workgroup without one has none later either
   const int queue = (int)(blockIdx.x % kQueues);
   if (queue_item(queue, blockIdx.x / kQueues) >= nitems) return;
-  int v = item_slot(p, queue_item(queue, blockIdx.x / kQueues));
+  const uint32_t stride = list_stride((uint32_t)nitems);
+  int v = item_slot(p, queue_item(queue, blockIdx.x / kQueues), (uint32_t)nitems, stride);
   for (int i = tid; i < kCopies * kCopyWords; i += kT) hist[i] = 0;
   if (tid == 0) tiny[0] = 0u;
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
@@ -713,7 +724,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     __syncthreads();  // B1: table complete
     const int in = sh.next;
     const bool has_next = in < nitems;
-    const int vn = has_next ? item_slot(p, in) : v;
+    const int vn = has_next ? item_slot(p, in, (uint32_t)nitems, stride) : v;
     const SlotP nxt = slot_params(p, vn);  // loads in flight meanwhile
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
