@@ -233,3 +233,33 @@ def test_rollback_full_size_pool_poison(oracle):
         for pos in range(o_len[b], lens[b]):
             page = pt0[b, pos // ps]
             assert bool((pool16[page, :, :, :, pos % ps, :] == -1).all())
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_greedy_random_configuration_sweep(oracle, case):
+    """Seeded random greedy shapes: V from 1 to 70000 (chunk tails of every
+    kind), bf16 and fp32, padded strides, draft tokens or draft logits,
+    per-row k, values rounded so that ties are common; bit-exact."""
+    rng = np.random.default_rng(3000 + case)
+    B, K = int(rng.integers(1, 20)), int(rng.integers(1, 10))
+    V = int(rng.choice([1, 3, 8, 9, 100, 16383, 16384, 16385, 40000, 70000]))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    pad = int(rng.choice([0, 0, 1, 5, 8]))
+    g = torch.Generator().manual_seed(4000 + case)
+    base_t = ((torch.randn((B, K + 1, V + pad), generator=g) * 3).round() / 2).to(dtype)
+    use_draft = rng.random() < 0.5
+    base_d = ((torch.randn((B, K, V + pad), generator=g) * 3).round() / 2).to(dtype)
+    toks = torch.from_numpy(rng.integers(0, V, (B, K)).astype(np.int32))
+    top = torch.argmax(base_t[:, :K, :V].float(), dim=2).to(torch.int32)
+    toks = torch.where(torch.from_numpy(rng.random((B, K)) < 0.7), top, toks)
+    kk = None if rng.random() < 0.5 else torch.from_numpy(rng.integers(1, K + 1, B).astype(np.int32))
+    d_t = base_t.to(DEV)[:, :, :V]
+    d_d = base_d.to(DEV)[:, :, :V] if use_draft else None
+    gg = sv.verify_greedy(d_t, None if use_draft else toks.to(DEV), d_d,
+                          None if kk is None else kk.to(DEV))
+    torch.cuda.synchronize()
+    og = oracle.verify_greedy(W.host_logits(base_t[:, :, :V].contiguous()),
+                              draft=W.host_logits(base_d[:, :, :V].contiguous()) if use_draft else None,
+                              draft_tokens=None if use_draft else toks.numpy(),
+                              k_per_row=None if kk is None else kk.numpy(), nthreads=8)
+    compare_exact(gg, og, GREEDY_KEYS)

@@ -398,3 +398,55 @@ def test_draft_sampler_parity(oracle):
         gt = g_toks.cpu().numpy()
         flagged = (cdf < 1e-6) | (topp < 1e-6)
         assert np.array_equal(gt[~flagged], o_toks[~flagged])
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_configuration_sweep(oracle, case):
+    """Seeded random shapes around the edges of the layouts: V from 1 to
+    70000 (tails of every length, several 16384-token groups), bf16 and fp32,
+    padded strides, per-row k and temperature, top-p off / on / target only,
+    random seeds and round counters.  Verification and the draft sampler
+    against the oracle on the same inputs."""
+    rng = np.random.default_rng(1000 + case)
+    B = int(rng.integers(1, 24))
+    K = int(rng.integers(1, 10))
+    V = int(rng.choice([1, 2, 7, 8, 9, 1000, 4097, 16384, 16385, 40000, 70000]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    pad = int(rng.choice([0, 0, 1, 3, 8]))
+    g = torch.Generator().manual_seed(2000 + case)
+    scale = float(rng.choice([0.5, 2.0, 4.0]))
+    base_t = (torch.randn((B, K + 1, V + pad), generator=g) * scale).to(dtype)
+    base_d = (base_t[:, :K].float() + torch.randn((B, K, V + pad), generator=g)
+              * float(rng.uniform(0.2, 1.5))).to(dtype)
+    T = torch.from_numpy(rng.uniform(0.2, 2.0, B).astype(np.float32))
+    mode = int(rng.integers(0, 3))          # 0 off, 1 both sides, 2 target only
+    P = None if mode == 0 else torch.from_numpy(rng.uniform(0.5, 1.0, B).astype(np.float32))
+    flags = sv.FLAG_TOPP_TARGET_ONLY if mode == 2 else 0
+    kk = None if rng.random() < 0.5 else torch.from_numpy(rng.integers(1, K + 1, B).astype(np.int32))
+    seed, offset = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**40))
+    host = W.SampleInputs(base_t[:, :, :V].contiguous(), base_d[:, :, :V].contiguous(), T, P, kk)
+    # the device keeps the padded strides
+    d_t = base_t.to(DEV)[:, :, :V]
+    d_d = base_d.to(DEV)[:, :, :V]
+    d_T, d_P = T.to(DEV), None if P is None else P.to(DEV)
+    d_k = None if kk is None else kk.to(DEV)
+    # draft sampling on both sides
+    o_toks, o_st, cdf, topp = oracle.draft_sample(
+        W.host_logits(host.draft), T.numpy(), None if P is None else P.numpy(),
+        None if kk is None else kk.numpy(), seed=seed, offset=offset, flags=flags, nthreads=NT,
+        diagnostics=True)
+    g_toks, g_st = sv.draft_sample(d_d, d_T, d_P, d_k, seed=seed, offset=offset, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_st.cpu().numpy(), o_st)
+    gt = g_toks.cpu().numpy()
+    flagged = (cdf < 1e-6) | (topp < 1e-6)
+    assert np.array_equal(gt[~flagged], o_toks[~flagged])
+    # verification of the oracle's draft tokens
+    out = sv.verify_sample(d_t, d_d, torch.from_numpy(o_toks).to(DEV), d_T, d_P, d_k, seed=seed,
+                           offset=offset, flags=flags)
+    torch.cuda.synchronize()
+    o = oracle_verify(oracle, host, o_toks, seed, offset, flags)
+    rep = compare_sample(out, o, kk, K)
+    print("sweep case", case, (B, K, V, str(dtype), pad, mode, kk is not None), rep)
+    assert rep.exact_rows + rep.flagged_rows + rep.error_rows == rep.rows
+    assert rep.excused_mismatches <= 1
