@@ -13,10 +13,14 @@
 // consecutive tokens; a scan over the segments finds the one holding u R;
 // pass 2 re-derives that segment's values token by token in fp64, scans
 // them across lanes and picks the token.  bf16 vectors that are 16-byte
-// aligned with V a multiple of 8 are read in groups of 16384 tokens, one
-// 1024-token segment per wave, with the next group's loads in flight; under
-// a top-p cut on p' pass 1 works on the listed tokens at or above tau_p
-// only.  Other vectors (fp32, unaligned, ragged V) are read in tiles of
+// aligned with V a multiple of 8 are read in groups of (NT / 64) x 1024
+// tokens, one 1024-token segment per wave, with the next group's loads in
+// flight; under a top-p cut on p' pass 1 works on the listed tokens at or
+// above tau_p only.  On this path a draw from p' alone (the bonus, the
+// zero-residual fallback, the draft sampler's q') knows R = 1 before it
+// starts, so pass 1 stops after the group in which the running sum passes
+// u -- about half the vector on average -- and the wave holding that
+// segment locates the token from its registers.  Other vectors (fp32, unaligned, ragged V) are read in tiles of
 // 1024 x 8 logits with 512-token segments.  Probabilities are exp2 of fp32
 // arguments (v_exp_f32) times the 1/G normalisers; segment and prefix sums
 // are fp64.
@@ -271,10 +275,78 @@ __device__ __forceinline__ void pass1_segment(const Dist& P, const Dist& Q, cons
   else segment_sum_uncut<MODE, PASS == kPassCutQ>(P, Q, c, seg, nchunks, segs);
 }
 
+// Pass 2 by one wave over the segment `seg` held in c: its tokens in order
+// (s, then lane, then t) in fp64, `before` the mass of every token ahead of
+// the segment.  Returns the first token whose inclusive prefix exceeds
+// `target`, else (a rounding edge) the last token with mass, -1 if none has
+// any.  The result is the same in every lane.
+template <int MODE>
+__device__ __forceinline__ int locate_in_segment(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
+                                                 int seg, int nchunks, double before, double target) {
+  const int l = threadIdx.x & 63;
+  double running = before;
+  int hit = 0x7FFFFFFF, lastpos = -1;
+#pragma unroll
+  for (int s = 0; s < kCps; ++s) {
+    const int ci = seg * (kSegTok / 8) + l + 64 * s;
+    double r[8];
+    chunk_r<MODE>(P, Q, c, s, ci < nchunks, r);
+    double ls = 0.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ls += r[t];
+    const double incl = wave_scan_add_f64(ls);
+    double cum = running + (incl - ls);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      cum += r[t];
+      if (r[t] > 0.0) {
+        lastpos = 8 * ci + t;
+        if (hit == 0x7FFFFFFF && cum > target) hit = 8 * ci + t;
+      }
+    }
+    running += wave_last_f64(incl);
+  }
+  hit = (int)wave_last_u32(wave_scan_u32<OpMinI32>((uint32_t)hit));
+  lastpos = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)lastpos));
+  return hit != 0x7FFFFFFF ? hit : lastpos;
+}
+
+// The early stop of a draw from a normalised distribution (MODE 1: p' alone,
+// whose mass is 1 by construction, so the crossing point u is known before
+// any token is read).  Called by every thread once the kWaves segment sums
+// of a group are in `seg`: adds them to `cum` in token order and returns the
+// wave whose segment holds the first prefix above `target` (-1 if the group
+// ends at or below it), with the mass before that segment in `before`.
+// Every thread reads the same values and adds them in the same order, so
+// all take the same decision.
+template <int kWaves>
+__device__ __forceinline__ int group_crossing(const double* seg, double target, double& cum,
+                                              double& before) {
+  int hw = -1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const double nx = cum + seg[w];
+    if (hw < 0 && nx > cum && nx > target) {
+      hw = w;
+      before = cum;
+    }
+    cum = nx;
+  }
+  return hw;
+}
+
 // One inverse-CDF draw with this layout: returns y, -1 if R is 0 (the
 // caller then retries on p' alone, for MODE 0) or the distribution is empty.
+//
+// MODE 0 reads the whole vector: R, the residual's mass, is known only at
+// the end.  MODE 1 stops after the group in which the running mass passes
+// u (R = 1 up to rounding); the wave that holds the crossing segment in its
+// registers locates the token without reading it again.  At a rounding edge
+// (the running mass never passes u) it falls back to the scan over all
+// segment sums with R their total, as MODE 0 does.
 template <int MODE, int PASS, int NT>
-__device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, CdfScratch<NT>& sc) {
+__device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u,
+                                              CdfScratch<NT>& sc) {
   constexpr int kWaves = NT / 64, kGroupTok = kWaves * kSegTok;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
@@ -287,13 +359,43 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
   {
     Chunks<MODE> ca, cb;
     uint32_t* list = sc.list[w];
+    double cum = 0.0, before = 0.0;
+    int hw = -1;
     load_segment<MODE>(ca, Pv, Qv, w, nchunks);
     for (int G = 0; G < ngroups; G += 2) {
       load_segment<MODE>(cb, Pv, Qv, min(G + 1, ngroups - 1) * kWaves + w, nchunks);
       pass1_segment<MODE, PASS>(P, Q, ca, G * kWaves + w, nchunks, sc.seg, list);
+      if (MODE == 1) {
+        __syncthreads();
+        hw = group_crossing<kWaves>(sc.seg + G * kWaves, u, cum, before);
+        if (hw >= 0) {
+          if (w == hw) {
+            const int y = locate_in_segment<MODE>(P, Q, ca, G * kWaves + w, nchunks, before, u);
+            if (l == 0) sc.y = y;
+          }
+          break;
+        }
+      }
       if (G + 1 >= ngroups) break;
       load_segment<MODE>(ca, Pv, Qv, min(G + 2, ngroups - 1) * kWaves + w, nchunks);
       pass1_segment<MODE, PASS>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg, list);
+      if (MODE == 1) {
+        __syncthreads();
+        hw = group_crossing<kWaves>(sc.seg + (G + 1) * kWaves, u, cum, before);
+        if (hw >= 0) {
+          if (w == hw) {
+            const int y = locate_in_segment<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, before, u);
+            if (l == 0) sc.y = y;
+          }
+          break;
+        }
+      }
+    }
+    if (hw >= 0) {  // the same in every thread
+      __syncthreads();
+      const int y = sc.y;
+      __syncthreads();  // sc is reused by the next call
+      return y;
     }
   }
   __syncthreads();
@@ -318,7 +420,7 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
   const double target = u * R;
   // the segment holding the crossing: the last segment whose exclusive prefix
   // is <= target and whose mass is positive (or, at a rounding edge, the last
-  // segment with mass); then its tokens in order (s, then lane, then t)
+  // segment with mass); then its tokens in order
   if (w == 0) {
     int best = -1, lastm = -1;
     for (int s0 = 0; s0 < nseg; s0 += 64) {
@@ -334,31 +436,8 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
     const int ss = best >= 0 ? best : lastm >= 0 ? lastm : 0;
     Chunks<MODE> c;
     load_segment<MODE>(c, Pv, Qv, ss, nchunks);
-    double running = sc.seg[ss];
-    int hit = 0x7FFFFFFF, lastpos = -1;
-#pragma unroll
-    for (int s = 0; s < kCps; ++s) {
-      const int ci = ss * (kSegTok / 8) + l + 64 * s;
-      double r[8];
-      chunk_r<MODE>(P, Q, c, s, ci < nchunks, r);
-      double ls = 0.0;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) ls += r[t];
-      const double incl = wave_scan_add_f64(ls);
-      double cum = running + (incl - ls);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        cum += r[t];
-        if (r[t] > 0.0) {
-          lastpos = 8 * ci + t;
-          if (hit == 0x7FFFFFFF && cum > target) hit = 8 * ci + t;
-        }
-      }
-      running += wave_last_f64(incl);
-    }
-    hit = (int)wave_last_u32(wave_scan_u32<OpMinI32>((uint32_t)hit));
-    lastpos = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)lastpos));
-    if (l == 0) sc.y = hit != 0x7FFFFFFF ? hit : lastpos;
+    const int y = locate_in_segment<MODE>(P, Q, c, ss, nchunks, sc.seg[ss], target);
+    if (l == 0) sc.y = y;
   }
   __syncthreads();
   const int y = sc.y;
@@ -371,7 +450,7 @@ __device__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u, C
 // mode 1: P alone.  Returns y (same value in every thread), or -1 if the
 // distribution is empty.  *zero_residual reports the fallback.
 template <int NT>
-__device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
+__device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
                            CdfScratch<NT>& sc, bool* zero_residual) {
   constexpr int kThreads = NT, kWaves = NT / 64, kTile = NT * 8;
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
@@ -507,16 +586,34 @@ __device__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, in
   return -1;
 }
 
-__device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, int dtype,
-                          const VecRec& rec, float T) {
+__device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, int dtype, float m,
+                          float tau, double inv_kept, float T) {
   Dist d;
   d.vec = (const char*)base + vec_index * stride * (dtype == SV_BF16 ? 2 : 4);
-  d.m = rec.m;
-  d.tau = rec.tau;
+  d.m = m;
+  d.tau = tau;
   d.c2 = log2e_over_T(T);
-  d.inv = rec.inv_kept;
-  d.invf = (float)rec.inv_kept;
+  d.inv = inv_kept;
+  d.invf = (float)inv_kept;
   return d;
+}
+
+// The fields of a record the kernels use, loaded field by field (a whole
+// VecRec copied under a lane condition stays a private array).
+struct RecFields {
+  float m, tau;
+  double inv_kept, px;
+  uint32_t status;
+};
+
+__device__ __forceinline__ RecFields load_rec(const VecRec* r, bool valid) {
+  RecFields f;
+  f.m = valid ? r->m : 0.0f;
+  f.tau = valid ? r->tau : 0.0f;
+  f.inv_kept = valid ? r->inv_kept : 0.0;
+  f.px = valid ? r->px : 0.0;
+  f.status = valid ? r->status : 0u;
+  return f;
 }
 
 struct RowShared {
@@ -524,6 +621,8 @@ struct RowShared {
   uint32_t status;
   float T;
   double u1;
+  float pm, ptau, qm, qtau;  // records of the drawn position (target, draft)
+  double pinv, qinv;
 };
 
 template <int NT>
@@ -534,27 +633,35 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
   const int per = slots_per_row(K);
   const VecRec* recs = p.recs + (int64_t)b * per;
   // Row header by wave 0, one lane per position: checks, ratios, uniforms;
-  // the first rejection is the lowest lane that rejects.
+  // the first rejection is the lowest lane that rejects.  Every load is
+  // issued up front -- lane l reads the draft token and the target and draft
+  // records of position l whatever k_b is, and k_b masks them afterwards --
+  // so the header waits for memory once.  The lane keeps its token for the
+  // output row.
+  int x = 0;
   if (tid < 64) {
     const int l = tid;
-    uint32_t st = 0;
     const int kb = p.k_per_row ? p.k_per_row[b] : K;
-    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
     const float T = p.temperature[b];
-    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
     const float P = p.top_p ? p.top_p[b] : 1.0f;
+    const uint64_t off = round_offset(p);
+    if (l < K) x = p.tokens[(int64_t)b * K + l];
+    const RecFields rt = load_rec(recs + min(l, K), l <= K);
+    const RecFields rd = load_rec(recs + K + 1 + min(l, K - 1), l < K);
+    uint32_t st = 0;
+    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
+    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
     if (isnan(P) || P <= 0.0f) st |= SV_ROW_BAD_TOP_P;
     double px = 0.0, qx = 0.0;
     uint32_t lst = 0;
     if (!(st & SV_ROW_BAD_K)) {
       if (l < kb) {
-        const int x = p.tokens[(int64_t)b * K + l];
         if (x < 0 || x >= V) lst |= SV_ROW_BAD_TOKEN;
-        px = recs[l].px;
-        qx = recs[K + 1 + l].px;
-        lst |= recs[l].status | recs[K + 1 + l].status;
+        px = rt.px;
+        qx = rd.px;
+        lst |= rt.status | rd.status;
       } else if (l == kb) {
-        lst |= recs[kb].status;
+        lst |= rt.status;
       }
     }
     st |= wave_last_u32(wave_scan_u32<OpOrU32>(lst));
@@ -563,7 +670,7 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       bool rej = false;
       if (l < kb) {
         const double rho = qx > 0.0 ? px / qx : 0.0;
-        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)l, 0, round_offset(p));
+        const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)l, 0, off);
         rej = !(u < rho);
       }
       const uint64_t rm = __ballot(rej);
@@ -571,6 +678,15 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       if (l < K) {
         if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + l] = l < kb ? (float)px : 0.0f;
         if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + l] = l < kb ? (float)qx : 0.0f;
+      }
+      // lane acc (<= k_b <= K) holds the drawn position's records
+      if (l == acc) {
+        rs.pm = rt.m;
+        rs.ptau = rt.tau;
+        rs.pinv = rt.inv_kept;
+        rs.qm = rd.m;
+        rs.qtau = rd.tau;
+        rs.qinv = rd.inv_kept;
       }
     } else {
       if (l <= K) p.out_tokens[(int64_t)b * (K + 1) + l] = -1;
@@ -591,59 +707,80 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       rs.status = st;
       rs.T = T;
       rs.mode = acc < kb ? 0 : 1;
-      rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, round_offset(p));
+      rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, off);
     }
   }
   __syncthreads();
   if (!rs.go) return;
   const int acc = rs.acc, mode = rs.mode;
-  const Dist P = make_dist(p.target, (int64_t)b * (K + 1) + acc, p.t_stride, p.dtype, recs[acc], rs.T);
+  const Dist P = make_dist(p.target, (int64_t)b * (K + 1) + acc, p.t_stride, p.dtype, rs.pm,
+                           rs.ptau, rs.pinv, rs.T);
   Dist Q = P;
-  if (mode == 0) Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, recs[K + 1 + acc], rs.T);
+  if (mode == 0)
+    Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, rs.qm, rs.qtau, rs.qinv, rs.T);
   bool zero = false;
   const int y = inverse_cdf(P, Q, mode, p.dtype, V, rs.u1, sc, &zero);
-  if (tid == 0) {
-    int32_t* out = p.out_tokens + (int64_t)b * (K + 1);
-    for (int j = 0; j <= K; ++j) out[j] = -1;
-    for (int i = 0; i < acc; ++i) out[i] = p.tokens[(int64_t)b * K + i];
-    out[acc] = y;
-    p.accepted[b] = acc;
-    if (p.num_emitted) p.num_emitted[b] = acc + 1;
-    if (p.row_status) p.row_status[b] = 0;
+  if (tid < 64) {
+    const int l = tid;
+    if (l <= K) {
+      const int32_t v = l < acc ? x : l == acc ? y : -1;
+      p.out_tokens[(int64_t)b * (K + 1) + l] = v;
+    }
+    if (l == 0) {
+      p.accepted[b] = acc;
+      if (p.num_emitted) p.num_emitted[b] = acc + 1;
+      if (p.row_status) p.row_status[b] = 0;
+    }
   }
 }
 
-// Draft sampling: one workgroup per (row, draft position).
+// Draft sampling: one workgroup per (row, draft position).  The header
+// issues every load at once, as the verification header does: k_b, T,
+// top-p, the round counter and the status words of all K draft records
+// (masked by k_b afterwards), and this position's record.
 template <int NT>
 __global__ __launch_bounds__(NT) void draft_sample_kernel(FinalizeParams p) {
   __shared__ CdfScratch<NT> sc;
   __shared__ int go;
   __shared__ float Ts;
+  __shared__ double us;
+  __shared__ float qm, qtau;
+  __shared__ double qinv;
   const int b = blockIdx.x / p.K, i = blockIdx.x % p.K, K = p.K, tid = threadIdx.x;
   const int per = slots_per_row(K);
   const VecRec* recs = p.recs + (int64_t)b * per;
-  if (tid == 0) {
-    uint32_t st = 0;
+  if (tid < 64) {
+    const int l = tid;
     const int kb = p.k_per_row ? p.k_per_row[b] : K;
-    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
     const float T = p.temperature[b];
-    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
     const float P = p.top_p ? p.top_p[b] : 1.0f;
+    const uint64_t off = round_offset(p);
+    const RecFields rd = load_rec(recs + K + 1 + min(l, K - 1), l < K);
+    uint32_t st = 0;
+    if (kb < 1 || kb > K) st |= SV_ROW_BAD_K;
+    if (!(T > 0.0f) || !isfinite(T)) st |= SV_ROW_BAD_TEMPERATURE;
     if (isnan(P) || P <= 0.0f) st |= SV_ROW_BAD_TOP_P;
-    if (!(st & SV_ROW_BAD_K))
-      for (int j = 0; j < kb; ++j) st |= recs[K + 1 + j].status;
-    // every workgroup of the row sees the same status; position 0 reports it
-    if (i == 0 && p.row_status) p.row_status[b] = (int32_t)st;
-    go = (st == 0 && i < kb) ? 1 : 0;
-    if (!go) p.draft_out[(int64_t)b * K + i] = -1;
-    Ts = T;
+    const uint32_t lst = !(st & SV_ROW_BAD_K) && l < kb ? rd.status : 0u;
+    st |= wave_last_u32(wave_scan_u32<OpOrU32>(lst));
+    if (l == i) {
+      qm = rd.m;
+      qtau = rd.tau;
+      qinv = rd.inv_kept;
+    }
+    if (l == 0) {
+      // every workgroup of the row sees the same status; position 0 reports it
+      if (i == 0 && p.row_status) p.row_status[b] = (int32_t)st;
+      go = (st == 0 && i < kb) ? 1 : 0;
+      if (!go) p.draft_out[(int64_t)b * K + i] = -1;
+      Ts = T;
+      us = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 2, off);
+    }
   }
   __syncthreads();
   if (!go) return;
-  const Dist Q = make_dist(p.draft, (int64_t)b * K + i, p.d_stride, p.dtype, recs[K + 1 + i], Ts);
+  const Dist Q = make_dist(p.draft, (int64_t)b * K + i, p.d_stride, p.dtype, qm, qtau, qinv, Ts);
   bool zero = false;
-  const double u = uniform24(p.seed, (uint64_t)b, (uint64_t)i, 2, round_offset(p));
-  const int y = inverse_cdf(Q, Q, 1, p.dtype, p.V, u, sc, &zero);
+  const int y = inverse_cdf(Q, Q, 1, p.dtype, p.V, us, sc, &zero);
   if (tid == 0) p.draft_out[(int64_t)b * K + i] = y;
 }
 
