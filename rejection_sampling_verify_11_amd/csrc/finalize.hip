@@ -13,10 +13,10 @@
 // consecutive tokens; a scan over the segments finds the one holding u R;
 // pass 2 re-derives that segment's values token by token in fp64, scans
 // them across lanes and picks the token.  bf16 vectors that are 16-byte
-// aligned with V a multiple of 8 are read in groups of (NT / 64) x 1024
-// tokens, one 1024-token segment per wave, with the next group's loads in
-// flight; under a top-p cut on p' pass 1 works on the listed tokens at or
-// above tau_p only.  On this path a draw from p' alone (the bonus, the
+// aligned with V a multiple of 8 are read in groups of NT / 64 segments,
+// one per wave (1024 tokens of both vectors for the residual, 2048 for p'
+// alone), with the next group's loads in flight; under a top-p cut on p'
+// pass 1 works on the listed tokens at or above tau_p only.  On this path a draw from p' alone (the bonus, the
 // zero-residual fallback, the draft sampler's q') knows R = 1 before it
 // starts, so pass 1 stops after the group in which the running sum passes
 // u -- about half the vector on average -- and the wave holding that
@@ -106,16 +106,16 @@ __device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int d
   }
 }
 
-// Tokens per wave segment of the bf16 path (defined with that path below).
-constexpr int kCpsFast = 2;
-constexpr int kSegTokFast = 512 * kCpsFast;
+// Capacity of a wave's token list on the bf16 path: two 8-token chunks per
+// lane (the path is defined below).
+constexpr int kListTok = 2 * 512;
 
 template <int NT>
 struct CdfScratch {
   double seg[kMaxSeg];
   // bf16 path with a top-p cut: each wave's list of the tokens of its
   // segment that can carry mass, plus one spare slot per lane
-  uint32_t list[NT / 64][kSegTokFast + 64];
+  uint32_t list[NT / 64][kListTok + 64];
   double wsum[NT / 64];
   double R;
   int sstar;
@@ -134,19 +134,24 @@ __device__ __forceinline__ bool is_aligned16(const void* p) {
 }
 
 // ---- bf16 fast path: 16-byte aligned vectors with V a multiple of 8.
-// Groups of (NT / 64) kSegTok tokens; in group G wave w owns the kSegTok
-// contiguous tokens G (NT / 64) kSegTok + kSegTok w + [0, kSegTok) (one
-// segment), lane l the
-// 8-token chunks at 512 s + 8 l (s < kCps), so every wave load is 1 KB
-// contiguous.  Pass 1 loads group G + 1 while it sums group G.
-constexpr int kCps = kCpsFast;             // chunks per lane per segment
-constexpr int kSegTok = kSegTokFast;
+// Groups of (NT / 64) segments of Seg<MODE>::tok tokens; in group G wave w
+// owns segment G (NT / 64) + w, the tok contiguous tokens from
+// (G (NT / 64) + w) tok, and lane l the 8-token chunks at 512 s + 8 l of it
+// (s < Seg<MODE>::cps), so every wave load is 1 KB contiguous.  Pass 1 loads
+// group G + 1 while it sums group G.  The residual (MODE 0) reads two
+// vectors and takes two chunks per lane; p' alone (MODE 1) takes four, so
+// that a wave has as many bytes in flight either way.
+template <int MODE>
+struct Seg {
+  static constexpr int cps = MODE == 1 ? 4 : 2;  // chunks per lane per segment
+  static constexpr int tok = 512 * cps;          // tokens per segment
+};
 
 // MODE 0: residual max(0, p' - q'); MODE 1: p' alone.
 template <int MODE>
 struct Chunks {
-  uint4 p[kCps];
-  uint4 q[MODE == 0 ? kCps : 1];
+  uint4 p[Seg<MODE>::cps];
+  uint4 q[MODE == 0 ? Seg<MODE>::cps : 1];
 };
 
 // Loads the chunks of this lane in segment `seg` (chunk indices past the last
@@ -155,9 +160,9 @@ template <int MODE>
 __device__ __forceinline__ void load_segment(Chunks<MODE>& c, const uint16_t* P, const uint16_t* Q,
                                              int seg, int nchunks) {
   const int l = threadIdx.x & 63;
-  const int c0 = seg * (kSegTok / 8) + l;
+  const int c0 = seg * (Seg<MODE>::tok / 8) + l;
 #pragma unroll
-  for (int s = 0; s < kCps; ++s) {
+  for (int s = 0; s < Seg<MODE>::cps; ++s) {
     const int ci = min(c0 + 64 * s, nchunks - 1);
     c.p[s] = *(const uint4*)(P + 8 * (int64_t)ci);
     if (MODE == 0) c.q[s] = *(const uint4*)(Q + 8 * (int64_t)ci);
@@ -183,26 +188,26 @@ __device__ __forceinline__ void chunk_r(const Dist& Pd, const Dist& Qd, const Ch
 }
 
 // Pass 1 of one segment: the sum of r over the chunks of this lane, summed
-// over the wave and stored as the segment's mass.  This version is for p'
-// without a top-p cut (tau_p = -inf, so no test on the p side), with a cut
-// on q' only when CQ.  A lane sums its 16 tokens in fp32
+// over the wave and stored as the segment's mass.  Every token's p' (and q')
+// is formed; the tau test on the p side is taken only when CP (p' has a
+// top-p cut), on the q side only when CQ.  A lane sums its tokens in fp32
 // before the fp64 wave sum: the token probabilities are fp32 values anyway,
 // and the located segment is re-derived token by token in fp64.
-template <int MODE, bool CQ>
-__device__ __forceinline__ void segment_sum_uncut(const Dist& P, const Dist& Q,
+template <int MODE, bool CP, bool CQ>
+__device__ __forceinline__ void segment_sum_direct(const Dist& P, const Dist& Q,
                                                   const Chunks<MODE>& c, int seg, int nchunks,
                                                   double* segs) {
   const int l = threadIdx.x & 63;
   float lf = 0.0f;
 #pragma unroll
-  for (int s = 0; s < kCps; ++s) {
-    const bool valid = seg * (kSegTok / 8) + l + 64 * s < nchunks;
+  for (int s = 0; s < Seg<MODE>::cps; ++s) {
+    const bool valid = seg * (Seg<MODE>::tok / 8) + l + 64 * s < nchunks;
     const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
     float cs = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float zp = __uint_as_float(t & 1 ? (pw[t >> 1] & 0xFFFF0000u) : (pw[t >> 1] << 16));
-      float v = __builtin_amdgcn_exp2f((zp - P.m) * P.c2) * P.invf;
+      float v = CP ? prob_f(P, zp) : __builtin_amdgcn_exp2f((zp - P.m) * P.c2) * P.invf;
       if (MODE == 0) {
         const uint32_t qw = t < 2 ? c.q[s].x : t < 4 ? c.q[s].y : t < 6 ? c.q[s].z : c.q[s].w;
         const float zq = __uint_as_float(t & 1 ? (qw & 0xFFFF0000u) : (qw << 16));
@@ -219,60 +224,67 @@ __device__ __forceinline__ void segment_sum_uncut(const Dist& P, const Dist& Q,
 
 // The same sum when p' has a top-p cut.  r is zero at every token below
 // tau_p (p' is zero there, so is max(0, p' - q')), and with a cut that is
-// most tokens.  The wave first lists the tokens at or above tau_p in LDS --
-// the raw p bits in the low half of an entry, q's in the high half -- by a
-// ballot and a lane prefix count (branch-free: a lane with nothing to list
-// writes its spare slot), then forms r on the list only.  The sum is over the
-// same fp32 values as segment_sum's, in another order.
+// most tokens.  Two chunks at a time, the wave first lists the tokens at or
+// above tau_p in LDS -- the raw p bits in the low half of an entry, q's in
+// the high half -- by a ballot and a lane prefix count (branch-free: a lane
+// with nothing to list writes its spare slot), then forms r on the list
+// only.  The sum is over the same fp32 values as segment_sum's, in another
+// order.
 template <int MODE>
 __device__ __forceinline__ void segment_sum_listed(const Dist& P, const Dist& Q,
                                                    const Chunks<MODE>& c, int seg, int nchunks,
                                                    double* segs, uint32_t* list) {
+  static_assert(Seg<MODE>::cps % 2 == 0 && 2 * 512 == kListTok, "two chunks fill the list");
   const int l = threadIdx.x & 63;
-  uint32_t n = 0;  // list length (wave-uniform)
-#pragma unroll
-  for (int s = 0; s < kCps; ++s) {
-    const bool valid = seg * (kSegTok / 8) + l + 64 * s < nchunks;
-    const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
-    uint32_t qw[4] = {0u, 0u, 0u, 0u};
-    if (MODE == 0) {
-      qw[0] = c.q[s].x; qw[1] = c.q[s].y; qw[2] = c.q[s].z; qw[3] = c.q[s].w;
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t word = pw[t >> 1];
-      const uint32_t hi = t & 1 ? word & 0xFFFF0000u : word << 16;  // p as fp32 bits
-      const bool keep = valid && __uint_as_float(hi) >= P.tau;
-      const uint64_t m = __ballot(keep);
-      const uint32_t pre =
-          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      uint32_t e = hi >> 16;
-      if (MODE == 0) e |= t & 1 ? qw[t >> 1] & 0xFFFF0000u : qw[t >> 1] << 16;
-      list[keep ? n + pre : (uint32_t)(kSegTok + l)] = e;
-      n += (uint32_t)__builtin_popcountll(m);
-    }
-  }
   double ls = 0.0;
-  for (uint32_t i0 = 0; i0 < n; i0 += 64) {
-    const uint32_t i = i0 + (uint32_t)l;
-    const uint32_t e = list[i < n ? i : 0u];
-    float v = prob_f(P, __uint_as_float(e << 16));
-    if (MODE == 0) v = fmaxf(v - prob_f(Q, __uint_as_float(e & 0xFFFF0000u)), 0.0f);
-    ls += i < n ? (double)v : 0.0;
+#pragma unroll
+  for (int h = 0; h < Seg<MODE>::cps; h += 2) {
+    uint32_t n = 0;  // list length (wave-uniform)
+#pragma unroll
+    for (int s = h; s < h + 2; ++s) {
+      const bool valid = seg * (Seg<MODE>::tok / 8) + l + 64 * s < nchunks;
+      const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
+      uint32_t qw[4] = {0u, 0u, 0u, 0u};
+      if (MODE == 0) {
+        qw[0] = c.q[s].x; qw[1] = c.q[s].y; qw[2] = c.q[s].z; qw[3] = c.q[s].w;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t word = pw[t >> 1];
+        const uint32_t hi = t & 1 ? word & 0xFFFF0000u : word << 16;  // p as fp32 bits
+        const bool keep = valid && __uint_as_float(hi) >= P.tau;
+        const uint64_t m = __ballot(keep);
+        const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        uint32_t e = hi >> 16;
+        if (MODE == 0) e |= t & 1 ? qw[t >> 1] & 0xFFFF0000u : qw[t >> 1] << 16;
+        list[keep ? n + pre : (uint32_t)(kListTok + l)] = e;
+        n += (uint32_t)__builtin_popcountll(m);
+      }
+    }
+    for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+      const uint32_t i = i0 + (uint32_t)l;
+      const uint32_t e = list[i < n ? i : 0u];
+      float v = prob_f(P, __uint_as_float(e << 16));
+      if (MODE == 0) v = fmaxf(v - prob_f(Q, __uint_as_float(e & 0xFFFF0000u)), 0.0f);
+      ls += i < n ? (double)v : 0.0;
+    }
   }
   ls = wave_last_f64(wave_scan_add_f64(ls));
   if (l == 0) segs[seg] = ls;
 }
 
-// Pass-1 variants: 0 listed tokens (p' has a top-p cut), 1 no cut on either
-// side, 2 a cut on q' only.
-enum { kPassListed = 0, kPassUncut = 1, kPassCutQ = 2 };
+// Pass-1 variants: 0 listed tokens (the residual when p' has a top-p cut:
+// most tokens then carry no mass, and listing spares their two exp2s),
+// 1 no cut on either side, 2 a cut on q' only, 3 p' alone with a cut (one
+// exp2 per token costs less than listing).
+enum { kPassListed = 0, kPassUncut = 1, kPassCutQ = 2, kPassCutP = 3 };
 
 template <int MODE, int PASS>
 __device__ __forceinline__ void pass1_segment(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
                                               int seg, int nchunks, double* segs, uint32_t* list) {
   if (PASS == kPassListed) segment_sum_listed<MODE>(P, Q, c, seg, nchunks, segs, list);
-  else segment_sum_uncut<MODE, PASS == kPassCutQ>(P, Q, c, seg, nchunks, segs);
+  else segment_sum_direct<MODE, PASS == kPassCutP, PASS == kPassCutQ>(P, Q, c, seg, nchunks, segs);
 }
 
 // Pass 2 by one wave over the segment `seg` held in c: its tokens in order
@@ -287,8 +299,8 @@ __device__ __forceinline__ int locate_in_segment(const Dist& P, const Dist& Q, c
   double running = before;
   int hit = 0x7FFFFFFF, lastpos = -1;
 #pragma unroll
-  for (int s = 0; s < kCps; ++s) {
-    const int ci = seg * (kSegTok / 8) + l + 64 * s;
+  for (int s = 0; s < Seg<MODE>::cps; ++s) {
+    const int ci = seg * (Seg<MODE>::tok / 8) + l + 64 * s;
     double r[8];
     chunk_r<MODE>(P, Q, c, s, ci < nchunks, r);
     double ls = 0.0;
@@ -347,7 +359,7 @@ __device__ __forceinline__ int group_crossing(const double* seg, double target, 
 template <int MODE, int PASS, int NT>
 __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u,
                                               CdfScratch<NT>& sc) {
-  constexpr int kWaves = NT / 64, kGroupTok = kWaves * kSegTok;
+  constexpr int kWaves = NT / 64, kGroupTok = kWaves * Seg<MODE>::tok;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
   const uint16_t* Qv = (const uint16_t*)Q.vec;
@@ -360,7 +372,7 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
     Chunks<MODE> ca, cb;
     uint32_t* list = sc.list[w];
     double cum = 0.0, before = 0.0;
-    int hw = -1;
+    int hw = -1, gx = 0;  // MODE 1: the crossing's wave and group
     load_segment<MODE>(ca, Pv, Qv, w, nchunks);
     for (int G = 0; G < ngroups; G += 2) {
       load_segment<MODE>(cb, Pv, Qv, min(G + 1, ngroups - 1) * kWaves + w, nchunks);
@@ -368,13 +380,8 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
       if (MODE == 1) {
         __syncthreads();
         hw = group_crossing<kWaves>(sc.seg + G * kWaves, u, cum, before);
-        if (hw >= 0) {
-          if (w == hw) {
-            const int y = locate_in_segment<MODE>(P, Q, ca, G * kWaves + w, nchunks, before, u);
-            if (l == 0) sc.y = y;
-          }
-          break;
-        }
+        gx = G;
+        if (hw >= 0) break;
       }
       if (G + 1 >= ngroups) break;
       load_segment<MODE>(ca, Pv, Qv, min(G + 2, ngroups - 1) * kWaves + w, nchunks);
@@ -382,16 +389,20 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
       if (MODE == 1) {
         __syncthreads();
         hw = group_crossing<kWaves>(sc.seg + (G + 1) * kWaves, u, cum, before);
-        if (hw >= 0) {
-          if (w == hw) {
-            const int y = locate_in_segment<MODE>(P, Q, cb, (G + 1) * kWaves + w, nchunks, before, u);
-            if (l == 0) sc.y = y;
-          }
-          break;
-        }
+        gx = G + 1;
+        if (hw >= 0) break;
       }
     }
-    if (hw >= 0) {  // the same in every thread
+    if (MODE == 1 && hw >= 0) {  // the same in every thread
+      if (w == hw) {
+        // the crossing group's chunks are in ca (even group) or cb (odd)
+        Chunks<MODE> c;
+        const bool odd = (gx & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < Seg<MODE>::cps; ++i) c.p[i] = odd ? cb.p[i] : ca.p[i];
+        const int y = locate_in_segment<MODE>(P, Q, c, gx * kWaves + w, nchunks, before, u);
+        if (l == 0) sc.y = y;
+      }
       __syncthreads();
       const int y = sc.y;
       __syncthreads();  // sc is reused by the next call
@@ -466,7 +477,7 @@ __device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mod
       // R == 0: the residual vanishes identically; draw from p' instead
       *zero_residual = true;
     }
-    return cutp ? inverse_cdf_bf16<1, kPassListed, NT>(P, P, V, u, sc)
+    return cutp ? inverse_cdf_bf16<1, kPassCutP, NT>(P, P, V, u, sc)
                 : inverse_cdf_bf16<1, kPassUncut, NT>(P, P, V, u, sc);
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
