@@ -450,3 +450,48 @@ def test_random_configuration_sweep(oracle, case):
     print("sweep case", case, (B, K, V, str(dtype), pad, mode, kk is not None), rep)
     assert rep.exact_rows + rep.flagged_rows + rep.error_rows == rep.rows
     assert rep.excused_mismatches <= 1
+
+
+# token positions around the segment (2048) and group (16384 / 32768) edges
+# of the p'-only draws, the two ends and the middle
+HOT = [0, 1, 7, 8, 2047, 2048, 16383, 16384, 32767, 32768, 75967, 151928, 151935]
+
+
+def _hot_logits(n, V, positions, cold=-200.0, hot=20.0):
+    z = torch.full((n, V), cold)
+    z[torch.arange(n), torch.as_tensor(positions)] = hot
+    return z
+
+
+@pytest.mark.parametrize("B", [8, 256])
+def test_pprime_draws_find_a_single_hot_token(oracle, B):
+    """Draws from p' alone (the draft sampler and the bonus position) on
+    vectors whose mass sits on one token: the draw is that token whatever u
+    is, wherever the token lies relative to the early stop's segments and
+    groups.  B=8 runs 1024-thread workgroups, B=256 512-thread ones.  The
+    oracle agrees on every row."""
+    K, V = 2, 151936
+    n = B * K
+    pos = [HOT[i % len(HOT)] for i in range(n)]
+    draft = _hot_logits(n, V, pos).view(B, K, V).to(torch.bfloat16)
+    T = torch.ones(B)
+    P = torch.where(torch.arange(B) % 2 == 0, torch.tensor(0.9), torch.tensor(1.0))
+    g_toks, g_st = sv.draft_sample(draft.to(DEV), T.to(DEV), P.to(DEV), seed=5, offset=1)
+    torch.cuda.synchronize()
+    expect = np.asarray(pos, np.int32).reshape(B, K)
+    assert np.array_equal(g_toks.cpu().numpy(), expect)
+    assert not g_st.any()
+    rows = list(range(min(B, 16)))
+    o_toks, _ = oracle.draft_sample(W.host_logits(draft[rows]), T[rows].numpy(), P[rows].numpy(),
+                                    seed=5, offset=1, nthreads=NT)
+    assert np.array_equal(o_toks, expect[rows])
+    # the bonus: drafts equal to the target, so every draft is accepted and
+    # the last position's single hot token is emitted
+    bonus = [HOT[(3 * i + 1) % len(HOT)] for i in range(B)]
+    target = torch.cat([draft, _hot_logits(B, V, bonus).view(B, 1, V).to(torch.bfloat16)], dim=1)
+    inp = W.SampleInputs(target, draft, T, P)
+    out = gpu_verify(inp, expect, 6, 2)
+    assert torch.all(out["accepted"] == K)
+    assert np.array_equal(out["out_tokens"].cpu().numpy()[:, K], np.asarray(bonus))
+    o = oracle_verify(oracle, inp, expect, 6, 2, rows=rows)
+    assert np.array_equal(o["out_tokens"][:, K], np.asarray(bonus)[rows])
