@@ -16,8 +16,9 @@ greedy verification at B=64, k=8, V=128256 (target logits only); the
 on-device round at B=512, V=128256 with per-row temperatures and k from the
 dynamic controller (verification, page-table rollback, controller update
 and round-counter advance), replayed as a HIP graph and, for comparison,
-launched eagerly; and, on the bench batch, the draft-side sampler and
-verification with top-p on the target only.
+launched eagerly; and, on the bench batch, the draft-side sampler,
+verification with top-p on the target only, and the statistics split over
+8 vocabulary shards (one shard's pass, the merge, the chain on one GPU).
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -158,6 +159,50 @@ def variant_legs(dev, sets, n):
     out["verify_topp_target_only"]["verified_positions_per_s"] = \
         B * K / (out["verify_topp_target_only"]["ms_per_call"] * 1e-3)
     return out
+
+
+def sharded_leg(dev, sets, n):
+    """Vocabulary-sharded statistics on the bench batch, as 8 GPUs holding
+    18992 columns each would run them: one GPU's share is the pass over its
+    shard (sv_shard_stats, 1/8 of the logit bytes), then the merge of the
+    8 partials (sv_shard_combine) and the finalize on the merged records.
+    The shard passes are timed in turn over all 8 shards, so that no pass
+    finds its shard in the last-level cache; the whole chain (8 passes,
+    merge, finalize) runs here on one GPU and is timed as well."""
+    import torch
+    import rejection_sampling_verify_11_amd as sv
+    inp, toks, _ = sets[0]
+    B, K, V = inp.draft.shape
+    G = 8
+    sc = sv.ShardedCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p, None,
+                        G, seed=0, offset=0)
+    for _ in range(10):
+        sc.run()
+    torch.cuda.synchronize()
+    i = [0]
+
+    def one_shard():
+        sc.run_shard(i[0] % G)
+        i[0] += 1
+
+    shard_ms = timed(one_shard, max(n, 2 * G), dev)
+    chain_ms = timed(sc.run, n, dev)
+    sv.timing_enable(dev, True)
+    for _ in range(10):
+        sc.run()
+    torch.cuda.synchronize()
+    kt = sv.timing_read(dev)
+    sv.timing_enable(dev, False)
+    assert int((sc.outputs["row_status"] != 0).sum()) == 0
+    kms = {k: v[1] / v[0] for k, v in kt.items()}
+    cols = sc.bounds[0][1]
+    shard_bytes = B * (2 * K + 1) * cols * 2
+    return {"workload": "B=256 k=6 V=151936 bf16 top-p 0.9 in 8 vocabulary shards of %d columns"
+                        % cols,
+            "shard_pass_ms": shard_ms,
+            "shard_stats_gbs": shard_bytes / (kms["shard_stats"] * 1e-3) / 1e9,
+            "one_gpu_chain_ms": chain_ms,
+            "kernels_ms": kms}
 
 
 def round_leg(dev, n):
@@ -348,6 +393,7 @@ def main():
         result["greedy"] = greedy_leg(dev, args.steps)
         result["round"] = round_leg(dev, args.steps)
         result.update(variant_legs(dev, sets, min(args.steps, 50)))
+        result["vocab_sharded"] = sharded_leg(dev, sets, min(args.steps, 50))
 
     if not args.no_cpu_baseline:
         from oracle import svref

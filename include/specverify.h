@@ -81,6 +81,13 @@ typedef enum { SV_FP32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_FLAG_TOPP_TARGET_ONLY (1u << 0) /* truncate p only, keep q whole
                                               ([SSD] §3.4, the author's
                                               preferred variant)              */
+#define SV_FLAG_RECORDS_READY    (1u << 1) /* sv_verify_sample and
+                                              sv_draft_sample: the workspace
+                                              already holds this call's
+                                              per-vector statistics (written
+                                              by sv_shard_combine with the same
+                                              sizes, slots, temperature, top-p
+                                              and flags); skip their pass     */
 
 /* Poison pattern written into rolled-back KV slots when a pool is given. */
 #define SV_POISON_BF16 0xFFFFu
@@ -278,6 +285,97 @@ sv_status sv_dynamic_k(sv_handle h, const sv_dynk_args* a, hipStream_t s);
  * any host work.  Wraps modulo 2^64.  SV_E_ARG if offset_dev is NULL or not
  * 8-byte aligned. */
 sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, hipStream_t s);
+
+/* ------------------------------------------------------------------------ */
+/* Vocabulary-sharded statistics                                            */
+/* ------------------------------------------------------------------------ */
+
+/* When a tensor-parallel LM head leaves each of G GPUs with a contiguous
+ * slice of the vocabulary, every per-vector statistic of the verification
+ * (the largest logit, the softmax normaliser, the tie-closed top-p
+ * threshold, p'(x) and q'(x); [SSD] §2.4 and §3.4) still needs all V
+ * logits.  The work splits in two: each shard counts its own columns
+ * (sv_shard_stats, the streaming pass over 1/G of the bytes), and the
+ * partials -- exact value counts, so merging them loses nothing -- are
+ * gathered and merged into the records of the whole vectors
+ * (sv_shard_combine).  On one GPU the gather is the caller handing every
+ * shard's partial buffer to sv_shard_combine.  bf16 logits only.  The
+ * records then drive sv_verify_sample or sv_draft_sample with
+ * SV_FLAG_RECORDS_READY. */
+#define SV_MAX_SHARDS 16
+
+/* One shard's pass.  Layout: the shard's target vector (b, i), i in
+ * [0, k_max], starts at element (b*(k_max+1) + i) * target_vec_stride of
+ * target_shard and holds columns [col_offset, col_offset + col_count) of the
+ * full vector (bf16, contiguous); draft vector (b, i) at
+ * (b*k_max + i) * draft_vec_stride of draft_shard.  Strides are in elements,
+ * >= col_count.  The slots counted are those of sv_verify_sample (mode 0:
+ * target positions 0..k_b, draft positions 0..k_b-1) or of sv_draft_sample
+ * (mode 1: draft positions only; target_shard and draft_tokens unused). */
+typedef struct {
+  int32_t B, k_max, V;              /* V: the full vocabulary                 */
+  int32_t col_offset, col_count;    /* this shard's columns, inside [0, V)    */
+  int32_t mode;                     /* 0 verification, 1 draft sampling       */
+  const void* target_shard;
+  int64_t target_vec_stride;
+  const void* draft_shard;
+  int64_t draft_vec_stride;
+  const int32_t* draft_tokens;      /* [B][k_max] ids in [0, V); mode 0       */
+  const int32_t* k_per_row;         /* [B] or NULL -> k_max                   */
+  void* partial;                    /* out: this shard's partials, at least
+                                       sv_shard_partial_bytes                 */
+  size_t partial_bytes;
+  void* workspace;                  /* scratch (work queues, slot list), at
+                                       least sv_shard_workspace_bytes         */
+  size_t workspace_bytes;
+} sv_shard_stats_args;
+
+/* Sizes of a shard's partial buffer and of its scratch.  Pure host. */
+size_t sv_shard_partial_bytes(int32_t B, int32_t k_max, int32_t col_count);
+size_t sv_shard_workspace_bytes(int32_t B, int32_t k_max);
+sv_status sv_check_shard_stats_args(const sv_shard_stats_args* a);
+
+/* Counts the shard's logits of every used vector slot into its partial:
+ * the count of each bf16 value in the window of magnitudes [2^-24, 2^16),
+ * the zeros and -infs, up to 64 nonzero values below the window, NaN / +inf
+ * and whether the shard holds a value the counts cannot (a finite magnitude
+ * of 2^16 or more, more than 64 values below the window, or 65536 equal
+ * values), and the logit of the slot's draft token when it is one of the
+ * shard's columns. */
+sv_status sv_shard_stats(sv_handle h, const sv_shard_stats_args* a, hipStream_t s);
+
+/* The merge.  Shards g = 0..G-1 must tile [0, V) in order:
+ * col_offset[0] = 0, col_offset[g+1] = col_offset[g] + col_count[g],
+ * and the last ends at V.  partials[g] is shard g's partial buffer from
+ * sv_shard_stats with the same B, k_max, V, mode, draft_tokens and
+ * k_per_row.  target_shards / draft_shards (with their strides) are shard
+ * g's logits, as passed to sv_shard_stats: they are read only for a vector
+ * whose merged counts the table cannot hold, which is then redone from the
+ * logits (the generic path of sv_verify_sample).  The records are written
+ * into `workspace`, a verification workspace (sv_verify_workspace_bytes
+ * for B, k_max, V), exactly as the statistics pass of sv_verify_sample
+ * (mode 0) or sv_draft_sample (mode 1) would write them for the
+ * concatenated vectors: pass that workspace, with SV_FLAG_RECORDS_READY set,
+ * to that entry point. */
+typedef struct {
+  int32_t B, k_max, V, mode, G;
+  const void* partials[SV_MAX_SHARDS];
+  int32_t col_offset[SV_MAX_SHARDS], col_count[SV_MAX_SHARDS];
+  const void* target_shards[SV_MAX_SHARDS];
+  int64_t target_vec_stride[SV_MAX_SHARDS];
+  const void* draft_shards[SV_MAX_SHARDS];
+  int64_t draft_vec_stride[SV_MAX_SHARDS];
+  const int32_t* draft_tokens;      /* [B][k_max]; mode 0                      */
+  const int32_t* k_per_row;         /* [B] or NULL                             */
+  const float* temperature;         /* [B]                                     */
+  const float* top_p;               /* [B] or NULL                             */
+  uint32_t flags;                   /* SV_FLAG_TOPP_TARGET_ONLY                */
+  void* workspace;                  /* out: records (a verification workspace) */
+  size_t workspace_bytes;
+} sv_shard_combine_args;
+
+sv_status sv_check_shard_combine_args(const sv_shard_combine_args* a);
+sv_status sv_shard_combine(sv_handle h, const sv_shard_combine_args* a, hipStream_t s);
 
 #ifdef __cplusplus
 }

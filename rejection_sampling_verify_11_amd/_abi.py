@@ -20,6 +20,8 @@ SV_MAX_K = 32
 SV_MAX_V = 1 << 30
 SV_MAX_V_SAMPLED = 1 << 21
 FLAG_TOPP_TARGET_ONLY = 1 << 0
+FLAG_RECORDS_READY = 1 << 1
+MAX_SHARDS = 16
 POISON_BF16 = 0xFFFF
 
 ROW_NONFINITE_LOGIT = 1 << 0
@@ -71,11 +73,39 @@ class DynkArgs(C.Structure):
     ]
 
 
+class ShardStatsArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("k_max", C.c_int32), ("V", C.c_int32),
+        ("col_offset", C.c_int32), ("col_count", C.c_int32), ("mode", C.c_int32),
+        ("target_shard", _P), ("target_vec_stride", C.c_int64),
+        ("draft_shard", _P), ("draft_vec_stride", C.c_int64),
+        ("draft_tokens", _P), ("k_per_row", _P),
+        ("partial", _P), ("partial_bytes", C.c_size_t),
+        ("workspace", _P), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class ShardCombineArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("k_max", C.c_int32), ("V", C.c_int32), ("mode", C.c_int32),
+        ("G", C.c_int32),
+        ("partials", _P * MAX_SHARDS),
+        ("col_offset", C.c_int32 * MAX_SHARDS), ("col_count", C.c_int32 * MAX_SHARDS),
+        ("target_shards", _P * MAX_SHARDS), ("target_vec_stride", C.c_int64 * MAX_SHARDS),
+        ("draft_shards", _P * MAX_SHARDS), ("draft_vec_stride", C.c_int64 * MAX_SHARDS),
+        ("draft_tokens", _P), ("k_per_row", _P), ("temperature", _P), ("top_p", _P),
+        ("flags", C.c_uint32),
+        ("workspace", _P), ("workspace_bytes", C.c_size_t),
+    ]
+
+
 EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
-           "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset")
+           "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset",
+           "sv_shard_partial_bytes", "sv_shard_workspace_bytes", "sv_check_shard_stats_args",
+           "sv_shard_stats", "sv_check_shard_combine_args", "sv_shard_combine")
 
 _lib = None
 _lock = threading.Lock()
@@ -122,6 +152,18 @@ def library():
                 L.sv_dynamic_k.restype = C.c_int
                 L.sv_advance_offset.argtypes = [_P, _P, C.c_uint64, _P]
                 L.sv_advance_offset.restype = C.c_int
+                L.sv_shard_partial_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+                L.sv_shard_partial_bytes.restype = C.c_size_t
+                L.sv_shard_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+                L.sv_shard_workspace_bytes.restype = C.c_size_t
+                L.sv_check_shard_stats_args.argtypes = [C.POINTER(ShardStatsArgs)]
+                L.sv_check_shard_stats_args.restype = C.c_int
+                L.sv_shard_stats.argtypes = [_P, C.POINTER(ShardStatsArgs), _P]
+                L.sv_shard_stats.restype = C.c_int
+                L.sv_check_shard_combine_args.argtypes = [C.POINTER(ShardCombineArgs)]
+                L.sv_check_shard_combine_args.restype = C.c_int
+                L.sv_shard_combine.argtypes = [_P, C.POINTER(ShardCombineArgs), _P]
+                L.sv_shard_combine.restype = C.c_int
                 _lib = L
     return _lib
 
@@ -425,3 +467,112 @@ def dynamic_k(accepted, k_per_row, state, window=64, k_min=2, k_max=8, up=(17, 2
     if rc != SV_OK:
         raise SpecVerifyError("sv_dynamic_k", rc)
     return k_per_row
+
+
+def shard_bounds(V, shards):
+    """Column ranges of `shards` contiguous shards tiling [0, V), as even as
+    possible and, where V allows, on multiples of 8 (16-byte rows)."""
+    if shards < 1 or shards > MAX_SHARDS or shards > V:
+        raise ValueError("shards must be in [1, min(%d, V)]" % MAX_SHARDS)
+    unit = 8 if V >= 8 * shards else 1
+    cuts = [min(V, (V // unit * g // shards) * unit) for g in range(shards)] + [V]
+    return [(cuts[g], cuts[g + 1] - cuts[g]) for g in range(shards)]
+
+
+class ShardedCall:
+    """Sampled verification ("sample") or draft sampling ("draft") with the
+    per-vector statistics taken over `shards` contiguous vocabulary shards:
+    one sv_shard_stats per shard (its columns only), sv_shard_combine over
+    all partials, then sv_verify_sample / sv_draft_sample with
+    FLAG_RECORDS_READY.  Here every shard is a column view of the same
+    logits on one GPU; with a tensor-parallel LM head each GPU would run its
+    own sv_shard_stats and the partials would be gathered for the merge.
+    `shards` is a count (shard_bounds) or a list of (offset, count) pairs
+    tiling [0, V)."""
+
+    def __init__(self, mode, target, draft, draft_tokens=None, temperature=None, top_p=None,
+                 k_per_row=None, shards=8, seed=0, offset=0, flags=0):
+        if mode not in ("sample", "draft"):
+            raise ValueError("mode must be 'sample' or 'draft'")
+        if draft.dtype != torch.bfloat16:
+            raise TypeError("sharded statistics take bf16 logits")
+        self.call = VerifyCall(mode, target, draft, draft_tokens, temperature, top_p, k_per_row,
+                               seed, offset, int(flags) | FLAG_RECORDS_READY)
+        va = self.call.args
+        dev, B, K, V = draft.device, va.B, va.k_max, va.V
+        m = 0 if mode == "sample" else 1
+        L = library()
+        self.bounds = shard_bounds(V, shards) if isinstance(shards, int) else \
+            [(int(o), int(c)) for o, c in shards]
+        self.shard_args, self.partials, self.scratch = [], [], []
+        for off, cnt in self.bounds:
+            a = ShardStatsArgs()
+            a.B, a.k_max, a.V, a.col_offset, a.col_count, a.mode = B, K, V, off, cnt, m
+            if m == 0:
+                a.target_shard = va.target_logits + 2 * off
+                a.target_vec_stride = va.target_vec_stride
+                a.draft_tokens = va.draft_tokens
+            a.draft_shard = va.draft_logits + 2 * off
+            a.draft_vec_stride = va.draft_vec_stride
+            a.k_per_row = va.k_per_row
+            part = torch.empty(max(L.sv_shard_partial_bytes(B, K, cnt), 256), dtype=torch.uint8,
+                               device=dev)
+            ws = torch.empty(max(L.sv_shard_workspace_bytes(B, K), 256), dtype=torch.uint8,
+                             device=dev)
+            a.partial, a.partial_bytes = part.data_ptr(), part.numel()
+            a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+            self.shard_args.append(a)
+            self.partials.append(part)
+            self.scratch.append(ws)
+        c = ShardCombineArgs()
+        c.B, c.k_max, c.V, c.mode, c.G = B, K, V, m, len(self.bounds)
+        for g, (off, cnt) in enumerate(self.bounds):
+            c.partials[g] = self.partials[g].data_ptr()
+            c.col_offset[g], c.col_count[g] = off, cnt
+            sa = self.shard_args[g]
+            c.target_shards[g] = sa.target_shard
+            c.target_vec_stride[g] = sa.target_vec_stride
+            c.draft_shards[g] = sa.draft_shard
+            c.draft_vec_stride[g] = sa.draft_vec_stride
+        c.draft_tokens, c.k_per_row = va.draft_tokens, va.k_per_row
+        c.temperature, c.top_p, c.flags = va.temperature, va.top_p, int(flags)
+        c.workspace, c.workspace_bytes = va.workspace, va.workspace_bytes
+        self.combine_args = c
+        self.outputs = self.call.outputs
+        self.device = dev
+        self._h = handle(dev)
+
+    def run_shard(self, g, stream=None):
+        """The pass over shard g alone (one GPU's share of the work)."""
+        rc = library().sv_shard_stats(self._h, C.byref(self.shard_args[g]),
+                                      _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_shard_stats", rc)
+
+    def run_combine(self, stream=None):
+        rc = library().sv_shard_combine(self._h, C.byref(self.combine_args),
+                                        _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_shard_combine", rc)
+
+    def run(self, stream=None):
+        for g in range(len(self.bounds)):
+            self.run_shard(g, stream)
+        self.run_combine(stream)
+        return self.call.run(stream)
+
+
+def verify_sample_sharded(target, draft, draft_tokens, temperature, top_p=None, k_per_row=None,
+                          shards=8, seed=0, offset=0, flags=0, stream=None):
+    """verify_sample with the statistics computed shard by shard and merged."""
+    return ShardedCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
+                       shards, seed, offset, flags).run(stream)
+
+
+def draft_sample_sharded(draft, temperature, top_p=None, k_per_row=None, shards=8, seed=0,
+                         offset=0, flags=0, stream=None):
+    """draft_sample with the statistics computed shard by shard and merged."""
+    out = ShardedCall("draft", None, draft, None, temperature, top_p, k_per_row, shards, seed,
+                      offset, flags).run(stream)
+    return out["draft_tokens"], out["row_status"]
+

@@ -213,6 +213,9 @@ static sv::StatsParams stats_params(const sv_verify_args* a, int mode) {
   p.slot_count = (int32_t*)(plan + align_up(sv::stats_ticket_bytes(), 256));
   const bool listed = a->k_per_row != nullptr || mode == 1;
   p.slot_list = listed ? p.slot_count + 64 : nullptr;
+  p.col_off = 0;
+  p.partial = nullptr;
+  p.part_stride = 0;
   return p;
 }
 
@@ -250,7 +253,9 @@ sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
-  if (sv::launch_stats(stats_params(a, 0), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (!(a->flags & SV_FLAG_RECORDS_READY) &&
+      sv::launch_stats(stats_params(a, 0), a->dtype, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
   if (sv::launch_finalize_sample(finalize_params(a), h->num_cus, s, h->active()) != hipSuccess)
     return SV_E_DEVICE;
   return SV_OK;
@@ -261,7 +266,9 @@ sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
-  if (sv::launch_stats(stats_params(a, 1), a->dtype, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (!(a->flags & SV_FLAG_RECORDS_READY) &&
+      sv::launch_stats(stats_params(a, 1), a->dtype, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
   if (sv::launch_draft_sample(finalize_params(a), h->num_cus, s, h->active()) != hipSuccess)
     return SV_E_DEVICE;
   return SV_OK;
@@ -379,3 +386,135 @@ sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, h
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- vocabulary shards
+
+size_t sv_shard_partial_bytes(int32_t B, int32_t k_max, int32_t col_count) {
+  if (B < 0 || k_max < 1 || k_max > SV_MAX_K || col_count < 1) return 0;
+  const size_t n = (size_t)B * sv::slots_per_row(k_max) * (size_t)sv::shard_part_stride(col_count);
+  return n > 0 ? n : 256;
+}
+
+size_t sv_shard_workspace_bytes(int32_t B, int32_t k_max) {
+  if (B < 0 || k_max < 1 || k_max > SV_MAX_K) return 0;
+  return sv::stats_plan_bytes(B, k_max);
+}
+
+sv_status sv_check_shard_stats_args(const sv_shard_stats_args* a) {
+  if (!a) return SV_E_ARG;
+  if (a->B < 0 || a->k_max < 1 || a->k_max > SV_MAX_K || a->V < 1 || a->V > kMaxVSampled)
+    return SV_E_ARG;
+  if (a->mode != 0 && a->mode != 1) return SV_E_ARG;
+  if (a->col_offset < 0 || a->col_count < 1 || (int64_t)a->col_offset + a->col_count > a->V)
+    return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (!a->draft_shard || a->draft_vec_stride < a->col_count) return SV_E_ARG;
+  if (a->mode == 0 &&
+      (!a->target_shard || a->target_vec_stride < a->col_count || !a->draft_tokens))
+    return SV_E_ARG;
+  if (!a->partial || a->partial_bytes < sv_shard_partial_bytes(a->B, a->k_max, a->col_count))
+    return SV_E_WORKSPACE;
+  if (!a->workspace || a->workspace_bytes < sv_shard_workspace_bytes(a->B, a->k_max))
+    return SV_E_WORKSPACE;
+  return SV_OK;
+}
+
+sv_status sv_shard_stats(sv_handle h, const sv_shard_stats_args* a, hipStream_t s) {
+  const sv_status st = sv_check_shard_stats_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::StatsParams p;
+  p.target = a->mode == 0 ? a->target_shard : a->draft_shard;
+  p.draft = a->draft_shard;
+  p.t_stride = a->mode == 0 ? a->target_vec_stride : a->draft_vec_stride;
+  p.d_stride = a->draft_vec_stride;
+  p.tokens = a->mode == 0 ? a->draft_tokens : nullptr;
+  p.k_per_row = a->k_per_row;
+  p.temperature = nullptr;  // the shard pass counts only
+  p.top_p = nullptr;
+  p.B = a->B;
+  p.K = a->k_max;
+  p.V = a->col_count;
+  p.flags = 0;
+  p.mode = a->mode;
+  p.recs = nullptr;
+  char* plan = (char*)a->workspace;
+  p.tickets = (uint32_t*)plan;
+  p.slot_count = (int32_t*)(plan + align_up(sv::stats_ticket_bytes(), 256));
+  const bool listed = a->k_per_row != nullptr || a->mode == 1;
+  p.slot_list = listed ? p.slot_count + 64 : nullptr;
+  p.col_off = a->col_offset;
+  p.partial = (uint8_t*)a->partial;
+  p.part_stride = sv::shard_part_stride(a->col_count);
+  if (sv::launch_shard_stats(p, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_check_shard_combine_args(const sv_shard_combine_args* a) {
+  if (!a) return SV_E_ARG;
+  if (a->B < 0 || a->k_max < 1 || a->k_max > SV_MAX_K || a->V < 1 || a->V > kMaxVSampled)
+    return SV_E_ARG;
+  if (a->mode != 0 && a->mode != 1) return SV_E_ARG;
+  if (a->G < 1 || a->G > SV_MAX_SHARDS) return SV_E_ARG;
+  int64_t end = 0;
+  for (int g = 0; g < a->G; ++g) {
+    if (a->col_offset[g] != end || a->col_count[g] < 1) return SV_E_ARG;
+    end += a->col_count[g];
+  }
+  if (end != a->V) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  for (int g = 0; g < a->G; ++g) {
+    if (!a->partials[g] || !a->draft_shards[g] || a->draft_vec_stride[g] < a->col_count[g])
+      return SV_E_ARG;
+    if (a->mode == 0 && (!a->target_shards[g] || a->target_vec_stride[g] < a->col_count[g]))
+      return SV_E_ARG;
+  }
+  if (!a->temperature || (a->mode == 0 && !a->draft_tokens)) return SV_E_ARG;
+  if (!a->workspace || a->workspace_bytes < sample_ws(a->B, a->k_max)) return SV_E_WORKSPACE;
+  return SV_OK;
+}
+
+sv_status sv_shard_combine(sv_handle h, const sv_shard_combine_args* a, hipStream_t s) {
+  const sv_status st = sv_check_shard_combine_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::CombineParams c;
+  memset(&c, 0, sizeof(c));
+  sv::StatsParams& p = c.sp;
+  p.target = a->mode == 0 ? a->target_shards[0] : a->draft_shards[0];
+  p.draft = a->draft_shards[0];
+  p.t_stride = a->mode == 0 ? a->target_vec_stride[0] : a->draft_vec_stride[0];
+  p.d_stride = a->draft_vec_stride[0];
+  p.tokens = a->mode == 0 ? a->draft_tokens : nullptr;
+  p.k_per_row = a->k_per_row;
+  p.temperature = a->temperature;
+  p.top_p = a->top_p;
+  p.B = a->B;
+  p.K = a->k_max;
+  p.V = a->V;
+  p.flags = a->flags;
+  p.mode = a->mode;
+  p.recs = (sv::VecRec*)a->workspace;
+  p.tickets = nullptr;
+  p.slot_count = nullptr;
+  p.slot_list = nullptr;
+  p.col_off = 0;
+  p.partial = nullptr;
+  p.part_stride = 0;
+  c.G = a->G;
+  for (int g = 0; g < a->G; ++g) {
+    c.part[g] = (const uint8_t*)a->partials[g];
+    c.part_stride[g] = sv::shard_part_stride(a->col_count[g]);
+    c.col_off[g] = a->col_offset[g];
+    c.col_len[g] = a->col_count[g];
+    c.tgt[g] = (const uint16_t*)(a->mode == 0 ? a->target_shards[g] : a->draft_shards[g]);
+    c.ts[g] = a->mode == 0 ? a->target_vec_stride[g] : a->draft_vec_stride[g];
+    c.dft[g] = (const uint16_t*)a->draft_shards[g];
+    c.ds[g] = a->draft_vec_stride[g];
+  }
+  if (sv::launch_shard_combine(c, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+

@@ -128,6 +128,13 @@ __device__ __forceinline__ float load_logit(const void* vec, int dtype, int64_t 
   return ((const float*)vec)[j];
 }
 
+// The logits of one vector stored in one piece, for generic_stats.
+struct VecLogits {
+  const void* vec;
+  int dtype;
+  __device__ __forceinline__ float operator()(int64_t j) const { return load_logit(vec, dtype, j); }
+};
+
 // Weight exp((z - m) / T) of one value, formed as the finalize kernel forms
 // it: exp2 of an fp32 argument, c2 = log2(e) / T.  (z - m) is exact for bf16.
 __device__ __forceinline__ double weight(float z, float m, float c2) {
@@ -170,17 +177,18 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // All NT threads of the block call this.  hist256 is LDS of 256 doubles.
 // The bf16 kernel reaches it only for a vector its count table cannot hold.
-template <int NT>
-__device__ __forceinline__ void generic_stats(const void* vec, int token, float T, double P,
-                                              int dtype, int V, double* hist256,
-                                              Scratch<NT / 64>& sc, VecRec* rec) {
+// logit(j) returns logit j of the vector, j in [0, V).
+template <int NT, class Logits>
+__device__ __forceinline__ void generic_stats(const Logits& logit, int token, float T, double P, int V,
+                                              double* hist256, Scratch<NT / 64>& sc,
+                                              VecRec* rec) {
   const int tid = threadIdx.x;
   const bool T_ok = T > 0.0f && isfinite(T);
   // pass 1: largest finite value, NaN / +inf, any finite entry
   float mx = -INFINITY;
   uint32_t fl = 0, nfin = 0;
   for (int64_t j = tid; j < V; j += NT) {
-    const float z = load_logit(vec, dtype, j);
+    const float z = logit(j);
     if (isnan(z) || z == INFINITY) fl |= SV_ROW_NONFINITE_LOGIT;
     else if (z > -INFINITY) { nfin = 1; mx = fmaxf(mx, z); }
   }
@@ -193,7 +201,7 @@ __device__ __forceinline__ void generic_stats(const void* vec, int token, float 
   uint32_t flags = 0;
   for (int i = 0; i < NT / 64; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
   __syncthreads();
-  const float zx = (token >= 0 && token < V) ? load_logit(vec, dtype, token)
+  const float zx = (token >= 0 && token < V) ? logit(token)
                                                : __uint_as_float(0x7FC00000u);
   uint32_t status = flags & SV_ROW_NONFINITE_LOGIT;
   if (!(flags & 0x80000000u)) status |= SV_ROW_NO_FINITE;
@@ -204,7 +212,7 @@ __device__ __forceinline__ void generic_stats(const void* vec, int token, float 
   const float c2 = log2e_over_T(T);
   // pass 2: normaliser S
   double acc = 0.0;
-  for (int64_t j = tid; j < V; j += NT) acc += weight(load_logit(vec, dtype, j), m, c2);
+  for (int64_t j = tid; j < V; j += NT) acc += weight(logit(j), m, c2);
   const double S = block_sum_d<NT>(acc, sc);
   if (!(P < 1.0)) {
     if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, S, 0, zx, rec);
@@ -221,7 +229,7 @@ __device__ __forceinline__ void generic_stats(const void* vec, int token, float 
     for (int i = tid; i < 256; i += NT) hist256[i] = 0.0;
     __syncthreads();
     for (int64_t j = tid; j < V; j += NT) {
-      const float z = load_logit(vec, dtype, j);
+      const float z = logit(j);
       if (!(z > -INFINITY)) continue;
       const uint32_t k = order_key(z);
       if ((k & hmask) != (prefix & hmask)) continue;
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams 
   __shared__ Scratch<kGenThreads / 64> sc;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
-  generic_stats<kGenThreads>(s.vec, s.token, s.T, s.P, dtype, p.V, hist256, sc,
+  generic_stats<kGenThreads>(VecLogits{s.vec, dtype}, s.token, s.T, s.P, p.V, hist256, sc,
                              p.recs + blockIdx.x);
 }
 
@@ -556,6 +564,8 @@ struct SlotP {
   double P;
 };
 
+// The shard pass (SHARD) counts only: it reads no temperature or top-p.
+template <bool SHARD>
 __device__ __forceinline__ SlotP slot_params(const StatsParams& p, int v) {
   const int K = p.K, per = slots_per_row(K);
   const int b = v / per, j = v % per;
@@ -566,11 +576,12 @@ __device__ __forceinline__ SlotP slot_params(const StatsParams& p, int v) {
                      : (const uint16_t*)p.target + ((int64_t)b * (K + 1) + i) * p.t_stride;
   // pointers that may be NULL are swapped for a valid dummy before loading
   const float* Tp = p.temperature + b;
-  const int32_t* tokp = p.tokens ? p.tokens + (int64_t)b * K + min(i, K - 1) : (const int32_t*)Tp;
-  const int32_t* kbp = p.k_per_row ? p.k_per_row + b : (const int32_t*)Tp;
+  const int32_t* dummy = SHARD ? p.slot_count : (const int32_t*)Tp;
+  const int32_t* tokp = p.tokens ? p.tokens + (int64_t)b * K + min(i, K - 1) : dummy;
+  const int32_t* kbp = p.k_per_row ? p.k_per_row + b : dummy;
   const float* Pp = p.top_p ? p.top_p + b : Tp;
   const int tok = *tokp, kbl = *kbp;
-  const float T = *Tp, Pl = *Pp;
+  const float T = SHARD ? 1.0f : *Tp, Pl = SHARD ? 1.0f : *Pp;
   const int kb = p.k_per_row ? kbl : K;
   s.token = (p.mode == 1 || (!draft_side && i >= kb)) ? -1 : tok;
   s.T = T;
@@ -587,18 +598,31 @@ struct Bf16Shared {
   int next;
 };
 
+// The count table as the streaming loop keeps it: one word per magnitude,
+// the count of +v in the low half and of -v in the high half.
+struct PackedTable {
+  const uint4* hist4;
+  // the counts of one sign at the four magnitudes of 16-byte group grp
+  __device__ __forceinline__ uint4 counts(int grp, bool pos) const {
+    const uint4 g = hist4[grp];
+    return pos ? make_uint4(g.x & 0xFFFFu, g.y & 0xFFFFu, g.z & 0xFFFFu, g.w & 0xFFFFu)
+               : make_uint4(g.x >> 16, g.y >> 16, g.z >> 16, g.w >> 16);
+  }
+};
+
 // Level 2 of the top-p search, run by one wave: the 256 magnitudes of bin b
 // of one sign, walked from the largest value down.  `above` is the mass of
 // all larger values.  Returns the threshold value and the kept mass through
 // it (wave-uniform).
-__device__ __forceinline__ void crossing_value(const uint4* hist4, int b, bool pos, double above,
+template <class Table>
+__device__ __forceinline__ void crossing_value(const Table& tab, int b, bool pos, double above,
                                                double target, float m, float c2, float* tau,
                                                double* kept) {
   const int l = threadIdx.x & 63;
   // lanes ascending = values descending: +values from the top magnitude
   // down, -values from the bottom magnitude up
   const int grp = b * 64 + (pos ? 63 - l : l);
-  const uint4 g = hist4[grp];
+  const uint4 g = tab.counts(grp, pos);
   const uint32_t xs[4] = {pos ? g.w : g.x, pos ? g.z : g.y, pos ? g.y : g.z, pos ? g.x : g.w};
   double mass[4];
   uint32_t keys[4];
@@ -606,7 +630,7 @@ __device__ __forceinline__ void crossing_value(const uint4* hist4, int b, bool p
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t word = 4u * (uint32_t)grp + (uint32_t)(pos ? 3 - i : i);
-    const uint32_t c = pos ? (xs[i] & 0xFFFFu) : (xs[i] >> 16);
+    const uint32_t c = xs[i];
     keys[i] = (word + kBase) | (pos ? 0u : 0x8000u);
     mass[i] = c ? (double)c * weight(bf16f(keys[i]), m, c2) : 0.0;
     part += mass[i];
@@ -681,6 +705,154 @@ __device__ __forceinline__ void tiny_crossing(const uint32_t* tiny, uint32_t n, 
   *kept = readlane_f64(above + ge, L);
 }
 
+// E2 of the epilogue: the masses of the values of each (wave, row) bin --
+// wave w with row j owns magnitude bin w + kWv j of both signs, thread t the
+// 16-byte groups t + kT j (bit j of gmask: the group holds a count) -- then
+// the zero bin and, by the last wave, the listed values below the window.
+template <class Table>
+__device__ __forceinline__ void bin_masses(const Table& tab, uint32_t gmask, float m, float c2,
+                                           uint32_t Z, const uint32_t* tiny, uint32_t NT,
+                                           double* bins) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+#pragma unroll 1
+  for (int j = 0; j < kGpt; ++j) {
+    const int g = tid + kT * j;
+    const int b = w + kWv * j;
+    double mp = 0.0, mn = 0.0;
+    if ((gmask >> j) & 1u) {
+      const uint4 cp = tab.counts(g, true), cn = tab.counts(g, false);
+      const uint32_t ps[4] = {cp.x, cp.y, cp.z, cp.w}, ns[4] = {cn.x, cn.y, cn.z, cn.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t key = 4u * (uint32_t)g + (uint32_t)q + kBase;
+        const uint32_t lo = ps[q], hi = ns[q];
+        if (lo) mp += (double)lo * weight(bf16f(key), m, c2);
+        if (hi) mn += (double)hi * weight(bf16f(key | 0x8000u), m, c2);
+      }
+    }
+    if (__ballot((gmask >> j) & 1u)) {
+      mp = wave_last_f64(wave_scan_add_f64(mp));
+      mn = wave_last_f64(wave_scan_add_f64(mn));
+    }
+    if (l == 0) { bins[pos_bin(b)] = mp; bins[neg_bin(b)] = mn; }
+  }
+  if (tid == 0) bins[kZeroBin] = Z ? (double)Z * weight(0.0f, m, c2) : 0.0;
+  if (w == kWv - 1) {  // the listed values below the window, by sign
+    double tp = 0.0, tn = 0.0;
+    if (NT) {
+      const bool has = (uint32_t)l < NT;
+      const uint32_t k = tiny[1 + (has ? l : 0)];
+      const double wt = has ? weight(bf16f(k), m, c2) : 0.0;
+      const bool neg = (k & 0x8000u) != 0u;
+      tp = wave_last_f64(wave_scan_add_f64(neg ? 0.0 : wt));
+      tn = wave_last_f64(wave_scan_add_f64(neg ? wt : 0.0));
+    }
+    if (l == 0) { bins[kZeroBin + 1] = tp; bins[kZeroBin - 1] = tn; }
+  }
+}
+
+// The last step of the epilogue, run by wave 0: S and the top-p threshold in
+// two levels (the rank bin holding the crossing, then the value inside it),
+// then the record (written by thread 0).  zx is the draft token's logit
+// (NaN when the slot verifies none).
+template <class Table>
+__device__ __forceinline__ void topp_record(const Table& tab, const double* bins,
+                                            const uint32_t* tiny, uint32_t NT, bool stats_ok,
+                                            double P, float m, float c2, int token, float T,
+                                            bool T_ok, int V, uint32_t status, float zx,
+                                            VecRec* rec) {
+  const int l = threadIdx.x & 63;
+  double S = 0.0, kept = 0.0;
+  float tau = -INFINITY;
+  if (stats_ok) {
+    // lane l holds rank bin kRankBins - 1 - l (values descending)
+    const int R = kRankBins - 1 - l;
+    const double part = R >= 0 ? bins[R] : 0.0;
+    const double incl = wave_scan_add_f64(part);
+    S = wave_last_f64(incl);
+    kept = S;
+    if (P < 1.0) {
+      const double target = P * S;
+      const uint64_t hit = __ballot(part > 0.0 && incl >= target);
+      const uint64_t any = __ballot(part > 0.0);
+      // S > 0 (the maximum has weight 1), so some lane has mass
+      const int L = hit ? __builtin_ctzll(hit) : any ? 63 - __builtin_clzll(any) : 0;
+      const int RL = kRankBins - 1 - L;
+      const double above = readlane_f64(incl - part, L);
+      if (RL == kZeroBin) {
+        tau = 0.0f;
+        kept = above + readlane_f64(part, L);
+      } else if (RL == kZeroBin + 1 || RL == kZeroBin - 1) {
+        tiny_crossing(tiny, NT, RL > kZeroBin, above, target, m, c2, &tau, &kept);
+      } else if (RL > kZeroBin) {
+        crossing_value(tab, RL - kZeroBin - 2, true, above, target, m, c2, &tau, &kept);
+      } else if (RL >= 0) {
+        crossing_value(tab, kZeroBin - 2 - RL, false, above, target, m, c2, &tau, &kept);
+      }
+    }
+  }
+  if (threadIdx.x == 0) write_record(token, T, T_ok, V, m, tau, kept, status, zx, rec);
+}
+
+// The shard pass's epilogue, once the copies are merged into copy 0: the
+// vector's partial -- ShardHead, the values below the window, and the
+// nonzero table words as (word, counts) pairs in thread order (a block-wide
+// exclusive scan of each thread's count places them).  All threads call it.
+__device__ __forceinline__ void shard_emit(const StatsParams& p, int v, const uint4* hist4,
+                                           uint32_t gmask, const uint32_t* tiny, uint32_t NT,
+                                           uint32_t status, int MP, int MN, uint32_t Z,
+                                           uint32_t NI, uint32_t zx, uint32_t* wlist) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  uint8_t* base = p.partial + (int64_t)v * p.part_stride;
+  uint2* list = reinterpret_cast<uint2*>(base + kShardListOffset);
+  uint32_t mine = 0;
+#pragma unroll 1
+  for (int j = 0; j < kGpt; ++j) {
+    if ((gmask >> j) & 1u) {
+      const uint4 d = hist4[tid + kT * j];
+      mine += (d.x != 0u ? 1u : 0u) + (d.y != 0u ? 1u : 0u) + (d.z != 0u ? 1u : 0u) +
+              (d.w != 0u ? 1u : 0u);
+    }
+  }
+  const uint32_t incl = wave_scan_u32<OpAddU32>(mine);
+  if (l == 63) wlist[w] = incl;
+  __syncthreads();
+  uint32_t o = incl - mine, total = 0;
+#pragma unroll
+  for (int k = 0; k < kWv; ++k) {
+    o += k < w ? wlist[k] : 0u;
+    total += wlist[k];
+  }
+#pragma unroll 1
+  for (int j = 0; j < kGpt; ++j) {
+    if ((gmask >> j) & 1u) {
+      const int g = tid + kT * j;
+      const uint4 d = hist4[g];
+      const uint32_t xs[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (xs[q]) list[o++] = make_uint2(4u * (uint32_t)g + (uint32_t)q, xs[q]);
+    }
+  }
+  uint32_t* tl = reinterpret_cast<uint32_t*>(base + sizeof(ShardHead));
+  if ((uint32_t)tid < min(NT, (uint32_t)kShardTinyCap)) tl[tid] = tiny[1 + tid];
+  if (tid == 0) {
+    ShardHead h;
+    h.status = status;
+    h.maxpos = MP;
+    h.minneg = MN;
+    h.zeros = Z;
+    h.ninf = NI;
+    h.ntiny = NT;
+    h.nlist = total;
+    h.zx = zx;
+    *reinterpret_cast<ShardHead*>(base) = h;
+  }
+}
+
+// SHARD: the pass over one vocabulary shard (V = the shard's columns), whose
+// epilogue writes the partial instead of the record.
+template <bool SHARD>
 __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p) {
   __shared__ __align__(16) uint32_t hist[kCopies * kCopyWords];
   __shared__ double bins[kRankBins];
@@ -702,16 +874,25 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   if (tid == 0) tiny[0] = 0u;
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
-  SlotP cur = slot_params(p, v);
+  SlotP cur = slot_params<SHARD>(p, v);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
     if (tid == 0) sh.next = take_ticket(p, queue);
     const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
-    // the draft token's logit, loaded by every thread from one address
-    const bool has_zx = cur.token >= 0 && cur.token < V;
-    const uint32_t zbits = cur.vec[has_zx ? cur.token : 0];
+    // the draft token's logit, loaded by every thread from one address (a
+    // shard holds columns col_off.. of the vector)
+    bool has_zx;
+    uint32_t zbits;
+    if constexpr (SHARD) {
+      const int tokl = cur.token - p.col_off;
+      has_zx = cur.token >= 0 && tokl >= 0 && tokl < V;
+      zbits = cur.vec[has_zx ? tokl : 0];
+    } else {
+      has_zx = cur.token >= 0 && cur.token < V;
+      zbits = cur.vec[has_zx ? cur.token : 0];
+    }
 
     Side sd;
     stream_vector(cur.vec, V, hcopy, tiny, sd);
@@ -725,7 +906,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     const int in = sh.next;
     const bool has_next = in < nitems;
     const int vn = has_next ? item_slot(p, in, (uint32_t)nitems, stride) : v;
-    const SlotP nxt = slot_params(p, vn);  // loads in flight meanwhile
+    const SlotP nxt = slot_params<SHARD>(p, vn);  // loads in flight meanwhile
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
     // and clears copy 1; largest +magnitude, smallest -magnitude present,
@@ -778,99 +959,39 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     }
     uint32_t status = FL & SV_ROW_NONFINITE_LOGIT;
     const uint32_t NT = tiny[0];
-    // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
-    // count past 65535), a logit above the window, more values below it than
-    // the list holds, or no positive value in the window while some lie
-    // below it (the largest logit would be one of them): the generic path
-    // redoes the vector
-    const bool fallback = !status && ((FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V ||
-                                      (MP < 0 && NT > 0));
-    if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
-    const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
-                  : Z > 0   ? 0.0f
-                  : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
-                                    : -INFINITY;
-    const bool stats_ok = !fallback && !status && T_ok;
-    const float c2 = log2e_over_T(cur.T);
+    if constexpr (SHARD) {
+      // a count that wrapped 16 bits, a logit above the window, or more
+      // values below it than the list holds: the merge redoes the vector
+      const bool over = (FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V;
+      shard_emit(p, v, hist4, gmask, tiny, NT, status | (over ? kShardFallback : 0u), MP, MN, Z,
+                 NI, has_zx ? (1u << 16) | (zbits & 0xFFFFu) : 0u,
+                 reinterpret_cast<uint32_t*>(bins));  // bins are free in this pass
+    } else {
+      // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
+      // count past 65535), a logit above the window, more values below it than
+      // the list holds, or no positive value in the window while some lie
+      // below it (the largest logit would be one of them): the generic path
+      // redoes the vector
+      const bool fallback =
+          !status && ((FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V ||
+                      (MP < 0 && NT > 0));
+      if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
+      const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
+                    : Z > 0   ? 0.0f
+                    : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
+                                      : -INFINITY;
+      const bool stats_ok = !fallback && !status && T_ok;
+      const float c2 = log2e_over_T(cur.T);
 
-    // ---- E2: masses of the values of each (wave, row) bin: wave w with row
-    // j owns magnitude bin w + kWv j of both signs
-    if (stats_ok) {
-#pragma unroll 1
-      for (int j = 0; j < kGpt; ++j) {
-        const int g = tid + kT * j;
-        const int b = w + kWv * j;
-        double mp = 0.0, mn = 0.0;
-        if ((gmask >> j) & 1u) {
-          const uint4 d = hist4[g];
-          const uint32_t xs[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t key = 4u * (uint32_t)g + (uint32_t)q + kBase;
-            const uint32_t lo = xs[q] & 0xFFFFu, hi = xs[q] >> 16;
-            if (lo) mp += (double)lo * weight(bf16f(key), m, c2);
-            if (hi) mn += (double)hi * weight(bf16f(key | 0x8000u), m, c2);
-          }
-        }
-        if (__ballot((gmask >> j) & 1u)) {
-          mp = wave_last_f64(wave_scan_add_f64(mp));
-          mn = wave_last_f64(wave_scan_add_f64(mn));
-        }
-        if (l == 0) { bins[pos_bin(b)] = mp; bins[neg_bin(b)] = mn; }
+      if (stats_ok) bin_masses(PackedTable{hist4}, gmask, m, c2, Z, tiny, NT, bins);
+      __syncthreads();  // B3: bins written
+      if (w == 0 && !fallback)
+        topp_record(PackedTable{hist4}, bins, tiny, NT, stats_ok, cur.P, m, c2, cur.token, cur.T,
+                    T_ok, V, status, has_zx ? bf16f(zbits) : __uint_as_float(0x7FC00000u), rec);
+      if (fallback) {
+        generic_stats<kT>(VecLogits{cur.vec, SV_BF16}, cur.token, cur.T, cur.P, V, hist256, sc,
+                          rec);
       }
-      if (tid == 0) bins[kZeroBin] = Z ? (double)Z * weight(0.0f, m, c2) : 0.0;
-      if (w == kWv - 1) {  // the listed values below the window, by sign
-        double tp = 0.0, tn = 0.0;
-        if (NT) {
-          const bool has = (uint32_t)l < NT;
-          const uint32_t k = tiny[1 + (has ? l : 0)];
-          const double wt = has ? weight(bf16f(k), m, c2) : 0.0;
-          const bool neg = (k & 0x8000u) != 0u;
-          tp = wave_last_f64(wave_scan_add_f64(neg ? 0.0 : wt));
-          tn = wave_last_f64(wave_scan_add_f64(neg ? wt : 0.0));
-        }
-        if (l == 0) { bins[kZeroBin + 1] = tp; bins[kZeroBin - 1] = tn; }
-      }
-    }
-    __syncthreads();  // B3: bins written
-
-    // ---- wave 0: S and the top-p threshold in two levels, then the record
-    if (w == 0 && !fallback) {
-      double S = 0.0, kept = 0.0;
-      float tau = -INFINITY;
-      if (stats_ok) {
-        // lane l holds rank bin kRankBins - 1 - l (values descending)
-        const int R = kRankBins - 1 - l;
-        const double part = R >= 0 ? bins[R] : 0.0;
-        const double incl = wave_scan_add_f64(part);
-        S = wave_last_f64(incl);
-        kept = S;
-        if (cur.P < 1.0) {
-          const double target = cur.P * S;
-          const uint64_t hit = __ballot(part > 0.0 && incl >= target);
-          const uint64_t any = __ballot(part > 0.0);
-          // S > 0 (the maximum has weight 1), so some lane has mass
-          const int L = hit ? __builtin_ctzll(hit) : any ? 63 - __builtin_clzll(any) : 0;
-          const int RL = kRankBins - 1 - L;
-          const double above = readlane_f64(incl - part, L);
-          if (RL == kZeroBin) {
-            tau = 0.0f;
-            kept = above + readlane_f64(part, L);
-          } else if (RL == kZeroBin + 1 || RL == kZeroBin - 1) {
-            tiny_crossing(tiny, NT, RL > kZeroBin, above, target, m, c2, &tau, &kept);
-          } else if (RL > kZeroBin) {
-            crossing_value(hist4, RL - kZeroBin - 2, true, above, target, m, c2, &tau, &kept);
-          } else if (RL >= 0) {
-            crossing_value(hist4, kZeroBin - 2 - RL, false, above, target, m, c2, &tau, &kept);
-          }
-        }
-      }
-      if (tid == 0)
-        write_record(cur.token, cur.T, T_ok, V, m, tau, kept, status,
-                     has_zx ? bf16f(zbits) : __uint_as_float(0x7FC00000u), rec);
-    }
-    if (fallback) {
-      generic_stats<kT>(cur.vec, cur.token, cur.T, cur.P, SV_BF16, V, hist256, sc, rec);
     }
     __syncthreads();  // B4: the table is no longer read
     if (tid == 0) tiny[0] = 0u;
@@ -880,6 +1001,141 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     if (!has_next) break;
     v = vn;
     cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------- shards
+
+static_assert(kWords == kTableWords && kTinyCap == kShardTinyCap, "shard partial layout");
+
+// The merged table of the combine: one 32-bit count per magnitude and sign
+// (a merged count may pass 16 bits).
+struct SplitTable {
+  const uint4* pos4;
+  const uint4* neg4;
+  __device__ __forceinline__ uint4 counts(int grp, bool pos) const {
+    return pos ? pos4[grp] : neg4[grp];
+  }
+};
+
+// The logits of one vector held as the shards' column slices, for
+// generic_stats (a vector the merged table cannot hold).
+struct SliceLogits {
+  const CombineParams& cp;
+  int64_t idx;  // vector index: b (k+1) + i on the target side, b k + i on the draft side
+  bool draft;
+  __device__ __forceinline__ float operator()(int64_t j) const {
+    int g = 0;
+    while (g + 1 < cp.G && j >= cp.col_off[g + 1]) ++g;
+    const uint16_t* vec = draft ? cp.dft[g] + idx * cp.ds[g] : cp.tgt[g] + idx * cp.ts[g];
+    return __uint_as_float((uint32_t)vec[j - cp.col_off[g]] << 16);
+  }
+};
+
+// One workgroup per vector slot: the G shards' partials merged into one
+// count table (integer adds, exact), the zeros, -infs and values below the
+// window gathered in shard order, then the same epilogue as the unsharded
+// pass -- bin masses, S, the tie-closed top-p threshold, p'(x) -- so the
+// record is the one the unsharded pass writes for the concatenated vector.
+// A vector whose counts the table cannot hold is redone from the shards'
+// logits by the generic path.
+__global__ __launch_bounds__(kT, kWgPerCu) void shard_combine_kernel(CombineParams cp) {
+  __shared__ __align__(16) uint32_t cpos[kWords];
+  __shared__ __align__(16) uint32_t cneg[kWords];
+  __shared__ double bins[kRankBins];
+  __shared__ uint32_t tiny[1 + kTinyCap];
+  __shared__ ShardHead heads[kMaxShards];
+  __shared__ double hist256[256];
+  __shared__ Scratch<kWv> sc;
+  const StatsParams& p = cp.sp;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int v = blockIdx.x;
+  const Slot s = slot_of(p, SV_BF16, v);
+  if (!s.needed) return;
+  const int G = cp.G;
+  uint4* pos4 = reinterpret_cast<uint4*>(cpos);
+  uint4* neg4 = reinterpret_cast<uint4*>(cneg);
+  for (int i = tid; i < kGroups; i += kT) {
+    pos4[i] = make_uint4(0u, 0u, 0u, 0u);
+    neg4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid < G)
+    heads[tid] = *reinterpret_cast<const ShardHead*>(cp.part[tid] + (int64_t)v * cp.part_stride[tid]);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const uint8_t* base = cp.part[g] + (int64_t)v * cp.part_stride[g];
+    const uint2* list = reinterpret_cast<const uint2*>(base + kShardListOffset);
+    const uint32_t n = min(heads[g].nlist, (uint32_t)shard_list_cap(cp.col_len[g]));
+    for (uint32_t e = (uint32_t)tid; e < n; e += kT) {
+      const uint2 x = list[e];
+      if (x.x < (uint32_t)kWords) {
+        const uint32_t lo = x.y & 0xFFFFu, hi = x.y >> 16;
+        if (lo) __hip_atomic_fetch_add(cpos + x.x, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (hi) __hip_atomic_fetch_add(cneg + x.x, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+  }
+  uint32_t st = 0, Z = 0, NI = 0, NT = 0;
+  int MP = -1, MN = 0x7FFFFFFF;
+  for (int g = 0; g < G; ++g) {
+    const ShardHead& h = heads[g];
+    st |= h.status;
+    Z += h.zeros;
+    NI += h.ninf;
+    NT += h.ntiny;
+    MP = max(MP, h.maxpos);
+    MN = min(MN, h.minneg);
+  }
+  if (w == 0) {  // the values below the window, in shard order
+    uint32_t o = 0;
+    for (int g = 0; g < G; ++g) {
+      const uint32_t n = min(heads[g].ntiny, (uint32_t)kShardTinyCap);
+      const uint32_t* t = reinterpret_cast<const uint32_t*>(
+          cp.part[g] + (int64_t)v * cp.part_stride[g] + sizeof(ShardHead));
+      if ((uint32_t)l < n && o + (uint32_t)l < (uint32_t)kTinyCap) tiny[1 + o + l] = t[l];
+      o += n;
+    }
+  }
+  __syncthreads();
+  uint32_t gmask = 0;
+#pragma unroll 1
+  for (int j = 0; j < kGpt; ++j) {
+    const uint4 a = pos4[tid + kT * j], b = neg4[tid + kT * j];
+    if (a.x | a.y | a.z | a.w | b.x | b.y | b.z | b.w) gmask |= 1u << j;
+  }
+  uint32_t status = st & SV_ROW_NONFINITE_LOGIT;
+  // a shard the table could not hold, more values below the window than
+  // the list holds, or no positive value in the window while some lie
+  // below it: the generic path over the shards' logits
+  const bool fallback = !status && ((st & kShardFallback) || NT > (uint32_t)kTinyCap ||
+                                    (MP < 0 && NT > 0));
+  if (!fallback && MP < 0 && MN == 0x7FFFFFFF && Z == 0) status |= SV_ROW_NO_FINITE;
+  const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
+                : Z > 0   ? 0.0f
+                : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
+                                  : -INFINITY;
+  const bool stats_ok = !fallback && !status && s.T_ok;
+  const float c2 = log2e_over_T(s.T);
+  const SplitTable tab{pos4, neg4};
+  if (stats_ok) bin_masses(tab, gmask, m, c2, Z, tiny, NT, bins);
+  __syncthreads();
+  VecRec* rec = p.recs + v;
+  if (w == 0 && !fallback) {
+    // the draft token's logit, from the shard that holds its column
+    float zx = __uint_as_float(0x7FC00000u);
+    if (s.token >= 0 && s.token < p.V) {
+      int g = 0;
+      while (g + 1 < G && s.token >= cp.col_off[g + 1]) ++g;
+      if ((heads[g].zx >> 16) & 1u) zx = bf16f(heads[g].zx & 0xFFFFu);
+    }
+    topp_record(tab, bins, tiny, NT, stats_ok, s.P, m, c2, s.token, s.T, s.T_ok, p.V, status, zx,
+                rec);
+  }
+  if (fallback) {
+    const int per = slots_per_row(p.K), b = v / per, j = v % per;
+    const bool draft = j > p.K;
+    const int64_t idx = draft ? (int64_t)b * p.K + (j - p.K - 1) : (int64_t)b * (p.K + 1) + j;
+    generic_stats<kT>(SliceLogits{cp, idx, draft}, s.token, s.T, s.P, p.V, hist256, sc, rec);
   }
 }
 
@@ -954,11 +1210,35 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
       hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
     }
     TimedScope ts(t, "stats_bf16", s);
-    hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, p);
+    hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, p);
   } else {
     TimedScope ts(t, "stats_generic", s);
     hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kGenThreads), 0, s, p, dtype);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_stats(const StatsParams& p, int num_cus, hipStream_t s, Timer* t) {
+  const unsigned nslots = (unsigned)p.B * (unsigned)slots_per_row(p.K);
+  if (nslots == 0) return hipSuccess;
+  const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
+  unsigned want = cus * (unsigned)kWgPerCu;
+  if (want < (unsigned)kQueues) want = (unsigned)kQueues;
+  const unsigned grid = nslots < want ? nslots : want;
+  {
+    TimedScope ts(t, "stats_plan", s);
+    hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
+  }
+  TimedScope ts(t, "shard_stats", s);
+  hipLaunchKernelGGL(stats_bf16_kernel<true>, dim3(grid), dim3(kT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_combine(const CombineParams& p, hipStream_t s, Timer* t) {
+  const unsigned nslots = (unsigned)p.sp.B * (unsigned)slots_per_row(p.sp.K);
+  if (nslots == 0) return hipSuccess;
+  TimedScope ts(t, "shard_combine", s);
+  hipLaunchKernelGGL(shard_combine_kernel, dim3(nslots), dim3(kT), 0, s, p);
   return hipGetLastError();
 }
 

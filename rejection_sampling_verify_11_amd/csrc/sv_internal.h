@@ -74,6 +74,55 @@ struct StatsParams {
   int32_t* slot_list;    // the slots the call uses, in order, when some rows
                          // use fewer than all of theirs (k_per_row given, or
                          // draft sampling); NULL: every slot, slot = item
+  // vocabulary shard pass only (V is then the shard's column count): the
+  // shard's first column, and where its per-vector partials go
+  int32_t col_off;
+  uint8_t* partial;
+  int64_t part_stride;   // bytes per vector slot
+};
+
+// ---- vocabulary shards
+// One vector's partial statistics from one shard of the vocabulary: exact
+// value counts of the shard's logits, as a list of the nonzero words of the
+// count table (window of magnitudes [2^-24, 2^16), 40 exponent rows x 128
+// mantissas; a word holds the count of +v in its low half and of -v in its
+// high half), the zeros and -infs, the nonzero values below the window, and
+// the draft token's logit when the token is one of the shard's columns.
+// Layout per vector slot: ShardHead, then kShardTinyCap tiny values (raw
+// bf16 bits), then the list of (word, counts) pairs.
+constexpr int kTableWords = 40 * 128;
+constexpr int kShardTinyCap = 64;
+constexpr uint32_t kShardFallback = 1u << 30;  // the count table cannot hold the shard's values
+struct ShardHead {
+  uint32_t status;   // SV_ROW_NONFINITE_LOGIT | kShardFallback
+  int32_t maxpos;    // largest word with a +count, -1 if none
+  int32_t minneg;    // smallest word with a -count, 0x7FFFFFFF if none
+  uint32_t zeros, ninf;
+  uint32_t ntiny;    // nonzero values below the window (more than the cap: fallback)
+  uint32_t nlist;    // entries of the list
+  uint32_t zx;       // bit 16: the draft token is a column of this shard; low 16: its bits
+};
+static_assert(sizeof(ShardHead) == 32, "ShardHead layout");
+constexpr size_t kShardListOffset = sizeof(ShardHead) + 4 * kShardTinyCap;  // 288
+inline __host__ __device__ int shard_list_cap(int32_t cols) {
+  return cols < kTableWords ? cols : kTableWords;
+}
+inline __host__ __device__ int64_t shard_part_stride(int32_t cols) {
+  return (int64_t)kShardListOffset + 8 * (int64_t)shard_list_cap(cols);
+}
+constexpr int kMaxShards = SV_MAX_SHARDS;
+
+// The merge of all shards' partials into the records of the full vectors.
+struct CombineParams {
+  StatsParams sp;  // the call over the whole vocabulary (B, K, V, tokens, ..., recs)
+  int32_t G;
+  const uint8_t* part[kMaxShards];
+  int64_t part_stride[kMaxShards];
+  int32_t col_off[kMaxShards], col_len[kMaxShards];
+  // the shards' logits, read only for a vector the count table cannot hold
+  const uint16_t* tgt[kMaxShards];
+  const uint16_t* dft[kMaxShards];
+  int64_t ts[kMaxShards], ds[kMaxShards];
 };
 
 // Bytes of workspace the bf16 stats kernel keeps its queue counters, slot
@@ -161,6 +210,8 @@ struct TimedScope {
 
 // Launchers (each returns hipGetLastError() of its launch(es)).
 hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_t s, Timer* t);
+hipError_t launch_shard_stats(const StatsParams& p, int num_cus, hipStream_t s, Timer* t);
+hipError_t launch_shard_combine(const CombineParams& p, hipStream_t s, Timer* t);
 hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);

@@ -55,7 +55,9 @@ def _c_layout(struct, fields):
 
 @pytest.mark.parametrize("cls,cname", [(_abi.VerifyArgs, "sv_verify_args"),
                                        (_abi.RollbackArgs, "sv_rollback_args"),
-                                       (_abi.DynkArgs, "sv_dynk_args")])
+                                       (_abi.DynkArgs, "sv_dynk_args"),
+                                       (_abi.ShardStatsArgs, "sv_shard_stats_args"),
+                                       (_abi.ShardCombineArgs, "sv_shard_combine_args")])
 def test_argument_block_layout_matches_header(cls, cname):
     fields = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -188,3 +190,104 @@ def test_device_offset_must_be_aligned():
 def test_status_strings():
     for code in range(6):
         assert _abi.status_string(code)
+
+
+def good_shard(B=4, K=3, V=1000, off=200, cnt=300, mode=0):
+    L = _abi.library()
+    a = _abi.ShardStatsArgs()
+    a.B, a.k_max, a.V, a.col_offset, a.col_count, a.mode = B, K, V, off, cnt, mode
+    fake = 0x10000
+    a.target_shard = a.draft_shard = a.draft_tokens = fake
+    a.target_vec_stride = a.draft_vec_stride = V
+    a.partial, a.partial_bytes = fake, L.sv_shard_partial_bytes(B, K, cnt)
+    a.workspace, a.workspace_bytes = fake, L.sv_shard_workspace_bytes(B, K)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("col_offset", -1, _abi.SV_E_ARG), ("col_count", 0, _abi.SV_E_ARG),
+    ("col_offset", 701, _abi.SV_E_ARG),            # runs past V
+    ("mode", 2, _abi.SV_E_ARG), ("draft_shard", None, _abi.SV_E_ARG),
+    ("target_shard", None, _abi.SV_E_ARG), ("draft_tokens", None, _abi.SV_E_ARG),
+    ("draft_vec_stride", 299, _abi.SV_E_ARG), ("target_vec_stride", 299, _abi.SV_E_ARG),
+    ("partial", None, _abi.SV_E_WORKSPACE), ("workspace", None, _abi.SV_E_WORKSPACE),
+])
+def test_shard_stats_validation(field, value, code):
+    L = _abi.library()
+    assert L.sv_check_shard_stats_args(C.byref(good_shard())) == _abi.SV_OK
+    a = good_shard()
+    setattr(a, field, value)
+    assert L.sv_check_shard_stats_args(C.byref(a)) == code
+    d = good_shard(mode=1)                  # draft slots: no target, no tokens needed
+    d.target_shard = d.draft_tokens = None
+    assert L.sv_check_shard_stats_args(C.byref(d)) == _abi.SV_OK
+    s = good_shard()
+    s.partial_bytes -= 1
+    assert L.sv_check_shard_stats_args(C.byref(s)) == _abi.SV_E_WORKSPACE
+
+
+def test_shard_partial_size_follows_the_columns():
+    L = _abi.library()
+    # header and tiny values (288 B), then one 8-byte entry per possible
+    # distinct table word: at most min(columns, 5120)
+    assert L.sv_shard_partial_bytes(2, 1, 100) == 2 * 3 * (288 + 8 * 100)
+    assert L.sv_shard_partial_bytes(2, 1, 100000) == 2 * 3 * (288 + 8 * 5120)
+    assert L.sv_shard_partial_bytes(2, 0, 100) == 0
+    assert L.sv_shard_workspace_bytes(256, 6) >= 64 * 128
+
+
+def good_combine(B=4, K=3, V=1000, G=3, mode=0):
+    L = _abi.library()
+    c = _abi.ShardCombineArgs()
+    c.B, c.k_max, c.V, c.mode, c.G = B, K, V, mode, G
+    fake = 0x10000
+    bounds = _abi.shard_bounds(V, G)
+    for g, (off, cnt) in enumerate(bounds):
+        c.partials[g] = c.target_shards[g] = c.draft_shards[g] = fake
+        c.col_offset[g], c.col_count[g] = off, cnt
+        c.target_vec_stride[g] = c.draft_vec_stride[g] = V
+    c.draft_tokens = c.temperature = fake
+    c.workspace = fake
+    c.workspace_bytes = L.sv_verify_workspace_bytes(B, K, V, _abi.SV_BF16, 0)
+    return c
+
+
+def test_shard_combine_validation():
+    L = _abi.library()
+    chk = lambda c: L.sv_check_shard_combine_args(C.byref(c))
+    assert chk(good_combine()) == _abi.SV_OK
+    assert chk(good_combine(G=16, V=1000)) == _abi.SV_OK
+    c = good_combine()
+    c.G = 17
+    assert chk(c) == _abi.SV_E_ARG
+    c = good_combine()
+    c.col_offset[1] += 1                    # a gap between shards
+    assert chk(c) == _abi.SV_E_ARG
+    c = good_combine()
+    c.col_count[2] -= 1                     # the shards stop short of V
+    assert chk(c) == _abi.SV_E_ARG
+    c = good_combine()
+    c.partials[1] = None
+    assert chk(c) == _abi.SV_E_ARG
+    c = good_combine()
+    c.temperature = None
+    assert chk(c) == _abi.SV_E_ARG
+    c = good_combine()
+    c.workspace_bytes = 64
+    assert chk(c) == _abi.SV_E_WORKSPACE
+    d = good_combine(mode=1)
+    d.draft_tokens = None
+    for g in range(d.G):
+        d.target_shards[g] = None
+    assert chk(d) == _abi.SV_OK
+
+
+def test_shard_bounds_tile_the_vocabulary():
+    for V, G in ((151936, 8), (30, 3), (100, 7), (5, 5), (1000, 16)):
+        b = _abi.shard_bounds(V, G)
+        assert len(b) == G and b[0][0] == 0
+        assert all(b[g][0] + b[g][1] == b[g + 1][0] for g in range(G - 1))
+        assert b[-1][0] + b[-1][1] == V and all(c >= 1 for _, c in b)
+    with pytest.raises(ValueError):
+        _abi.shard_bounds(10, 17)
+
