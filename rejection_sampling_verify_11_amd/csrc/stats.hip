@@ -443,30 +443,53 @@ __device__ __forceinline__ void load_batch(uint4 (&d)[kBatch], const uint4* body
   for (int s = 0; s < kBatch; ++s) d[s] = body[min(i + s * kT, nb - 1)];
 }
 
-// Streams one vector into the table.  Full batches go through the fast path
-// unless a logit of the batch lies outside the window (a wave-uniform test);
-// the last, partial batch and the unaligned head and tail always go through
-// the slow path.  Batch k is counted while batch k + 1 loads.
-__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
-                                              uint32_t* tiny, Side& sd) {
+// The loads that open a vector: its unaligned head and tail logits (a lane
+// without one loads logit 0 and counts nothing) and the first batch of its
+// body.  The shard pass, whose vectors are short, issues them for the next
+// vector before the epilogue of the current one.
+struct VecStart {
+  const uint4* body;
+  int nb;
+  bool has_head, has_tail;
+  uint32_t xh, xt;
+  uint4 a[kBatch];
+};
+
+__device__ __forceinline__ void begin_vector(const uint16_t* vec, int V, VecStart& s) {
+  const int tid = threadIdx.x;
+  int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
+  if (head > V) head = V;
+  s.body = (const uint4*)(vec + head);
+  s.nb = (V - head) >> 3;
+  const int t0 = head + (s.nb << 3);
+  s.has_head = tid < head;
+  s.has_tail = t0 + tid < V;
+  s.xh = vec[s.has_head ? tid : 0];
+  s.xt = vec[s.has_tail ? t0 + tid : 0];
+  if (s.nb > 0) load_batch(s.a, s.body, tid, s.nb);
+}
+
+// Streams one vector, opened by begin_vector, into the table.  Full batches
+// go through the fast path unless a logit of the batch lies outside the
+// window (a wave-uniform test); the last, partial batch and the unaligned
+// head and tail always go through the slow path.  Batch k is counted while
+// batch k + 1 loads.
+__device__ __forceinline__ void stream_started(const VecStart& st, uint32_t* hist, uint32_t* tiny,
+                                               Side& sd) {
   const int tid = threadIdx.x;
   const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
   uint32_t* hbase = hist - kBase;
-  int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
-  if (head > V) head = V;
-  const uint4* body = (const uint4*)(vec + head);
-  const int nb = (V - head) >> 3;
-  const int t0 = head + (nb << 3);
-  // head and tail logits (a lane without one loads logit 0 and counts nothing)
-  const bool has_head = tid < head, has_tail = t0 + tid < V;
-  const uint32_t xh = vec[has_head ? tid : 0];
-  const uint32_t xt = vec[has_tail ? t0 + tid : 0];
+  const uint4* body = st.body;
+  const int nb = st.nb;
+  const bool has_head = st.has_head, has_tail = st.has_tail;
+  const uint32_t xh = st.xh, xt = st.xt;
   if (nb > 0) {
     const int step = kBatch * kT;
     const int nfull = nb / step;
     const bool part = nfull * step < nb;
     uint4 a[kBatch];
-    load_batch(a, body, tid, nb);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) a[q] = st.a[q];
     int i = tid;
     for (int k = 0; k < nfull; ++k) {
       uint4 n[kBatch];
@@ -508,6 +531,13 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
   } else {
     sd = count_pair_slow(hist, tiny, xh, has_head, xt, has_tail, spare, sd);
   }
+}
+
+__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
+                                              uint32_t* tiny, Side& sd) {
+  VecStart st;
+  begin_vector(vec, V, st);
+  stream_started(st, hist, tiny, sd);
 }
 
 // Vectors are handed out dynamically: a workgroup that finishes early takes
@@ -875,6 +905,8 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
   SlotP cur = slot_params<SHARD>(p, v);
+  VecStart st;  // the shard pass: the current vector's first loads
+  if constexpr (SHARD) begin_vector(cur.vec, V, st);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
@@ -895,7 +927,8 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     }
 
     Side sd;
-    stream_vector(cur.vec, V, hcopy, tiny, sd);
+    if constexpr (SHARD) stream_started(st, hcopy, tiny, sd);
+    else stream_vector(cur.vec, V, hcopy, tiny, sd);
     {
       const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nzero));
       const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nninf));
@@ -903,10 +936,14 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       if (l == 0) { sh.wzero[w] = z; sh.wninf[w] = n; sh.wflag[w] = f; }
     }
     __syncthreads();  // B1: table complete
-    const int in = sh.next;
+    int in = sh.next;
+    if constexpr (SHARD) in = __builtin_amdgcn_readfirstlane(in);  // the same in every thread
     const bool has_next = in < nitems;
     const int vn = has_next ? item_slot(p, in, (uint32_t)nitems, stride) : v;
     const SlotP nxt = slot_params<SHARD>(p, vn);  // loads in flight meanwhile
+    if constexpr (SHARD) {
+      if (has_next) begin_vector(nxt.vec, V, st);  // lands during the epilogue
+    }
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
     // and clears copy 1; largest +magnitude, smallest -magnitude present,
@@ -1044,57 +1081,94 @@ __global__ __launch_bounds__(kT, kWgPerCu) void shard_combine_kernel(CombinePara
   __shared__ __align__(16) uint32_t cneg[kWords];
   __shared__ double bins[kRankBins];
   __shared__ uint32_t tiny[1 + kTinyCap];
-  __shared__ ShardHead heads[kMaxShards];
+  __shared__ __align__(16) ShardHead heads[kMaxShards];
+  __shared__ uint32_t lstart[kMaxShards + 1], tstart[kMaxShards + 1];
+  __shared__ const uint2* lbase[kMaxShards];
   __shared__ double hist256[256];
   __shared__ Scratch<kWv> sc;
   const StatsParams& p = cp.sp;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int v = blockIdx.x;
+  const int G = cp.G;
+  // the shards' headers load while the slot's parameters do (a slot the
+  // call does not use has no partial: its header is read, not used)
+  uint4 h0 = make_uint4(0u, 0u, 0u, 0u), h1 = h0;  // ShardHead as two 16-byte words
+  if (tid < G) {
+    const uint4* hp = reinterpret_cast<const uint4*>(cp.part[tid] + (int64_t)v * cp.part_stride[tid]);
+    h0 = hp[0];
+    h1 = hp[1];
+  }
   const Slot s = slot_of(p, SV_BF16, v);
   if (!s.needed) return;
-  const int G = cp.G;
   uint4* pos4 = reinterpret_cast<uint4*>(cpos);
   uint4* neg4 = reinterpret_cast<uint4*>(cneg);
   for (int i = tid; i < kGroups; i += kT) {
     pos4[i] = make_uint4(0u, 0u, 0u, 0u);
     neg4[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  if (tid < G)
-    heads[tid] = *reinterpret_cast<const ShardHead*>(cp.part[tid] + (int64_t)v * cp.part_stride[tid]);
+  if (tid < G) {
+    reinterpret_cast<uint4*>(heads + tid)[0] = h0;
+    reinterpret_cast<uint4*>(heads + tid)[1] = h1;
+    lstart[tid + 1] = min(h1.z, (uint32_t)shard_list_cap(cp.col_len[tid]));  // nlist
+    tstart[tid + 1] = min(h1.y, (uint32_t)kShardTinyCap);                    // ntiny
+    lbase[tid] = reinterpret_cast<const uint2*>(cp.part[tid] + (int64_t)v * cp.part_stride[tid] +
+                                                kShardListOffset);
+  }
+  if (tid == 0) lstart[0] = tstart[0] = 0u;
   __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const uint8_t* base = cp.part[g] + (int64_t)v * cp.part_stride[g];
-    const uint2* list = reinterpret_cast<const uint2*>(base + kShardListOffset);
-    const uint32_t n = min(heads[g].nlist, (uint32_t)shard_list_cap(cp.col_len[g]));
-    for (uint32_t e = (uint32_t)tid; e < n; e += kT) {
-      const uint2 x = list[e];
-      if (x.x < (uint32_t)kWords) {
-        const uint32_t lo = x.y & 0xFFFFu, hi = x.y >> 16;
-        if (lo) __hip_atomic_fetch_add(cpos + x.x, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (hi) __hip_atomic_fetch_add(cneg + x.x, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (tid == 0)
+    for (int g = 0; g < G; ++g) {
+      lstart[g + 1] += lstart[g];
+      tstart[g + 1] += tstart[g];
+    }
+  __syncthreads();
+  // all shards' lists as one range of entries, eight per thread in flight
+  // before their adds (entry e is entry e - lstart[g] of shard g)
+  const uint32_t nent = lstart[G];
+  constexpr int kUnroll = 8;
+  for (uint32_t e0 = (uint32_t)tid; e0 < nent; e0 += kUnroll * kT) {
+    uint2 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = e0 + (uint32_t)(u * kT);
+      x[u] = make_uint2((uint32_t)kWords, 0u);
+      if (e < nent) {
+        int g = 0;
+        while (g + 1 < G && e >= lstart[g + 1]) ++g;
+        x[u] = lbase[g][e - lstart[g]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (x[u].x < (uint32_t)kWords) {
+        const uint32_t lo = x[u].y & 0xFFFFu, hi = x[u].y >> 16;
+        if (lo)
+          __hip_atomic_fetch_add(cpos + x[u].x, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (hi)
+          __hip_atomic_fetch_add(cneg + x[u].x, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   }
   uint32_t st = 0, Z = 0, NI = 0, NT = 0;
   int MP = -1, MN = 0x7FFFFFFF;
   for (int g = 0; g < G; ++g) {
-    const ShardHead& h = heads[g];
-    st |= h.status;
-    Z += h.zeros;
-    NI += h.ninf;
-    NT += h.ntiny;
-    MP = max(MP, h.maxpos);
-    MN = min(MN, h.minneg);
+    const ShardHead& hg = heads[g];
+    st |= hg.status;
+    Z += hg.zeros;
+    NI += hg.ninf;
+    NT += hg.ntiny;
+    MP = max(MP, hg.maxpos);
+    MN = min(MN, hg.minneg);
   }
-  if (w == 0) {  // the values below the window, in shard order
-    uint32_t o = 0;
-    for (int g = 0; g < G; ++g) {
-      const uint32_t n = min(heads[g].ntiny, (uint32_t)kShardTinyCap);
-      const uint32_t* t = reinterpret_cast<const uint32_t*>(
-          cp.part[g] + (int64_t)v * cp.part_stride[g] + sizeof(ShardHead));
-      if ((uint32_t)l < n && o + (uint32_t)l < (uint32_t)kTinyCap) tiny[1 + o + l] = t[l];
-      o += n;
-    }
+  // the values below the window, in shard order: lane l takes entry l of
+  // the concatenated lists (one load each)
+  const uint32_t ntl = tstart[G];
+  if (w == 0 && ntl > 0 && (uint32_t)l < min(ntl, (uint32_t)kTinyCap)) {
+    int g = 0;
+    while (g + 1 < G && (uint32_t)l >= tstart[g + 1]) ++g;
+    const uint32_t* t = reinterpret_cast<const uint32_t*>(
+        cp.part[g] + (int64_t)v * cp.part_stride[g] + sizeof(ShardHead));
+    tiny[1 + l] = t[l - tstart[g]];
   }
   __syncthreads();
   uint32_t gmask = 0;

@@ -107,8 +107,9 @@ constexpr size_t kShardListOffset = sizeof(ShardHead) + 4 * kShardTinyCap;  // 2
 inline __host__ __device__ int shard_list_cap(int32_t cols) {
   return cols < kTableWords ? cols : kTableWords;
 }
+// bytes per vector slot, a multiple of 16 (the header is read as 16-byte words)
 inline __host__ __device__ int64_t shard_part_stride(int32_t cols) {
-  return (int64_t)kShardListOffset + 8 * (int64_t)shard_list_cap(cols);
+  return ((int64_t)kShardListOffset + 8 * (int64_t)shard_list_cap(cols) + 15) / 16 * 16;
 }
 constexpr int kMaxShards = SV_MAX_SHARDS;
 
