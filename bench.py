@@ -162,30 +162,40 @@ def variant_legs(dev, sets, n):
 
 
 def sharded_leg(dev, sets, n):
-    """Vocabulary-sharded statistics on the bench batch, as 8 GPUs holding
-    18992 columns each would run them: one GPU's share is the pass over its
-    shard (sv_shard_stats, 1/8 of the logit bytes), then the merge of the
-    8 partials (sv_shard_combine) and the finalize on the merged records.
-    The shard passes are timed in turn over all 8 shards, so that no pass
-    finds its shard in the last-level cache; the whole chain (8 passes,
-    merge, finalize) runs here on one GPU and is timed as well."""
+    """Sampled verification of the bench batch with the vocabulary split into
+    8 shards of 18992 columns, as 8 GPUs behind a tensor-parallel LM head
+    would hold it.  One GPU's share is: the statistics pass over its shard
+    (sv_shard_stats, 1/8 of the logit bytes), the merge of the gathered
+    partials (sv_shard_combine; all 3328 vectors here, 1/8 of them each
+    when the GPUs split the merge), the masses of its columns at every
+    row's drawn position (sv_shard_draw_mass) and, after the exchange of
+    those masses, the draw of the rows whose token lies in its columns
+    (sv_shard_draw_locate).  The per-shard steps are timed in turn over all
+    8 shards, so that no launch finds its shard in the last-level cache; the
+    whole chain (8 of each, on one GPU) is timed as well."""
     import torch
     import rejection_sampling_verify_11_amd as sv
     inp, toks, _ = sets[0]
     B, K, V = inp.draft.shape
     G = 8
     sc = sv.ShardedCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p, None,
-                        G, seed=0, offset=0)
+                        G, seed=0, offset=0, sharded_draw=True)
     for _ in range(10):
         sc.run()
     torch.cuda.synchronize()
-    i = [0]
 
-    def one_shard():
-        sc.run_shard(i[0] % G)
-        i[0] += 1
+    def cycled(fn):
+        i = [0]
 
-    shard_ms = timed(one_shard, max(n, 2 * G), dev)
+        def step():
+            fn(i[0] % G)
+            i[0] += 1
+        return timed(step, max(n, 2 * G), dev)
+
+    shard_ms = cycled(sc.run_shard)
+    combine_ms = timed(sc.run_combine, n, dev)
+    mass_ms = cycled(lambda g: sc.run_draw(g, False))
+    locate_ms = cycled(lambda g: sc.run_draw(g, True))
     chain_ms = timed(sc.run, n, dev)
     sv.timing_enable(dev, True)
     for _ in range(10):
@@ -199,7 +209,8 @@ def sharded_leg(dev, sets, n):
     shard_bytes = B * (2 * K + 1) * cols * 2
     return {"workload": "B=256 k=6 V=151936 bf16 top-p 0.9 in 8 vocabulary shards of %d columns"
                         % cols,
-            "shard_pass_ms": shard_ms,
+            "per_shard_ms": {"stats": shard_ms, "draw_mass": mass_ms, "draw_locate": locate_ms},
+            "merge_all_vectors_ms": combine_ms,
             "shard_stats_gbs": shard_bytes / (kms["shard_stats"] * 1e-3) / 1e9,
             "one_gpu_chain_ms": chain_ms,
             "kernels_ms": kms}

@@ -377,6 +377,55 @@ typedef struct {
 sv_status sv_check_shard_combine_args(const sv_shard_combine_args* a);
 sv_status sv_shard_combine(sv_handle h, const sv_shard_combine_args* a, hipStream_t s);
 
+/* The draw of sampled verification over the same shards, in two steps per
+ * shard with an exchange between them.  After the acceptance scan (computed
+ * alike by every shard from the merged records), the drawn position a of
+ * row b needs y = min{j : C_j > u(b,a,1) R} over the whole vocabulary in
+ * token order ([SSD] §2.4, §4.3; [SD] §2.2):
+ *   sv_shard_draw_mass:   shard g writes masses[g][b] = {R_g, P_g}, the
+ *                         residual max(0, p'_a - q'_a) and p'_a summed over
+ *                         its columns (R_g = 0 for a bonus row);
+ *   (exchange: every shard needs every shard's masses -- an all-gather of
+ *    G x B x 16 bytes; on one GPU, one buffer written by all shards)
+ *   sv_shard_draw_locate: with R = sum of R_g (or of P_g for the bonus and
+ *                         for a zero residual), the shard whose running mass
+ *                         in shard order first passes u R draws the token
+ *                         from its own columns; every shard writes the row's
+ *                         other outputs, identically.
+ * Both read the records that sv_shard_combine (mode 0) wrote into
+ * `records`; outputs, seed, offset and flags are those of sv_verify_sample,
+ * whose results this reproduces (on one GPU: after every shard's locate). */
+typedef struct {
+  int32_t B, k_max, V;
+  int32_t col_offset, col_count;    /* this shard's columns                   */
+  int32_t G, shard;                 /* shard index in [0, G), G <= SV_MAX_SHARDS */
+  const void* target_shard;         /* bf16, layout as in sv_shard_stats_args */
+  int64_t target_vec_stride;
+  const void* draft_shard;
+  int64_t draft_vec_stride;
+  const int32_t* draft_tokens;      /* [B][k_max], global ids                 */
+  const int32_t* k_per_row;         /* [B] or NULL                            */
+  const float* temperature;         /* [B]                                    */
+  const float* top_p;               /* [B] or NULL                            */
+  uint64_t seed, offset;
+  const uint64_t* offset_dev;       /* as in sv_verify_args                   */
+  uint32_t flags;
+  const void* records;              /* the merged records: the verification
+                                       workspace sv_shard_combine wrote      */
+  size_t records_bytes;
+  double* masses;                   /* [G][B][2] exchange buffer              */
+  int32_t* out_tokens;              /* outputs as in sv_verify_args           */
+  int32_t* accepted;
+  int32_t* num_emitted;
+  float* p_at_draft;
+  float* q_at_draft;
+  int32_t* row_status;
+} sv_shard_draw_args;
+
+sv_status sv_check_shard_draw_args(const sv_shard_draw_args* a);
+sv_status sv_shard_draw_mass(sv_handle h, const sv_shard_draw_args* a, hipStream_t s);
+sv_status sv_shard_draw_locate(sv_handle h, const sv_shard_draw_args* a, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,13 +99,30 @@ class ShardCombineArgs(C.Structure):
     ]
 
 
+class ShardDrawArgs(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("k_max", C.c_int32), ("V", C.c_int32),
+        ("col_offset", C.c_int32), ("col_count", C.c_int32), ("G", C.c_int32),
+        ("shard", C.c_int32),
+        ("target_shard", _P), ("target_vec_stride", C.c_int64),
+        ("draft_shard", _P), ("draft_vec_stride", C.c_int64),
+        ("draft_tokens", _P), ("k_per_row", _P), ("temperature", _P), ("top_p", _P),
+        ("seed", C.c_uint64), ("offset", C.c_uint64), ("offset_dev", _P),
+        ("flags", C.c_uint32),
+        ("records", _P), ("records_bytes", C.c_size_t), ("masses", _P),
+        ("out_tokens", _P), ("accepted", _P), ("num_emitted", _P),
+        ("p_at_draft", _P), ("q_at_draft", _P), ("row_status", _P),
+    ]
+
+
 EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
            "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset",
            "sv_shard_partial_bytes", "sv_shard_workspace_bytes", "sv_check_shard_stats_args",
-           "sv_shard_stats", "sv_check_shard_combine_args", "sv_shard_combine")
+           "sv_shard_stats", "sv_check_shard_combine_args", "sv_shard_combine",
+           "sv_check_shard_draw_args", "sv_shard_draw_mass", "sv_shard_draw_locate")
 
 _lib = None
 _lock = threading.Lock()
@@ -164,6 +181,11 @@ def library():
                 L.sv_check_shard_combine_args.restype = C.c_int
                 L.sv_shard_combine.argtypes = [_P, C.POINTER(ShardCombineArgs), _P]
                 L.sv_shard_combine.restype = C.c_int
+                L.sv_check_shard_draw_args.argtypes = [C.POINTER(ShardDrawArgs)]
+                L.sv_check_shard_draw_args.restype = C.c_int
+                for f in (L.sv_shard_draw_mass, L.sv_shard_draw_locate):
+                    f.argtypes = [_P, C.POINTER(ShardDrawArgs), _P]
+                    f.restype = C.c_int
                 _lib = L
     return _lib
 
@@ -491,9 +513,11 @@ class ShardedCall:
     tiling [0, V)."""
 
     def __init__(self, mode, target, draft, draft_tokens=None, temperature=None, top_p=None,
-                 k_per_row=None, shards=8, seed=0, offset=0, flags=0):
+                 k_per_row=None, shards=8, seed=0, offset=0, flags=0, sharded_draw=False):
         if mode not in ("sample", "draft"):
             raise ValueError("mode must be 'sample' or 'draft'")
+        if sharded_draw and mode != "sample":
+            raise ValueError("the sharded draw is the verification's (mode 'sample')")
         if draft.dtype != torch.bfloat16:
             raise TypeError("sharded statistics take bf16 logits")
         self.call = VerifyCall(mode, target, draft, draft_tokens, temperature, top_p, k_per_row,
@@ -541,6 +565,26 @@ class ShardedCall:
         self.outputs = self.call.outputs
         self.device = dev
         self._h = handle(dev)
+        self.sharded_draw = sharded_draw
+        self.draw_args = []
+        if sharded_draw:
+            G = len(self.bounds)
+            self.masses = torch.zeros((G, max(B, 1), 2), dtype=torch.float64, device=dev)
+            for g, (off, cnt) in enumerate(self.bounds):
+                sa = self.shard_args[g]
+                d = ShardDrawArgs()
+                d.B, d.k_max, d.V, d.col_offset, d.col_count, d.G, d.shard = B, K, V, off, cnt, G, g
+                d.target_shard, d.target_vec_stride = sa.target_shard, sa.target_vec_stride
+                d.draft_shard, d.draft_vec_stride = sa.draft_shard, sa.draft_vec_stride
+                d.draft_tokens, d.k_per_row = va.draft_tokens, va.k_per_row
+                d.temperature, d.top_p = va.temperature, va.top_p
+                d.seed, d.offset, d.offset_dev, d.flags = va.seed, va.offset, va.offset_dev, int(flags)
+                d.records, d.records_bytes = va.workspace, va.workspace_bytes
+                d.masses = self.masses.data_ptr()
+                for f in ("out_tokens", "accepted", "num_emitted", "p_at_draft", "q_at_draft",
+                          "row_status"):
+                    setattr(d, f, getattr(va, f))
+                self.draw_args.append(d)
 
     def run_shard(self, g, stream=None):
         """The pass over shard g alone (one GPU's share of the work)."""
@@ -555,18 +599,32 @@ class ShardedCall:
         if rc != SV_OK:
             raise SpecVerifyError("sv_shard_combine", rc)
 
+    def run_draw(self, g, locate, stream=None):
+        """Shard g's part of the draw: its masses, or (locate) its token."""
+        f = library().sv_shard_draw_locate if locate else library().sv_shard_draw_mass
+        rc = f(self._h, C.byref(self.draw_args[g]), _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_shard_draw", rc)
+
     def run(self, stream=None):
         for g in range(len(self.bounds)):
             self.run_shard(g, stream)
         self.run_combine(stream)
-        return self.call.run(stream)
+        if not self.sharded_draw:
+            return self.call.run(stream)
+        for g in range(len(self.bounds)):
+            self.run_draw(g, False, stream)
+        for g in range(len(self.bounds)):
+            self.run_draw(g, True, stream)
+        return self.outputs
 
 
 def verify_sample_sharded(target, draft, draft_tokens, temperature, top_p=None, k_per_row=None,
-                          shards=8, seed=0, offset=0, flags=0, stream=None):
-    """verify_sample with the statistics computed shard by shard and merged."""
+                          shards=8, seed=0, offset=0, flags=0, sharded_draw=True, stream=None):
+    """verify_sample with the statistics computed shard by shard and merged,
+    and (sharded_draw) the draw split over the shards as well."""
     return ShardedCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
-                       shards, seed, offset, flags).run(stream)
+                       shards, seed, offset, flags, sharded_draw).run(stream)
 
 
 def draft_sample_sharded(draft, temperature, top_p=None, k_per_row=None, shards=8, seed=0,

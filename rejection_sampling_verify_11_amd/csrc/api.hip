@@ -518,3 +518,69 @@ sv_status sv_shard_combine(sv_handle h, const sv_shard_combine_args* a, hipStrea
   return SV_OK;
 }
 
+sv_status sv_check_shard_draw_args(const sv_shard_draw_args* a) {
+  if (!a) return SV_E_ARG;
+  if (a->B < 0 || a->k_max < 1 || a->k_max > SV_MAX_K || a->V < 1 || a->V > kMaxVSampled)
+    return SV_E_ARG;
+  if (a->G < 1 || a->G > SV_MAX_SHARDS || a->shard < 0 || a->shard >= a->G) return SV_E_ARG;
+  if (a->col_offset < 0 || a->col_count < 1 || (int64_t)a->col_offset + a->col_count > a->V)
+    return SV_E_ARG;
+  if ((uintptr_t)a->offset_dev & 7) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (!a->target_shard || !a->draft_shard || !a->draft_tokens || !a->temperature ||
+      !a->masses || !a->out_tokens || !a->accepted)
+    return SV_E_ARG;
+  if (a->target_vec_stride < a->col_count || a->draft_vec_stride < a->col_count) return SV_E_ARG;
+  if (!a->records || a->records_bytes < sample_ws(a->B, a->k_max)) return SV_E_WORKSPACE;
+  return SV_OK;
+}
+
+static sv_status shard_draw(sv_handle h, const sv_shard_draw_args* a, bool locate, hipStream_t s) {
+  const sv_status st = sv_check_shard_draw_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  sv::FinalizeParams f;
+  memset(&f, 0, sizeof(f));
+  f.tokens = a->draft_tokens;
+  f.k_per_row = a->k_per_row;
+  f.temperature = a->temperature;
+  f.top_p = a->top_p;
+  f.B = a->B;
+  f.K = a->k_max;
+  f.V = a->V;
+  f.dtype = SV_BF16;
+  f.flags = a->flags;
+  f.seed = a->seed;
+  f.offset = a->offset;
+  f.offset_dev = a->offset_dev;
+  f.recs = (const sv::VecRec*)a->records;
+  f.out_tokens = a->out_tokens;
+  f.accepted = a->accepted;
+  f.num_emitted = a->num_emitted;
+  f.p_at_draft = a->p_at_draft;
+  f.q_at_draft = a->q_at_draft;
+  f.row_status = a->row_status;
+  sv::ShardDrawParams d;
+  d.tgt = a->target_shard;
+  d.dft = a->draft_shard;
+  d.ts = a->target_vec_stride;
+  d.ds = a->draft_vec_stride;
+  d.col_off = a->col_offset;
+  d.col_len = a->col_count;
+  d.G = a->G;
+  d.shard = a->shard;
+  d.masses = a->masses;
+  if (sv::launch_shard_draw(f, d, locate, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_shard_draw_mass(sv_handle h, const sv_shard_draw_args* a, hipStream_t s) {
+  return shard_draw(h, a, false, s);
+}
+
+sv_status sv_shard_draw_locate(sv_handle h, const sv_shard_draw_args* a, hipStream_t s) {
+  return shard_draw(h, a, true, s);
+}
+

@@ -351,14 +351,16 @@ __device__ __forceinline__ int group_crossing(const double* seg, double target, 
 // caller then retries on p' alone, for MODE 0) or the distribution is empty.
 //
 // MODE 0 reads the whole vector: R, the residual's mass, is known only at
-// the end.  MODE 1 stops after the group in which the running mass passes
-// u (R = 1 up to rounding); the wave that holds the crossing segment in its
-// registers locates the token without reading it again.  At a rounding edge
-// (the running mass never passes u) it falls back to the scan over all
-// segment sums with R their total, as MODE 0 does.
+// the end.  MODE 1 knows its mass before it starts -- `scale`: 1 for a
+// whole normalised p', a shard's own mass for the part of p' it holds -- and
+// stops after the group in which the running mass passes u * scale; the wave
+// that holds the crossing segment in its registers locates the token without
+// reading it again.  At a rounding edge (the running mass never passes
+// u * scale) it falls back to the scan over all segment sums with R their
+// total, as MODE 0 does.
 template <int MODE, int PASS, int NT>
 __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, int V, double u,
-                                              CdfScratch<NT>& sc) {
+                                              double scale, CdfScratch<NT>& sc) {
   constexpr int kWaves = NT / 64, kGroupTok = kWaves * Seg<MODE>::tok;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Pv = (const uint16_t*)P.vec;
@@ -379,7 +381,7 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
       pass1_segment<MODE, PASS>(P, Q, ca, G * kWaves + w, nchunks, sc.seg, list);
       if (MODE == 1) {
         __syncthreads();
-        hw = group_crossing<kWaves>(sc.seg + G * kWaves, u, cum, before);
+        hw = group_crossing<kWaves>(sc.seg + G * kWaves, u * scale, cum, before);
         gx = G;
         if (hw >= 0) break;
       }
@@ -388,7 +390,7 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
       pass1_segment<MODE, PASS>(P, Q, cb, (G + 1) * kWaves + w, nchunks, sc.seg, list);
       if (MODE == 1) {
         __syncthreads();
-        hw = group_crossing<kWaves>(sc.seg + (G + 1) * kWaves, u, cum, before);
+        hw = group_crossing<kWaves>(sc.seg + (G + 1) * kWaves, u * scale, cum, before);
         gx = G + 1;
         if (hw >= 0) break;
       }
@@ -400,7 +402,8 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
         const bool odd = (gx & 1) != 0;
 #pragma unroll
         for (int i = 0; i < Seg<MODE>::cps; ++i) c.p[i] = odd ? cb.p[i] : ca.p[i];
-        const int y = locate_in_segment<MODE>(P, Q, c, gx * kWaves + w, nchunks, before, u);
+        const int y =
+            locate_in_segment<MODE>(P, Q, c, gx * kWaves + w, nchunks, before, u * scale);
         if (l == 0) sc.y = y;
       }
       __syncthreads();
@@ -462,7 +465,7 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
 // distribution is empty.  *zero_residual reports the fallback.
 template <int NT>
 __device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
-                           CdfScratch<NT>& sc, bool* zero_residual) {
+                           CdfScratch<NT>& sc, bool* zero_residual, double scale = 1.0) {
   constexpr int kThreads = NT, kWaves = NT / 64, kTile = NT * 8;
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
       (mode == 1 || is_aligned16(Q.vec))) {
@@ -470,15 +473,15 @@ __device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mod
     // the same in every thread
     const bool cutp = P.tau > -INFINITY, cutq = Q.tau > -INFINITY;
     if (mode == 0) {
-      const int y = cutp ? inverse_cdf_bf16<0, kPassListed, NT>(P, Q, V, u, sc)
-                  : cutq ? inverse_cdf_bf16<0, kPassCutQ, NT>(P, Q, V, u, sc)
-                         : inverse_cdf_bf16<0, kPassUncut, NT>(P, Q, V, u, sc);
+      const int y = cutp ? inverse_cdf_bf16<0, kPassListed, NT>(P, Q, V, u, 1.0, sc)
+                  : cutq ? inverse_cdf_bf16<0, kPassCutQ, NT>(P, Q, V, u, 1.0, sc)
+                         : inverse_cdf_bf16<0, kPassUncut, NT>(P, Q, V, u, 1.0, sc);
       if (y >= 0) return y;
       // R == 0: the residual vanishes identically; draw from p' instead
       *zero_residual = true;
     }
-    return cutp ? inverse_cdf_bf16<1, kPassCutP, NT>(P, P, V, u, sc)
-                : inverse_cdf_bf16<1, kPassUncut, NT>(P, P, V, u, sc);
+    return cutp ? inverse_cdf_bf16<1, kPassCutP, NT>(P, P, V, u, scale, sc)
+                : inverse_cdf_bf16<1, kPassUncut, NT>(P, P, V, u, scale, sc);
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = (V + kTile - 1) / kTile;
@@ -636,22 +639,20 @@ struct RowShared {
   double pinv, qinv;
 };
 
-template <int NT>
-__global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
-  __shared__ CdfScratch<NT> sc;
-  __shared__ RowShared rs;
-  const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
-  const int per = slots_per_row(K);
-  const VecRec* recs = p.recs + (int64_t)b * per;
-  // Row header by wave 0, one lane per position: checks, ratios, uniforms;
-  // the first rejection is the lowest lane that rejects.  Every load is
-  // issued up front -- lane l reads the draft token and the target and draft
-  // records of position l whatever k_b is, and k_b masks them afterwards --
-  // so the header waits for memory once.  The lane keeps its token for the
-  // output row.
+// Row header by wave 0 (every thread calls it), one lane per position:
+// checks, ratios, uniforms; the first rejection is the lowest lane that
+// rejects.  Every load is issued up front -- lane l reads the draft token and
+// the target and draft records of position l whatever k_b is, and k_b masks
+// them afterwards -- so the header waits for memory once.  Fills rs; with
+// OUT, also writes p'(x_i), q'(x_i) and a flagged row's outputs.  Returns the
+// lane's draft token (lanes of wave 0), for the output row.
+template <bool OUT>
+__device__ __forceinline__ int row_header(const FinalizeParams& p, int b, RowShared& rs) {
   int x = 0;
-  if (tid < 64) {
-    const int l = tid;
+  if (threadIdx.x < 64) {
+    const int K = p.K, V = p.V;
+    const VecRec* recs = p.recs + (int64_t)b * slots_per_row(K);
+    const int l = threadIdx.x;
     const int kb = p.k_per_row ? p.k_per_row[b] : K;
     const float T = p.temperature[b];
     const float P = p.top_p ? p.top_p[b] : 1.0f;
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       }
       const uint64_t rm = __ballot(rej);
       acc = rm ? __builtin_ctzll(rm) : kb;
-      if (l < K) {
+      if (OUT && l < K) {
         if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + l] = l < kb ? (float)px : 0.0f;
         if (p.q_at_draft) p.q_at_draft[(int64_t)b * K + l] = l < kb ? (float)qx : 0.0f;
       }
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
         rs.qtau = rd.tau;
         rs.qinv = rd.inv_kept;
       }
-    } else {
+    } else if (OUT) {
       if (l <= K) p.out_tokens[(int64_t)b * (K + 1) + l] = -1;
       if (l < K) {
         if (p.p_at_draft) p.p_at_draft[(int64_t)b * K + l] = NAN;
@@ -721,6 +722,15 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       rs.u1 = uniform24(p.seed, (uint64_t)b, (uint64_t)acc, 1, off);
     }
   }
+  return x;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
+  __shared__ CdfScratch<NT> sc;
+  __shared__ RowShared rs;
+  const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
+  const int x = row_header<true>(p, b, rs);
   __syncthreads();
   if (!rs.go) return;
   const int acc = rs.acc, mode = rs.mode;
@@ -795,6 +805,165 @@ __global__ __launch_bounds__(NT) void draft_sample_kernel(FinalizeParams p) {
   if (tid == 0) p.draft_out[(int64_t)b * K + i] = y;
 }
 
+// ---- vocabulary-sharded draw
+// Shard g holds columns [col_off, col_off + col_len) of every vector, and the
+// records are the merged ones.  The draw takes two launches per shard with an
+// exchange between them:
+//   mass:   over its own columns of the drawn position, each shard sums the
+//           residual max(0, p' - q') and p' (masses[g][b] = {R_g, P_g});
+//   locate: with every shard's masses, each finds the shard whose running
+//           mass, in shard order, first passes u R -- R the sum of the R_g,
+//           or of the P_g for the bonus and for a zero residual ([SSD] §4.3)
+//           -- and that shard alone draws the token from its columns, with
+//           the target u R less the mass of the shards before it.
+// Every shard writes the same row outputs; the drawn token comes from the
+// shard that holds it.
+
+// Sums over n columns of the residual (mode 0) and of p', four 8-token chunks
+// per thread in flight; fp32 within a chunk, fp64 across chunks and threads.
+template <int NT>
+__device__ __forceinline__ void column_masses(const Dist& P, const Dist& Q, int mode, int dtype,
+                                              int n, double* red, double* rsum, double* psum) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const bool aligned = is_aligned16(P.vec) && (mode == 1 || is_aligned16(Q.vec));
+  double r = 0.0, q = 0.0;
+  constexpr int kU = 4;
+  for (int64_t j0 = 8 * (int64_t)tid; j0 < n; j0 += 8 * (int64_t)NT * kU) {
+    float zp[kU][8], zq[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t j = j0 + 8 * (int64_t)NT * u;
+      load8(P.vec, dtype, j, n, aligned, zp[u]);  // past n: -inf, mass 0
+      if (mode == 0) load8(Q.vec, dtype, j, n, aligned, zq[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float cr = 0.0f, cp = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float pp = prob_f(P, zp[u][t]);
+        cp += pp;
+        if (mode == 0) cr += fmaxf(pp - prob_f(Q, zq[u][t]), 0.0f);
+      }
+      r += cr;
+      q += cp;
+    }
+  }
+  r = wave_last_f64(wave_scan_add_f64(r));
+  q = wave_last_f64(wave_scan_add_f64(q));
+  if (l == 0) {
+    red[2 * w] = r;
+    red[2 * w + 1] = q;
+  }
+  __syncthreads();
+  double a = 0.0, c = 0.0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    a += red[2 * k];
+    c += red[2 * k + 1];
+  }
+  *rsum = a;
+  *psum = c;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void shard_mass_kernel(FinalizeParams p, ShardDrawParams d) {
+  __shared__ RowShared rs;
+  __shared__ double red[2 * (NT / 64)];
+  const int b = blockIdx.x, K = p.K;
+  row_header<false>(p, b, rs);
+  __syncthreads();
+  double* out = d.masses + ((int64_t)d.shard * p.B + b) * 2;
+  if (!rs.go) {
+    if (threadIdx.x == 0) out[0] = out[1] = 0.0;
+    return;
+  }
+  const int acc = rs.acc, mode = rs.mode;
+  const Dist P = make_dist(d.tgt, (int64_t)b * (K + 1) + acc, d.ts, p.dtype, rs.pm, rs.ptau,
+                           rs.pinv, rs.T);
+  Dist Q = P;
+  if (mode == 0)
+    Q = make_dist(d.dft, (int64_t)b * K + acc, d.ds, p.dtype, rs.qm, rs.qtau, rs.qinv, rs.T);
+  double rsum, psum;
+  column_masses<NT>(P, Q, mode, p.dtype, d.col_len, red, &rsum, &psum);
+  if (threadIdx.x == 0) {
+    out[0] = mode == 0 ? rsum : 0.0;
+    out[1] = psum;
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void shard_locate_kernel(FinalizeParams p, ShardDrawParams d) {
+  __shared__ CdfScratch<NT> sc;
+  __shared__ RowShared rs;
+  __shared__ double ms[kMaxShards][2];
+  const int b = blockIdx.x, K = p.K, tid = threadIdx.x;
+  if (tid < d.G) {
+    const double* m = d.masses + ((int64_t)tid * p.B + b) * 2;
+    ms[tid][0] = m[0];
+    ms[tid][1] = m[1];
+  }
+  const int x = row_header<true>(p, b, rs);
+  __syncthreads();
+  if (!rs.go) return;
+  const int acc = rs.acc;
+  // the total and the owner, the same in every thread (LDS, shard order)
+  double R = 0.0;
+  for (int g = 0; g < d.G; ++g) R += ms[g][0];
+  int mode = rs.mode;
+  if (mode == 0 && !(R > 0.0)) mode = 1;  // a zero residual: draw from p'
+  const int side = mode == 0 ? 0 : 1;
+  if (side == 1) {
+    R = 0.0;
+    for (int g = 0; g < d.G; ++g) R += ms[g][1];
+  }
+  const double target = rs.u1 * R;
+  int owner = -1, lastm = -1;
+  double before = 0.0, before_last = 0.0, run = 0.0;
+  for (int g = 0; g < d.G; ++g) {
+    const double m = ms[g][side];
+    if (m > 0.0) {
+      if (owner < 0 && run + m > target) {
+        owner = g;
+        before = run;
+      }
+      lastm = g;
+      before_last = run;
+    }
+    run += m;
+  }
+  if (owner < 0) {  // rounding edge: the last shard with mass
+    owner = lastm;
+    before = before_last;
+  }
+  int y = -1;  // no mass at all: an empty distribution
+  if (owner == d.shard) {
+    const Dist P = make_dist(d.tgt, (int64_t)b * (K + 1) + acc, d.ts, p.dtype, rs.pm, rs.ptau,
+                             rs.pinv, rs.T);
+    Dist Q = P;
+    if (mode == 0)
+      Q = make_dist(d.dft, (int64_t)b * K + acc, d.ds, p.dtype, rs.qm, rs.qtau, rs.qinv, rs.T);
+    const double m = ms[owner][side];
+    bool zero = false;
+    // u' m is the target less the mass of the shards before this one
+    const int yl = inverse_cdf(P, Q, mode, p.dtype, d.col_len, (target - before) / m, sc, &zero, m);
+    y = yl >= 0 ? d.col_off + yl : -1;
+  }
+  const bool writes_y = owner == d.shard || (owner < 0 && d.shard == 0);
+  if (tid < 64) {
+    const int l = tid;
+    if (l <= K && (l != acc || writes_y)) {
+      const int32_t v = l < acc ? x : l == acc ? y : -1;
+      p.out_tokens[(int64_t)b * (K + 1) + l] = v;
+    }
+    if (l == 0) {
+      p.accepted[b] = acc;
+      if (p.num_emitted) p.num_emitted[b] = acc + 1;
+      if (p.row_status) p.row_status[b] = 0;
+    }
+  }
+}
+
 }  // namespace
 
 // 512-thread workgroups when there are at least two per CU.
@@ -821,6 +990,26 @@ hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t
     hipLaunchKernelGGL(draft_sample_kernel<512>, dim3(n), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL(draft_sample_kernel<1024>, dim3(n), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_draw(const FinalizeParams& p, const ShardDrawParams& d, bool locate,
+                             int num_cus, hipStream_t s, Timer* t) {
+  if (p.B == 0) return hipSuccess;
+  const bool half = use_half_blocks((unsigned)p.B, num_cus);
+  if (locate) {
+    TimedScope ts(t, "shard_locate", s);
+    if (half)
+      hipLaunchKernelGGL(shard_locate_kernel<512>, dim3(p.B), dim3(512), 0, s, p, d);
+    else
+      hipLaunchKernelGGL(shard_locate_kernel<1024>, dim3(p.B), dim3(1024), 0, s, p, d);
+  } else {
+    TimedScope ts(t, "shard_mass", s);
+    if (half)
+      hipLaunchKernelGGL(shard_mass_kernel<512>, dim3(p.B), dim3(512), 0, s, p, d);
+    else
+      hipLaunchKernelGGL(shard_mass_kernel<1024>, dim3(p.B), dim3(1024), 0, s, p, d);
+  }
   return hipGetLastError();
 }
 

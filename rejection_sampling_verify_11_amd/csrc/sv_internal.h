@@ -183,6 +183,16 @@ struct RollbackParams {
   RollRec* recs;
 };
 
+// One shard's part of the draw: its columns of every vector, and the
+// exchange buffer of all shards' per-row masses.
+struct ShardDrawParams {
+  const void* tgt;
+  const void* dft;
+  int64_t ts, ds;
+  int32_t col_off, col_len, G, shard;
+  double* masses;  // [G][B][2]: residual mass, p' mass of the drawn position
+};
+
 struct DynkParams {
   int32_t B, W, k_min, k_max, up_num, up_den, down_num, down_den;
   const int32_t* accepted;
@@ -215,6 +225,8 @@ hipError_t launch_shard_stats(const StatsParams& p, int num_cus, hipStream_t s, 
 hipError_t launch_shard_combine(const CombineParams& p, hipStream_t s, Timer* t);
 hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
+hipError_t launch_shard_draw(const FinalizeParams& p, const ShardDrawParams& d, bool locate,
+                             int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
 hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t);

@@ -57,7 +57,8 @@ def _c_layout(struct, fields):
                                        (_abi.RollbackArgs, "sv_rollback_args"),
                                        (_abi.DynkArgs, "sv_dynk_args"),
                                        (_abi.ShardStatsArgs, "sv_shard_stats_args"),
-                                       (_abi.ShardCombineArgs, "sv_shard_combine_args")])
+                                       (_abi.ShardCombineArgs, "sv_shard_combine_args"),
+                                       (_abi.ShardDrawArgs, "sv_shard_draw_args")])
 def test_argument_block_layout_matches_header(cls, cname):
     fields = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -290,4 +291,35 @@ def test_shard_bounds_tile_the_vocabulary():
         assert b[-1][0] + b[-1][1] == V and all(c >= 1 for _, c in b)
     with pytest.raises(ValueError):
         _abi.shard_bounds(10, 17)
+
+
+def good_draw(B=4, K=3, V=1000, off=200, cnt=300, G=3, shard=1):
+    L = _abi.library()
+    d = _abi.ShardDrawArgs()
+    d.B, d.k_max, d.V, d.col_offset, d.col_count, d.G, d.shard = B, K, V, off, cnt, G, shard
+    fake = 0x10000
+    d.target_shard = d.draft_shard = d.draft_tokens = d.temperature = fake
+    d.masses = d.out_tokens = d.accepted = fake
+    d.target_vec_stride = d.draft_vec_stride = V
+    d.records = fake
+    d.records_bytes = L.sv_verify_workspace_bytes(B, K, V, _abi.SV_BF16, 0)
+    return d
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("shard", 3, _abi.SV_E_ARG), ("shard", -1, _abi.SV_E_ARG), ("G", 17, _abi.SV_E_ARG),
+    ("col_count", 801, _abi.SV_E_ARG), ("masses", None, _abi.SV_E_ARG),
+    ("target_shard", None, _abi.SV_E_ARG), ("draft_tokens", None, _abi.SV_E_ARG),
+    ("out_tokens", None, _abi.SV_E_ARG), ("draft_vec_stride", 299, _abi.SV_E_ARG),
+    ("offset_dev", 0x10004, _abi.SV_E_ARG), ("records", None, _abi.SV_E_WORKSPACE),
+    ("records_bytes", 64, _abi.SV_E_WORKSPACE),
+])
+def test_shard_draw_validation(field, value, code):
+    L = _abi.library()
+    assert L.sv_check_shard_draw_args(C.byref(good_draw())) == _abi.SV_OK
+    d = good_draw()
+    setattr(d, field, value)
+    assert L.sv_check_shard_draw_args(C.byref(d)) == code
+    for fn in (L.sv_shard_draw_mass, L.sv_shard_draw_locate):
+        assert fn(None, C.byref(good_draw()), None) == _abi.SV_E_ARG  # no handle
 

@@ -24,13 +24,13 @@ def records(call, B, K):
     return call.workspace[:n].view(B * (2 * K + 1), 32).cpu().numpy()
 
 
-def sharded_and_plain(inp, toks, shards, seed=3, offset=1, flags=0):
+def sharded_and_plain(inp, toks, shards, seed=3, offset=1, flags=0, sharded_draw=False):
     d = to_dev(inp)
     t = torch.as_tensor(toks, dtype=torch.int32).to(DEV)
     plain = sv.VerifyCall("sample", d.target, d.draft, t, d.temperature, d.top_p, d.k_per_row,
                           seed, offset, flags)
     shard = sv.ShardedCall("sample", d.target, d.draft, t, d.temperature, d.top_p, d.k_per_row,
-                           shards, seed, offset, flags)
+                           shards, seed, offset, flags, sharded_draw)
     po = plain.run()
     so = shard.run()
     torch.cuda.synchronize()
@@ -77,10 +77,11 @@ def test_random_shardings_match_the_oracle(oracle, case):
     kk = None if rng.random() < 0.5 else torch.from_numpy(rng.integers(1, K + 1, B).astype(np.int32))
     inp = W.SampleInputs(zt, zd, T, P, kk)
     toks = oracle_tokens(oracle, inp, 8, case, flags)
-    plain, po, shard, so = sharded_and_plain(inp, toks, shards, 8, case, flags)
+    sharded_draw = case % 2 == 1
+    plain, po, shard, so = sharded_and_plain(inp, toks, shards, 8, case, flags, sharded_draw)
     rep = compare_sample(so, oracle_verify(oracle, inp, toks, 8, case, flags), kk, K)
     assert rep.excused_mismatches <= 1
-    for k in po:                  # the same records, so the same outputs
+    for k in po:  # the same records (and draws up to rounding order), so the same outputs
         assert torch.equal(po[k], so[k]), k
 
 
@@ -139,3 +140,55 @@ def test_vectors_the_table_cannot_hold(oracle):
     for k in po:
         a, b = po[k][same].float(), so[k][same].float()
         assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b)), k
+
+
+@pytest.mark.parametrize("shards", [1, 2, 3, 8, 16])
+def test_sharded_draw(oracle, shards):
+    """The draw split over the shards (each sums its columns' residual and p'
+    masses; the shard holding u R draws from its own columns) on the bench
+    logits: the same outputs as the unsharded call, and the oracle's."""
+    inp = W.workload4(5, B=8)
+    toks = oracle_tokens(oracle, inp, 6, 2)
+    plain, po, shard, so = sharded_and_plain(inp, toks, shards, 6, 2, sharded_draw=True)
+    for k in po:
+        assert torch.equal(po[k], so[k]), k
+    rep = compare_sample(so, oracle_verify(oracle, inp, toks, 6, 2), None, inp.draft.shape[1])
+    assert rep.excused_mismatches <= 1
+    assert shard.masses.sum().item() > 0
+
+
+def test_sharded_draw_degenerate_rows(oracle):
+    """q = p (every draft accepted: the bonus from p'), disjoint supports
+    (every first draft rejected), a zero residual (the draw falls back to p'
+    across shards), mass only in the last shard, and a row error, over 5
+    unaligned shards."""
+    V, B = 4096, 10
+    g = torch.Generator().manual_seed(21)
+    zt = torch.randn((B, 3, V), generator=g) * 2
+    zd = zt[:, :2].clone()                                   # rows 0-1: q = p
+    zt[2:4, :, : V // 2] = float("-inf")                     # rows 2-3: disjoint supports
+    zd[2:4, :, V // 2:] = float("-inf")
+    zd[4:6] = zt[4:6, :2]                                    # rows 4-5: zero residual
+    zt[4:6, :, 7] = zd[4:6, :, 7] = float("-inf")
+    zt[6:8, :, : V - 100] = float("-inf")                    # rows 6-7: target mass at the end
+    zt[8, 0, 3] = float("nan")                               # row 8: an error
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.ones(B), None)
+    toks = np.zeros((B, 2), np.int32)
+    ok = [0, 1, 2, 3, 6, 7, 9]
+    sub = W.SampleInputs(inp.target[ok], inp.draft[ok], inp.temperature[ok], None)
+    toks[ok] = oracle_tokens(oracle, sub, 9, 0)
+    toks[4:6] = 7                                            # outside both supports: rejected
+    toks[8] = 0
+    shards = [(0, 999), (999, 1), (1000, 1501), (2501, 1000), (3501, 595)]
+    plain, po, shard, so = sharded_and_plain(inp, toks, shards, 9, 0, sharded_draw=True)
+    st = so["row_status"].cpu().numpy()
+    assert st[8] & sv.ROW_NONFINITE_LOGIT and np.all(np.delete(st, 8) == 0)
+    for k in po:
+        a, b = torch.nan_to_num(po[k].float()), torch.nan_to_num(so[k].float())
+        assert torch.equal(a, b), k
+    acc = so["accepted"].cpu().numpy()
+    assert np.all(acc[[0, 1]] == 2) and np.all(acc[[2, 3, 4, 5]] == 0)
+    rows = [r for r in range(B) if r != 8]
+    rep = compare_sample(so, oracle_verify(oracle, inp, toks, 9, 0, rows=rows), None, 2, rows=rows)
+    assert rep.excused_mismatches == 0
+
