@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the greedy and round legs")
+    ap.add_argument("--leg", choices=("greedy", "round", "variants", "sharded"),
+                    help="run only this extra leg on the bench inputs and print its JSON (for "
+                         "profiling one leg); no headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -311,6 +314,14 @@ def main():
                              None, seed=0, offset=0)
         sets.append((inp, toks, call))
     torch.cuda.synchronize()
+
+    if args.leg:
+        n = args.steps
+        leg = {"greedy": lambda: greedy_leg(dev, n), "round": lambda: round_leg(dev, n),
+               "variants": lambda: variant_legs(dev, sets, min(n, 50)),
+               "sharded": lambda: sharded_leg(dev, sets, min(n, 50))}[args.leg]()
+        print(json.dumps({"leg": args.leg, "result": leg}))
+        return
 
     # rollback state: contexts U[4096, 8192] plus the k+1 slots this round wrote
     rows = W.workload5_rows(0, B=B, ctx_lo=4096, ctx_hi=8192)
