@@ -443,53 +443,30 @@ __device__ __forceinline__ void load_batch(uint4 (&d)[kBatch], const uint4* body
   for (int s = 0; s < kBatch; ++s) d[s] = body[min(i + s * kT, nb - 1)];
 }
 
-// The loads that open a vector: its unaligned head and tail logits (a lane
-// without one loads logit 0 and counts nothing) and the first batch of its
-// body.  The shard pass, whose vectors are short, issues them for the next
-// vector before the epilogue of the current one.
-struct VecStart {
-  const uint4* body;
-  int nb;
-  bool has_head, has_tail;
-  uint32_t xh, xt;
-  uint4 a[kBatch];
-};
-
-__device__ __forceinline__ void begin_vector(const uint16_t* vec, int V, VecStart& s) {
-  const int tid = threadIdx.x;
-  int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
-  if (head > V) head = V;
-  s.body = (const uint4*)(vec + head);
-  s.nb = (V - head) >> 3;
-  const int t0 = head + (s.nb << 3);
-  s.has_head = tid < head;
-  s.has_tail = t0 + tid < V;
-  s.xh = vec[s.has_head ? tid : 0];
-  s.xt = vec[s.has_tail ? t0 + tid : 0];
-  if (s.nb > 0) load_batch(s.a, s.body, tid, s.nb);
-}
-
-// Streams one vector, opened by begin_vector, into the table.  Full batches
-// go through the fast path unless a logit of the batch lies outside the
-// window (a wave-uniform test); the last, partial batch and the unaligned
-// head and tail always go through the slow path.  Batch k is counted while
-// batch k + 1 loads.
-__device__ __forceinline__ void stream_started(const VecStart& st, uint32_t* hist, uint32_t* tiny,
-                                               Side& sd) {
+// Streams one vector into the table.  Full batches go through the fast path
+// unless a logit of the batch lies outside the window (a wave-uniform test);
+// the last, partial batch and the unaligned head and tail always go through
+// the slow path.  Batch k is counted while batch k + 1 loads.
+__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
+                                              uint32_t* tiny, Side& sd) {
   const int tid = threadIdx.x;
   const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
   uint32_t* hbase = hist - kBase;
-  const uint4* body = st.body;
-  const int nb = st.nb;
-  const bool has_head = st.has_head, has_tail = st.has_tail;
-  const uint32_t xh = st.xh, xt = st.xt;
+  int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
+  if (head > V) head = V;
+  const uint4* body = (const uint4*)(vec + head);
+  const int nb = (V - head) >> 3;
+  const int t0 = head + (nb << 3);
+  // head and tail logits (a lane without one loads logit 0 and counts nothing)
+  const bool has_head = tid < head, has_tail = t0 + tid < V;
+  const uint32_t xh = vec[has_head ? tid : 0];
+  const uint32_t xt = vec[has_tail ? t0 + tid : 0];
   if (nb > 0) {
     const int step = kBatch * kT;
     const int nfull = nb / step;
     const bool part = nfull * step < nb;
     uint4 a[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) a[q] = st.a[q];
+    load_batch(a, body, tid, nb);
     int i = tid;
     for (int k = 0; k < nfull; ++k) {
       uint4 n[kBatch];
@@ -531,13 +508,6 @@ __device__ __forceinline__ void stream_started(const VecStart& st, uint32_t* his
   } else {
     sd = count_pair_slow(hist, tiny, xh, has_head, xt, has_tail, spare, sd);
   }
-}
-
-__device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
-                                              uint32_t* tiny, Side& sd) {
-  VecStart st;
-  begin_vector(vec, V, st);
-  stream_started(st, hist, tiny, sd);
 }
 
 // Vectors are handed out dynamically: a workgroup that finishes early takes
@@ -905,8 +875,6 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
   SlotP cur = slot_params<SHARD>(p, v);
-  VecStart st;  // the shard pass: the current vector's first loads
-  if constexpr (SHARD) begin_vector(cur.vec, V, st);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
@@ -927,8 +895,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     }
 
     Side sd;
-    if constexpr (SHARD) stream_started(st, hcopy, tiny, sd);
-    else stream_vector(cur.vec, V, hcopy, tiny, sd);
+    stream_vector(cur.vec, V, hcopy, tiny, sd);
     {
       const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nzero));
       const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nninf));
@@ -936,14 +903,10 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       if (l == 0) { sh.wzero[w] = z; sh.wninf[w] = n; sh.wflag[w] = f; }
     }
     __syncthreads();  // B1: table complete
-    int in = sh.next;
-    if constexpr (SHARD) in = __builtin_amdgcn_readfirstlane(in);  // the same in every thread
+    const int in = sh.next;
     const bool has_next = in < nitems;
     const int vn = has_next ? item_slot(p, in, (uint32_t)nitems, stride) : v;
     const SlotP nxt = slot_params<SHARD>(p, vn);  // loads in flight meanwhile
-    if constexpr (SHARD) {
-      if (has_next) begin_vector(nxt.vec, V, st);  // lands during the epilogue
-    }
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
     // and clears copy 1; largest +magnitude, smallest -magnitude present,
