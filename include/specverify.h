@@ -348,7 +348,8 @@ sv_status sv_shard_stats(sv_handle h, const sv_shard_stats_args* a, hipStream_t 
  * col_offset[0] = 0, col_offset[g+1] = col_offset[g] + col_count[g],
  * and the last ends at V.  partials[g] is shard g's partial buffer from
  * sv_shard_stats with the same B, k_max, V, mode, draft_tokens and
- * k_per_row.  target_shards / draft_shards (with their strides) are shard
+ * k_per_row (partial_bytes[g] its size, checked like sv_shard_stats
+ * checks it).  target_shards / draft_shards (with their strides) are shard
  * g's logits, as passed to sv_shard_stats: they are read only for a vector
  * whose merged counts the table cannot hold, which is then redone from the
  * logits (the generic path of sv_verify_sample).  The records are written
@@ -360,6 +361,7 @@ sv_status sv_shard_stats(sv_handle h, const sv_shard_stats_args* a, hipStream_t 
 typedef struct {
   int32_t B, k_max, V, mode, G;
   const void* partials[SV_MAX_SHARDS];
+  size_t partial_bytes[SV_MAX_SHARDS]; /* each at least sv_shard_partial_bytes */
   int32_t col_offset[SV_MAX_SHARDS], col_count[SV_MAX_SHARDS];
   const void* target_shards[SV_MAX_SHARDS];
   int64_t target_vec_stride[SV_MAX_SHARDS];
@@ -414,6 +416,7 @@ typedef struct {
                                        workspace sv_shard_combine wrote      */
   size_t records_bytes;
   double* masses;                   /* [G][B][2] exchange buffer              */
+  size_t masses_bytes;              /* at least G * B * 16                    */
   int32_t* out_tokens;              /* outputs as in sv_verify_args           */
   int32_t* accepted;
   int32_t* num_emitted;

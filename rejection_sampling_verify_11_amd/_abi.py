@@ -89,7 +89,7 @@ class ShardCombineArgs(C.Structure):
     _fields_ = [
         ("B", C.c_int32), ("k_max", C.c_int32), ("V", C.c_int32), ("mode", C.c_int32),
         ("G", C.c_int32),
-        ("partials", _P * MAX_SHARDS),
+        ("partials", _P * MAX_SHARDS), ("partial_bytes", C.c_size_t * MAX_SHARDS),
         ("col_offset", C.c_int32 * MAX_SHARDS), ("col_count", C.c_int32 * MAX_SHARDS),
         ("target_shards", _P * MAX_SHARDS), ("target_vec_stride", C.c_int64 * MAX_SHARDS),
         ("draft_shards", _P * MAX_SHARDS), ("draft_vec_stride", C.c_int64 * MAX_SHARDS),
@@ -110,6 +110,7 @@ class ShardDrawArgs(C.Structure):
         ("seed", C.c_uint64), ("offset", C.c_uint64), ("offset_dev", _P),
         ("flags", C.c_uint32),
         ("records", _P), ("records_bytes", C.c_size_t), ("masses", _P),
+        ("masses_bytes", C.c_size_t),
         ("out_tokens", _P), ("accepted", _P), ("num_emitted", _P),
         ("p_at_draft", _P), ("q_at_draft", _P), ("row_status", _P),
     ]
@@ -552,6 +553,7 @@ class ShardedCall:
         c.B, c.k_max, c.V, c.mode, c.G = B, K, V, m, len(self.bounds)
         for g, (off, cnt) in enumerate(self.bounds):
             c.partials[g] = self.partials[g].data_ptr()
+            c.partial_bytes[g] = self.partials[g].numel()
             c.col_offset[g], c.col_count[g] = off, cnt
             sa = self.shard_args[g]
             c.target_shards[g] = sa.target_shard
@@ -581,6 +583,7 @@ class ShardedCall:
                 d.seed, d.offset, d.offset_dev, d.flags = va.seed, va.offset, va.offset_dev, int(flags)
                 d.records, d.records_bytes = va.workspace, va.workspace_bytes
                 d.masses = self.masses.data_ptr()
+                d.masses_bytes = self.masses.numel() * 8
                 for f in ("out_tokens", "accepted", "num_emitted", "p_at_draft", "q_at_draft",
                           "row_status"):
                     setattr(d, f, getattr(va, f))

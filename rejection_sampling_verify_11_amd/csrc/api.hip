@@ -469,6 +469,8 @@ sv_status sv_check_shard_combine_args(const sv_shard_combine_args* a) {
       return SV_E_ARG;
     if (a->mode == 0 && (!a->target_shards[g] || a->target_vec_stride[g] < a->col_count[g]))
       return SV_E_ARG;
+    if (a->partial_bytes[g] < sv_shard_partial_bytes(a->B, a->k_max, a->col_count[g]))
+      return SV_E_WORKSPACE;
   }
   if (!a->temperature || (a->mode == 0 && !a->draft_tokens)) return SV_E_ARG;
   if (!a->workspace || a->workspace_bytes < sample_ws(a->B, a->k_max)) return SV_E_WORKSPACE;
@@ -532,6 +534,7 @@ sv_status sv_check_shard_draw_args(const sv_shard_draw_args* a) {
     return SV_E_ARG;
   if (a->target_vec_stride < a->col_count || a->draft_vec_stride < a->col_count) return SV_E_ARG;
   if (!a->records || a->records_bytes < sample_ws(a->B, a->k_max)) return SV_E_WORKSPACE;
+  if (a->masses_bytes < (size_t)a->G * (size_t)a->B * 2 * sizeof(double)) return SV_E_WORKSPACE;
   return SV_OK;
 }
 

@@ -245,6 +245,7 @@ def good_combine(B=4, K=3, V=1000, G=3, mode=0):
     bounds = _abi.shard_bounds(V, G)
     for g, (off, cnt) in enumerate(bounds):
         c.partials[g] = c.target_shards[g] = c.draft_shards[g] = fake
+        c.partial_bytes[g] = L.sv_shard_partial_bytes(B, K, cnt)
         c.col_offset[g], c.col_count[g] = off, cnt
         c.target_vec_stride[g] = c.draft_vec_stride[g] = V
     c.draft_tokens = c.temperature = fake
@@ -276,6 +277,9 @@ def test_shard_combine_validation():
     c = good_combine()
     c.workspace_bytes = 64
     assert chk(c) == _abi.SV_E_WORKSPACE
+    c = good_combine()
+    c.partial_bytes[2] -= 1                 # a partial buffer too small for its shard
+    assert chk(c) == _abi.SV_E_WORKSPACE
     d = good_combine(mode=1)
     d.draft_tokens = None
     for g in range(d.G):
@@ -303,6 +307,7 @@ def good_draw(B=4, K=3, V=1000, off=200, cnt=300, G=3, shard=1):
     d.target_vec_stride = d.draft_vec_stride = V
     d.records = fake
     d.records_bytes = L.sv_verify_workspace_bytes(B, K, V, _abi.SV_BF16, 0)
+    d.masses_bytes = G * B * 16
     return d
 
 
@@ -312,7 +317,7 @@ def good_draw(B=4, K=3, V=1000, off=200, cnt=300, G=3, shard=1):
     ("target_shard", None, _abi.SV_E_ARG), ("draft_tokens", None, _abi.SV_E_ARG),
     ("out_tokens", None, _abi.SV_E_ARG), ("draft_vec_stride", 299, _abi.SV_E_ARG),
     ("offset_dev", 0x10004, _abi.SV_E_ARG), ("records", None, _abi.SV_E_WORKSPACE),
-    ("records_bytes", 64, _abi.SV_E_WORKSPACE),
+    ("records_bytes", 64, _abi.SV_E_WORKSPACE), ("masses_bytes", 16 * 4 * 3 - 1, _abi.SV_E_WORKSPACE),
 ])
 def test_shard_draw_validation(field, value, code):
     L = _abi.library()
