@@ -16,14 +16,15 @@
 // aligned with V a multiple of 8 are read in groups of NT / 64 segments,
 // one per wave (1024 tokens of both vectors for the residual, 2048 for p'
 // alone), with the next group's loads in flight; under a top-p cut on p'
-// pass 1 works on the listed tokens at or above tau_p only.  On this path a draw from p' alone (the bonus, the
-// zero-residual fallback, the draft sampler's q') knows R = 1 before it
-// starts, so pass 1 stops after the group in which the running sum passes
-// u -- about half the vector on average -- and the wave holding that
-// segment locates the token from its registers.  Other vectors (fp32, unaligned, ragged V) are read in tiles of
-// 1024 x 8 logits with 512-token segments.  Probabilities are exp2 of fp32
-// arguments (v_exp_f32) times the 1/G normalisers; segment and prefix sums
-// are fp64.
+// the residual's pass 1 works on the listed tokens at or above tau_p only.
+// On this path a draw from p' alone (the bonus, the zero-residual fallback,
+// the draft sampler's q') knows its mass before it starts (R = 1), so pass 1
+// stops after the group in which the running sum passes u -- about half
+// the vector on average -- and the wave holding that segment locates the
+// token from its registers.  Other vectors (fp32, unaligned, ragged V) are
+// read in tiles of 1024 x 8 logits with 512-token segments.  Probabilities
+// are exp2 of fp32 arguments (v_exp_f32) times the 1/G normalisers; segment
+// and prefix sums are fp64.
 #include <math.h>
 
 #include "philox.h"
@@ -171,8 +172,8 @@ __device__ __forceinline__ void load_segment(Chunks<MODE>& c, const uint16_t* P,
 
 // r of the 8 tokens of chunk s (0 where the chunk lies past the end).
 template <int MODE>
-__device__ __forceinline__ void chunk_r(const Dist& Pd, const Dist& Qd, const Chunks<MODE>& c, int s,
-                                        bool valid, double r[8]) {
+__device__ __forceinline__ void chunk_r(const Dist& Pd, const Dist& Qd, const Chunks<MODE>& c,
+                                        int s, bool valid, double r[8]) {
   const uint32_t pw[4] = {c.p[s].x, c.p[s].y, c.p[s].z, c.p[s].w};
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -293,8 +294,9 @@ __device__ __forceinline__ void pass1_segment(const Dist& P, const Dist& Q, cons
 // `target`, else (a rounding edge) the last token with mass, -1 if none has
 // any.  The result is the same in every lane.
 template <int MODE>
-__device__ __forceinline__ int locate_in_segment(const Dist& P, const Dist& Q, const Chunks<MODE>& c,
-                                                 int seg, int nchunks, double before, double target) {
+__device__ __forceinline__ int locate_in_segment(const Dist& P, const Dist& Q,
+                                                 const Chunks<MODE>& c, int seg, int nchunks,
+                                                 double before, double target) {
   const int l = threadIdx.x & 63;
   double running = before;
   int hit = 0x7FFFFFFF, lastpos = -1;
@@ -464,8 +466,9 @@ __device__ __forceinline__ int inverse_cdf_bf16(const Dist& P, const Dist& Q, in
 // mode 1: P alone.  Returns y (same value in every thread), or -1 if the
 // distribution is empty.  *zero_residual reports the fallback.
 template <int NT>
-__device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V, double u,
-                           CdfScratch<NT>& sc, bool* zero_residual, double scale = 1.0) {
+__device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mode, int dtype, int V,
+                                           double u, CdfScratch<NT>& sc, bool* zero_residual,
+                                           double scale = 1.0) {
   constexpr int kThreads = NT, kWaves = NT / 64, kTile = NT * 8;
   if (dtype == SV_BF16 && (V & 7) == 0 && is_aligned16(P.vec) &&
       (mode == 1 || is_aligned16(Q.vec))) {
@@ -738,7 +741,8 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
                            rs.ptau, rs.pinv, rs.T);
   Dist Q = P;
   if (mode == 0)
-    Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, rs.qm, rs.qtau, rs.qinv, rs.T);
+    Q = make_dist(p.draft, (int64_t)b * K + acc, p.d_stride, p.dtype, rs.qm, rs.qtau, rs.qinv,
+                  rs.T);
   bool zero = false;
   const int y = inverse_cdf(P, Q, mode, p.dtype, V, rs.u1, sc, &zero);
   if (tid < 64) {
