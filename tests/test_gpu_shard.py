@@ -192,3 +192,19 @@ def test_sharded_draw_degenerate_rows(oracle):
     rep = compare_sample(so, oracle_verify(oracle, inp, toks, 9, 0, rows=rows), None, 2, rows=rows)
     assert rep.excused_mismatches == 0
 
+
+
+@pytest.mark.parametrize("V,G", [(1, 1), (5, 5), (9, 4)])
+def test_tiny_vocabularies(oracle, V, G):
+    """One-column shards and vocabularies smaller than a 16-byte load."""
+    B, K = 3, 2
+    g = torch.Generator().manual_seed(V * 31 + G)
+    zt = (torch.randn((B, K + 1, V), generator=g) * 2).to(torch.bfloat16)
+    zd = (zt[:, :K].float() + torch.randn((B, K, V), generator=g)).to(torch.bfloat16)
+    inp = W.SampleInputs(zt, zd, torch.ones(B), torch.full((B,), 0.95))
+    toks = oracle_tokens(oracle, inp, 12, 3)
+    plain, po, shard, so = sharded_and_plain(inp, toks, G, 12, 3, sharded_draw=True)
+    for k in po:
+        assert torch.equal(po[k], so[k]), k
+    rep = compare_sample(so, oracle_verify(oracle, inp, toks, 12, 3), None, K)
+    assert rep.excused_mismatches == 0
