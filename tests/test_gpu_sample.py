@@ -212,19 +212,77 @@ def test_row_errors_are_isolated(oracle):
 
 def test_count_overflow_falls_back_exactly(oracle):
     """More than 65535 bit-identical bf16 logits in one vector wrap a 16-bit
-    count; the vector must be redone exactly on the generic path."""
-    B, K, V = 3, 2, 70000
+    count: the whole vector one value (row 1), or 7/8 of it with every eighth
+    logit drawn afresh (row 3); such vectors must come out exact (the
+    generic path redoes them)."""
+    B, K, V = 4, 2, 151936
     zt = torch.zeros((B, K + 1, V))
     zt[:, :, :5] = torch.tensor([3.0, 2.0, 2.0, 1.0, 0.5])
-    zt[1] = -7.25                      # one value 70000 times
+    zt[1] = -7.25                      # one value V times
     zt[2, :, 100:] = float("-inf")     # a large masked block
+    zt[3] = -7.25                      # 7/8 of the vector one value ...
+    zt[3, :, ::8] = torch.randn((K + 1, V // 8), generator=torch.Generator().manual_seed(3))
     zd = zt[:, :K].clone()
     zd[:, :, 1] += 1.0
     inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.ones(B),
                          torch.full((B,), 0.9))
-    toks = np.array([[0, 1], [7, 69999], [2, 3]], np.int32)
+    toks = np.array([[0, 1], [7, V - 1], [2, 3], [8, 9]], np.int32)
     rep = check_round(oracle, inp, toks, 2, 0)
     assert rep.exact_rows == B
+
+
+FILLS = {
+    # name: [(fill value, fraction of the vector)], independent masks on each side
+    "finite_mask_999": [(-1e4, 0.999)],
+    "half_fill": [(-30.0, 0.5)],
+    "ninf_mask_999": [(float("-inf"), 0.999)],
+    "zero_fill": [(0.0, 0.9)],
+    "negative_zero_fill": [(-0.0, 0.9)],
+    "positive_fill_holds_the_mass": [(2.0, 0.8)],
+    "two_fills": [(-30.0, 0.45), (-20.0, 0.45)],
+    "filled_first_half": [(-9.5, "first_half")],
+}
+
+
+@pytest.mark.parametrize("case", sorted(FILLS))
+def test_vectors_filled_with_one_value(oracle, case):
+    """A value filling much of a vector (a mask constant, zeros, a repeated
+    logit): many lanes of one table atomic hit one word, and a count may pass
+    16 bits.  Verification and the draft sampler must still match the oracle
+    (top-p 0.9; for the positive fill the crossing lies in the filled value's
+    own word)."""
+    B, K, V = 4, 3, 151936
+    g = torch.Generator().manual_seed(sorted(FILLS).index(case) + 40)
+    zt = torch.randn((B, K + 1, V), generator=g) * 3
+    zd = zt[:, :K] + torch.randn((B, K, V), generator=g)
+
+    def fill(z):
+        z = z.clone()
+        u = torch.rand(z.shape, generator=g)
+        lo = 0.0
+        for value, frac in FILLS[case]:
+            if frac == "first_half":
+                z[..., : V // 2] = value
+            else:
+                z[(u >= lo) & (u < lo + frac)] = value
+                lo += frac
+        return z
+
+    zt, zd = fill(zt), fill(zd)
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.ones(B),
+                         torch.full((B,), 0.9))
+    toks = oracle_tokens(oracle, inp, 21, 0)
+    rep = check_round(oracle, inp, toks, 21, 0)
+    assert rep.exact_rows >= rep.rows - 1
+    d = to_dev(inp)
+    g_toks, g_st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=21, offset=1)
+    torch.cuda.synchronize()
+    o_toks, o_st, cdf, topp = oracle.draft_sample(
+        W.host_logits(inp.draft), inp.temperature.numpy(), inp.top_p.numpy(), seed=21, offset=1,
+        nthreads=NT, diagnostics=True)
+    assert np.array_equal(g_st.cpu().numpy(), o_st)
+    flagged = (cdf < 1e-6) | (topp < 1e-6)
+    assert np.array_equal(g_toks.cpu().numpy()[~flagged], o_toks[~flagged])
 
 
 def test_values_below_the_count_window(oracle):
