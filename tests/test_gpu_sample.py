@@ -285,6 +285,72 @@ def test_vectors_filled_with_one_value(oracle, case):
     assert np.array_equal(g_toks.cpu().numpy()[~flagged], o_toks[~flagged])
 
 
+BF16_MIN = -3.3895313892515355e38  # the most negative finite bf16, a common mask value
+HUGE_NEGATIVE = ["min_mask_999", "min_mask_half", "scattered", "hot_temperature", "only_huge",
+                 "draft_token_masked"]
+
+
+@pytest.mark.parametrize("case", HUGE_NEGATIVE)
+def test_negative_logits_above_the_window(oracle, case):
+    """Negative logits of magnitude 2^16 or more -- the most negative bf16 as a
+    mask, or values such as -7e4 scattered among the logits -- lie above the
+    count table's window; so do vectors with no other finite logit, and the
+    case T = 1000 keeps them at a visible weight.  Verification and the draft
+    sampler must match the oracle, and a masked draft token is rejected."""
+    B, K, V = 4, 3, 32000
+    g = torch.Generator().manual_seed(HUGE_NEGATIVE.index(case) + 60)
+    zt = torch.randn((B, K + 1, V), generator=g) * 3
+    zd = zt[:, :K] + torch.randn((B, K, V), generator=g)
+    T = torch.ones(B)
+
+    def mask(z, frac):
+        z = z.clone()
+        z[torch.rand(z.shape, generator=g) < frac] = BF16_MIN
+        return z
+
+    def scatter(z):
+        z = z.clone()
+        pick = torch.rand(z.shape, generator=g) < 0.01
+        vals = torch.tensor([-7e4, -1e5, -3e38, BF16_MIN])
+        z[pick] = vals[torch.randint(0, 4, (int(pick.sum()),), generator=g)]
+        return z
+
+    if case in ("min_mask_999", "draft_token_masked"):
+        zt, zd = mask(zt, 0.999), mask(zd, 0.999)
+    elif case == "min_mask_half":
+        zt, zd = mask(zt, 0.5), mask(zd, 0.5)
+    elif case in ("scattered", "hot_temperature"):
+        zt, zd = scatter(zt), scatter(zd)
+        if case == "hot_temperature":
+            T[:2] = 1000.0
+    else:  # only_huge: vectors whose finite logits all lie above the window
+        zt, zd = scatter(zt), scatter(zd)
+        zt[0, 0] = -7e4
+        zt[0, 0, 5] = float("-inf")
+        zd[1, 1] = BF16_MIN
+        zd[1, 1, :100] = -1e5
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), T, torch.full((B,), 0.9))
+    toks = oracle_tokens(oracle, inp, 23, 0)
+    if case == "draft_token_masked":
+        # draft tokens where the target is masked: p'(x) = 0, rejected
+        for b in range(B):
+            toks[b, 0] = int(torch.nonzero(zt[b, 0] == BF16_MIN)[b * 7, 0])
+    rep = check_round(oracle, inp, toks, 23, 0)
+    assert rep.exact_rows >= rep.rows - 1
+    if case == "draft_token_masked":
+        out = gpu_verify(inp, toks, 23, 0)
+        assert torch.all(out["accepted"] == 0)
+    d = to_dev(inp)
+    g_toks, g_st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=23, offset=1)
+    torch.cuda.synchronize()
+    o_toks, o_st, cdf, topp = oracle.draft_sample(
+        W.host_logits(inp.draft), inp.temperature.numpy(), inp.top_p.numpy(), seed=23, offset=1,
+        nthreads=NT, diagnostics=True)
+    assert np.array_equal(g_st.cpu().numpy(), o_st)
+    flagged = (cdf < 1e-6) | (topp < 1e-6)
+    assert np.array_equal(g_toks.cpu().numpy()[~flagged], o_toks[~flagged])
+
+
 def test_values_below_the_count_window(oracle):
     """Nonzero logits below 2^-24 in magnitude (a few per vector in
     N(0, 3^2) logits) are listed beside the count table: scattered ones with

@@ -142,6 +142,31 @@ def test_vectors_the_table_cannot_hold(oracle):
         assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b)), k
 
 
+@pytest.mark.parametrize("T", [1.0, 1000.0])
+def test_negative_logits_above_the_window_sharded(oracle, T):
+    """Masks at the most negative bf16 and scattered values such as -7e4,
+    above the count table's window in every shard: the merge redoes such a
+    vector from the shards' logits, as the unsharded pass redoes it from the
+    whole vector, so the records are bit for bit the same (T = 1 and
+    T = 1000), and both match the oracle."""
+    B, K, V, G = 4, 3, 60000, 5
+    g = torch.Generator().manual_seed(81)
+    zt = torch.randn((B, K + 1, V), generator=g) * 3
+    zd = zt[:, :K] + torch.randn((B, K, V), generator=g)
+    for z in (zt, zd):
+        z[torch.rand(z.shape, generator=g) < 0.3] = -3.3895313892515355e38
+        z[torch.rand(z.shape, generator=g) < 0.01] = -7e4
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.full((B,), T),
+                         torch.full((B,), 0.9))
+    toks = oracle_tokens(oracle, inp, 5, 0)
+    plain, po, shard, so = sharded_and_plain(inp, toks, G, 5, 0)
+    assert np.array_equal(records(plain, B, K), records(shard.call, B, K))
+    for k in po:
+        assert torch.equal(torch.nan_to_num(po[k].float()), torch.nan_to_num(so[k].float())), k
+    rep = compare_sample(so, oracle_verify(oracle, inp, toks, 5, 0), None, K)
+    assert rep.excused_mismatches <= 1
+
+
 @pytest.mark.parametrize("shards", [1, 2, 3, 8, 16])
 def test_sharded_draw(oracle, shards):
     """The draw split over the shards (each sums its columns' residual and p'
