@@ -222,9 +222,10 @@ def sharded_leg(dev, sets, n):
 
 
 def round_leg(dev, n):
-    """The on-device round at B=512, k_max=8, V=128256: verification, rollback
-    over a preallocated page table (pages stay mapped), the dynamic-k
-    controller and the round counter.  Between rounds a torch add stands in
+    """The on-device round at B=512, k_max=8, V=128256: verification with the
+    rollback over a preallocated page table fused in (pages stay mapped, so
+    each row rolls itself back), the dynamic-k controller and the round
+    counter; also timed eagerly with the rollback as its own kernel.  Between rounds a torch add stands in
     for the target model's k+1 KV writes; the logits and draft tokens stay
     fixed."""
     import torch
@@ -235,7 +236,7 @@ def round_leg(dev, n):
     k = torch.full((B,), 5, dtype=torch.int32, device=dev)
     inp = W.workload5(0, rows, k, k_max=K, device=dev, V=V)
     toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 0)
-    ctx_max = 4096 + 2 * (n + 40) * (K + 1)
+    ctx_max = 4096 + (4 * n + 100) * (K + 1)  # every round below lengthens a row by <= K + 1
     MP = (ctx_max + ps - 1) // ps
     page_table = torch.arange(B * MP, dtype=torch.int32, device=dev).view(B, MP)
     kv_len = rows.kv_len0.to(dev).clone()
@@ -246,10 +247,13 @@ def round_leg(dev, n):
     acc = verify.outputs["accepted"]
     roll = sv.RollbackCall(kv_len, acc, page_table, ps, K, k_per_row=k, num_pages=B * MP)
 
-    def one_round():
+    def one_round(fused=True):
         kv_len.add_(k).add_(1)     # the target forward's k + 1 speculative writes
-        verify.run()
-        roll.run()
+        if fused:
+            verify.run_with_rollback(roll)
+        else:
+            verify.run()
+            roll.run()
         sv.dynamic_k(acc, k, state)
         sv.advance_offset(offset)
 
@@ -277,9 +281,25 @@ def round_leg(dev, n):
         k_sum += k.sum()
         g.replay()
     mean_k = k_sum.item() / (20 * B)
+    # the fused rollback against its own kernel, with k held where it is
+    # (the controller would move it between the two timings)
+
+    def verify_roll(fused):
+        kv_len.add_(k).add_(1)
+        if fused:
+            verify.run_with_rollback(roll)
+        else:
+            verify.run()
+            roll.run()
+
+    pair = {True: 0.0, False: 0.0}
+    for _ in range(2):
+        for fused in (True, False):
+            pair[fused] += timed(lambda: verify_roll(fused), n // 2, dev) / 2
     return {"workload": "B=512 k_b in [2, 8] from the controller (window 64) V=128256 bf16, "
                         "T_b ~ U[0.1, 1], no top-p, page-table rollback",
             "graph_ms_per_round": graph_ms, "eager_ms_per_round": eager_ms,
+            "verify_rollback_ms": {"fused": pair[True], "rollback_kernel": pair[False]},
             "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "mean_k": mean_k, "verified_positions_per_s": mean_k * B / (graph_ms * 1e-3),
             "mean_accepted": acc.float().mean().item()}

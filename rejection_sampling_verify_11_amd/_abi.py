@@ -120,6 +120,7 @@ EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "s
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
+           "sv_check_verify_rollback_args", "sv_verify_sample_rollback",
            "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset",
            "sv_shard_partial_bytes", "sv_shard_workspace_bytes", "sv_check_shard_stats_args",
            "sv_shard_stats", "sv_check_shard_combine_args", "sv_shard_combine",
@@ -164,6 +165,12 @@ def library():
                 L.sv_check_rollback_args.restype = C.c_int
                 L.sv_kv_rollback.argtypes = [_P, C.POINTER(RollbackArgs), _P]
                 L.sv_kv_rollback.restype = C.c_int
+                L.sv_check_verify_rollback_args.argtypes = [C.POINTER(VerifyArgs),
+                                                            C.POINTER(RollbackArgs)]
+                L.sv_check_verify_rollback_args.restype = C.c_int
+                L.sv_verify_sample_rollback.argtypes = [_P, C.POINTER(VerifyArgs),
+                                                        C.POINTER(RollbackArgs), _P]
+                L.sv_verify_sample_rollback.restype = C.c_int
                 L.sv_check_dynk_args.argtypes = [C.POINTER(DynkArgs)]
                 L.sv_check_dynk_args.restype = C.c_int
                 L.sv_dynamic_k.argtypes = [_P, C.POINTER(DynkArgs), _P]
@@ -370,6 +377,17 @@ class VerifyCall:
         rc = self._fn(self._h, self._ref, _stream(self.device, stream))
         if rc != SV_OK:
             raise SpecVerifyError("specverify " + self.mode, rc)
+        return self.outputs
+
+    def run_with_rollback(self, roll, stream=None):
+        """This verification, then roll's rollback on its accepted counts
+        (sv_verify_sample_rollback; roll must read outputs["accepted"])."""
+        if self.mode != "sample":
+            raise ValueError("only sampled verification has a fused rollback")
+        rc = library().sv_verify_sample_rollback(self._h, self._ref, roll._ref,
+                                                 _stream(self.device, stream))
+        if rc != SV_OK:
+            raise SpecVerifyError("sv_verify_sample_rollback", rc)
         return self.outputs
 
 

@@ -245,6 +245,10 @@ static sv::FinalizeParams finalize_params(const sv_verify_args* a) {
   f.q_at_draft = a->q_at_draft;
   f.row_status = a->row_status;
   f.draft_out = const_cast<int32_t*>(a->draft_tokens);
+  f.kv_len = nullptr;
+  f.page_table = nullptr;
+  f.ps = f.MP = f.num_pages = 0;
+  f.roll_status = nullptr;
   return f;
 }
 
@@ -346,6 +350,43 @@ sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) 
   p.row_status = a->row_status;
   p.recs = (sv::RollRec*)a->workspace;
   if (sv::launch_rollback(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
+sv_status sv_check_verify_rollback_args(const sv_verify_args* v, const sv_rollback_args* r) {
+  sv_status st = sv_check_verify_args(v, 0);
+  if (st != SV_OK) return st;
+  st = sv_check_rollback_args(r);
+  if (st != SV_OK) return st;
+  if (r->B != v->B || r->k_max != v->k_max || r->k_per_row != v->k_per_row) return SV_E_ARG;
+  if (v->B > 0 && r->accepted != v->accepted) return SV_E_ARG;
+  return SV_OK;
+}
+
+sv_status sv_verify_sample_rollback(sv_handle h, const sv_verify_args* v,
+                                    const sv_rollback_args* r, hipStream_t s) {
+  const sv_status st = sv_check_verify_rollback_args(v, r);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (v->B == 0) return SV_OK;
+  if (r->free_pages || r->kv_pool) {
+    // releases are placed on the stack by a scan over all rows
+    const sv_status sv = sv_verify_sample(h, v, s);
+    if (sv != SV_OK) return sv;
+    return sv_kv_rollback(h, r, s);
+  }
+  if (!(v->flags & SV_FLAG_RECORDS_READY) &&
+      sv::launch_stats(stats_params(v, 0), v->dtype, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
+  sv::FinalizeParams f = finalize_params(v);
+  f.kv_len = r->kv_len;
+  f.page_table = r->page_table;
+  f.ps = r->page_size;
+  f.MP = r->max_pages_per_seq;
+  f.num_pages = r->num_pages;
+  f.roll_status = r->row_status;
+  if (sv::launch_finalize_sample(f, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
   return SV_OK;
 }
 

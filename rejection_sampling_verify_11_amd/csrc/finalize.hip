@@ -728,14 +728,68 @@ __device__ __forceinline__ int row_header(const FinalizeParams& p, int b, RowSha
   return x;
 }
 
-template <int NT>
+// ---- the rollback of a row, fused into its verification
+// Used when the cache has no free stack and no pool: the rollback of one row
+// then needs nothing from the others, and is the rollback kernel's decision
+// for that row ([SSD] §3.3: the write pointer moves back to the accepted
+// prefix; the pages holding the dropped positions must be mapped), taken on
+// the accepted count the row's verification just found (-1 for a flagged
+// row).  Wave 0 takes the decision after the header and loads the page
+// entries it checks (a lane per page), so that their latency overlaps the
+// draw; the entries are tested, and the length written, at the end.
+struct RollCheck {
+  uint32_t st;
+  int new_len, first, used;
+  int32_t e;  // page entry first + lane (when below used)
+};
+
+__device__ __forceinline__ int ceil_div_i(int x, int d) { return (x + d - 1) / d; }
+
+__device__ __forceinline__ RollCheck roll_begin(const FinalizeParams& p, int b, const RowShared& rs,
+                                                int old) {
+  RollCheck r;
+  const int k = rs.kb, acc = rs.go ? rs.acc : -1;
+  r.st = 0;
+  if (k < 1 || k > p.K) r.st |= SV_ROW_BAD_K;
+  else if (acc < 0 || acc > k || old - (k - acc) < 0) r.st |= SV_ROW_BAD_ACCEPTED;
+  if (old < 0 || ceil_div_i(old, p.ps) > p.MP) r.st |= SV_ROW_BAD_PAGES;
+  r.new_len = r.st ? old : old - (k - acc);
+  r.used = r.st ? 0 : ceil_div_i(old, p.ps);
+  r.first = r.st ? 0 : r.new_len / p.ps;
+  // clamped into the row (used <= MP), loaded whether or not it is tested
+  const int pg = min(r.first + (int)(threadIdx.x & 63), max(r.used - 1, 0));
+  r.e = p.page_table[(int64_t)b * p.MP + pg];
+  return r;
+}
+
+__device__ __forceinline__ void roll_end(const FinalizeParams& p, int b, const RollCheck& r) {
+  const int l = threadIdx.x & 63;
+  auto bad_entry = [&](int32_t e) { return e < 0 || (p.num_pages > 0 && e >= p.num_pages); };
+  bool bad = r.first + l < r.used && bad_entry(r.e);
+  for (int pg = r.first + 64 + l; pg < r.used; pg += 64)  // more than 64 pages dropped (rare)
+    bad = bad || bad_entry(p.page_table[(int64_t)b * p.MP + pg]);
+  const uint32_t st = r.st | (__any(bad) ? (uint32_t)SV_ROW_BAD_PAGES : 0u);
+  if (l == 0) {
+    if (!st) p.kv_len[b] = r.new_len;
+    if (p.roll_status) p.roll_status[b] = (int32_t)st;
+  }
+}
+
+template <int NT, bool ROLL>
 __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
   __shared__ CdfScratch<NT> sc;
   __shared__ RowShared rs;
   const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
+  // the KV length loads with the header's loads
+  const int old = ROLL && tid < 64 ? p.kv_len[b] : 0;
   const int x = row_header<true>(p, b, rs);
   __syncthreads();
-  if (!rs.go) return;
+  RollCheck rc;
+  if (ROLL && tid < 64) rc = roll_begin(p, b, rs, old);
+  if (!rs.go) {
+    if (ROLL && tid < 64) roll_end(p, b, rc);
+    return;
+  }
   const int acc = rs.acc, mode = rs.mode;
   const Dist P = make_dist(p.target, (int64_t)b * (K + 1) + acc, p.t_stride, p.dtype, rs.pm,
                            rs.ptau, rs.pinv, rs.T);
@@ -756,6 +810,7 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       if (p.num_emitted) p.num_emitted[b] = acc + 1;
       if (p.row_status) p.row_status[b] = 0;
     }
+    if (ROLL) roll_end(p, b, rc);
   }
 }
 
@@ -979,10 +1034,15 @@ static bool use_half_blocks(unsigned nblocks, int num_cus) {
 hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t) {
   if (p.B == 0) return hipSuccess;
   TimedScope ts(t, "finalize_sample", s);
-  if (use_half_blocks((unsigned)p.B, num_cus))
-    hipLaunchKernelGGL(finalize_sample_kernel<512>, dim3(p.B), dim3(512), 0, s, p);
+  const bool half = use_half_blocks((unsigned)p.B, num_cus);
+  if (half && p.kv_len)
+    hipLaunchKernelGGL((finalize_sample_kernel<512, true>), dim3(p.B), dim3(512), 0, s, p);
+  else if (half)
+    hipLaunchKernelGGL((finalize_sample_kernel<512, false>), dim3(p.B), dim3(512), 0, s, p);
+  else if (p.kv_len)
+    hipLaunchKernelGGL((finalize_sample_kernel<1024, true>), dim3(p.B), dim3(1024), 0, s, p);
   else
-    hipLaunchKernelGGL(finalize_sample_kernel<1024>, dim3(p.B), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL((finalize_sample_kernel<1024, false>), dim3(p.B), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 

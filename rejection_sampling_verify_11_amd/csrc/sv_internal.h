@@ -151,6 +151,12 @@ struct FinalizeParams {
   float* q_at_draft;
   int32_t* row_status;
   int32_t* draft_out;  // draft sampling mode: tokens written here
+  // verification with the rollback of a cache that has no free stack and
+  // no pool (kv_len non-null): each row also moves its own KV length back
+  int32_t* kv_len;
+  const int32_t* page_table;
+  int32_t ps, MP, num_pages;
+  int32_t* roll_status;
 };
 
 struct GreedyParams {

@@ -164,6 +164,35 @@ def test_rollback_validation():
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG
 
 
+def test_verify_rollback_validation():
+    """The fused verify + rollback checks both blocks and that they describe
+    the same rows: B, k_max, k_per_row, and the rollback reading the
+    verification's accepted counts."""
+    L = _abi.library()
+    v = good_args(B=4, K=3)
+
+    def roll():
+        r = _abi.RollbackArgs()
+        r.B, r.k_max, r.page_size, r.max_pages_per_seq = 4, 3, 16, 10
+        r.kv_len = r.page_table = 0x20000
+        r.accepted = v.accepted
+        return r
+
+    chk = lambda r: L.sv_check_verify_rollback_args(C.byref(v), C.byref(r))
+    assert chk(roll()) == _abi.SV_OK
+    for field, value in (("B", 5), ("k_max", 4), ("k_per_row", 0x30000), ("accepted", 0x30000)):
+        r = roll()
+        setattr(r, field, value)
+        assert chk(r) == _abi.SV_E_ARG, field
+    r = roll()
+    r.page_size = 0
+    assert chk(r) == _abi.SV_E_ARG
+    v.V = 0
+    assert chk(roll()) == _abi.SV_E_ARG
+    v = good_args(B=4, K=3)
+    assert L.sv_verify_sample_rollback(None, C.byref(v), C.byref(roll()), None) == _abi.SV_E_ARG
+
+
 def test_dynk_validation():
     L = _abi.library()
     a = _abi.DynkArgs(4, 64, 2, 8, 17, 20, 7, 10, 0x10000, 0x10000, 0x10000)
