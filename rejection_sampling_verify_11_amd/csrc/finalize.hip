@@ -25,6 +25,10 @@
 // read in tiles of 1024 x 8 logits with 512-token segments.  Probabilities
 // are exp2 of fp32 arguments (v_exp_f32) times the 1/G normalisers; segment
 // and prefix sums are fp64.
+//
+// With a KV rollback that keeps pages mapped (no free stack, no pool), the
+// row's workgroup also rolls the row back on the accepted count it found
+// (finalize_sample_kernel<NT, true>, below).
 #include <math.h>
 
 #include "philox.h"
