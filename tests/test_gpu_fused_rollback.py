@@ -134,3 +134,46 @@ def test_fused_entry_with_a_free_stack(oracle):
     pt, n = page_table(lens, ps, MP)
     out = run_both(inp, toks, None, lens, ps, pt, n, free_spare=6)
     assert torch.all(out["roll_status"] == 0)
+
+
+def test_fused_rollback_in_a_replayed_graph(oracle):
+    """Rounds of (k + 1 KV writes, fused verification + rollback) captured
+    once as a HIP graph and replayed, against the same rounds run eagerly as
+    two calls: every replay leaves the same lengths and outputs."""
+    B, K, ps = 64, 4, 16
+    inp = W.workload2(6, B=B, k=K, V=32000)
+    toks = torch.as_tensor(oracle_tokens(oracle, inp, 7, 1), dtype=torch.int32, device=DEV)
+    d = to_dev(inp)
+    MP = (300 + 8 * (K + 1) + ps - 1) // ps
+    lens0 = torch.as_tensor(np.random.default_rng(2).integers(100, 300, B), dtype=torch.int32)
+
+    def chain():
+        call = sv.VerifyCall("sample", d.target, d.draft, toks, d.temperature, d.top_p, None, 7, 1)
+        kv = lens0.to(DEV).clone()
+        pt = torch.arange(B * MP, dtype=torch.int32, device=DEV).view(B, MP)
+        roll = sv.RollbackCall(kv, call.outputs["accepted"], pt, ps, K, num_pages=B * MP)
+        return call, kv, roll
+
+    g_call, g_kv, g_roll = chain()
+    e_call, e_kv, e_roll = chain()
+
+    def fused_round():
+        g_kv.add_(K + 1)
+        g_call.run_with_rollback(g_roll)
+
+    fused_round()  # loads the kernels before the capture
+    torch.cuda.synchronize()
+    g_kv.copy_(lens0.to(DEV))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fused_round()
+    for r in range(5):
+        e_kv.add_(K + 1)
+        e_call.run()
+        e_roll.run()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_kv, e_kv), r
+        assert torch.equal(g_roll.row_status, e_roll.row_status), r
+        for n in ("out_tokens", "accepted", "num_emitted", "row_status"):
+            assert torch.equal(g_call.outputs[n], e_call.outputs[n]), (r, n)
