@@ -20,17 +20,16 @@ class EventTimer final : public sv::Timer {
     }
   }
   void begin(const char* name, hipStream_t s) override {
-    if (used_ >= kMax) { cur_ = -1; return; }
-    if (used_ == pool_.size()) {
-      hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess) { cur_ = -1; return; }
-      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); cur_ = -1; return; }
-      pool_.push_back({a, b});
-    }
-    cur_ = (long)used_++;
-    names_.resize(used_);
-    names_[cur_] = name;
-    hipEventRecord(pool_[cur_].first, s);
+    cur_ = take(name);
+    if (cur_ >= 0) hipEventRecord(pool_[cur_].first, s);
+  }
+  bool pair(const char* name, hipEvent_t* start, hipEvent_t* stop) override {
+    const long i = take(name);
+    cur_ = -1;
+    if (i < 0) return false;
+    *start = pool_[i].first;
+    *stop = pool_[i].second;
+    return true;
   }
   void end(hipStream_t s) override {
     if (cur_ >= 0) hipEventRecord(pool_[cur_].second, s);
@@ -60,6 +59,20 @@ class EventTimer final : public sv::Timer {
   }
 
  private:
+  // the next entry's index (its events created on first use), -1 if full
+  long take(const char* name) {
+    if (used_ >= kMax) return -1;
+    if (used_ == pool_.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return -1;
+      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return -1; }
+      pool_.push_back({a, b});
+    }
+    const long i = (long)used_++;
+    names_.resize(used_);
+    names_[i] = name;
+    return i;
+  }
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool_;
   std::vector<const char*> names_;
   size_t used_ = 0;

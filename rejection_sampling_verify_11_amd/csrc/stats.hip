@@ -29,6 +29,7 @@
 // Generic path (fp32 logits, or a bf16 vector the table cannot hold): passes
 // over the vector in global memory: max, fp64 sum, then a 4-pass radix select
 // on 32-bit order-preserving keys with fp64 mass histograms.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "sv_internal.h"
@@ -1246,8 +1247,13 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
       TimedScope ts(t, "stats_plan", s);
       hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
     }
-    TimedScope ts(t, "stats_bf16", s);
-    hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, p);
+    // timed by events attached to the dispatch, which bound the kernel's
+    // execution as a kernel trace does
+    hipEvent_t e0, e1;
+    if (t && t->pair("stats_bf16", &e0, &e1))
+      hipExtLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, e0, e1, 0u, p);
+    else
+      hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, p);
   } else {
     TimedScope ts(t, "stats_generic", s);
     hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kGenThreads), 0, s, p, dtype);

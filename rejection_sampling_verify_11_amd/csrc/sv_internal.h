@@ -212,6 +212,10 @@ class Timer {
   virtual ~Timer() {}
   virtual void begin(const char* name, hipStream_t s) = 0;
   virtual void end(hipStream_t s) = 0;
+  // An unrecorded event pair for a launch that records them itself
+  // (hipExtLaunchKernelGGL: the events then bound the kernel's execution,
+  // not the launch); false if none is left.
+  virtual bool pair(const char* name, hipEvent_t* start, hipEvent_t* stop) = 0;
 };
 
 struct TimedScope {
