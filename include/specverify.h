@@ -97,8 +97,10 @@ sv_status sv_destroy(sv_handle h);
 const char* sv_status_string(sv_status s);
 
 /* Kernel timing (diagnostics).  While enabled, every kernel this handle
- * launches is bracketed by two HIP events recorded on the caller's stream
- * (events are created on first use and reused; at most 4096 launches are
+ * launches is bracketed by two HIP events on the caller's stream: recorded
+ * around the launch, or, for the bf16 statistics kernel, attached to its
+ * dispatch so that they bound its execution alone (events are created on
+ * first use and reused; at most 4096 launches are
  * kept between reads).  sv_timing_read waits for those events, writes up to
  * max_entries (kernel name, launch count, total milliseconds) triples
  * accumulated since the previous read, clears the record and returns the
