@@ -246,6 +246,24 @@ static int32_t inverse_cdf(const double* r, int32_t V, double u, double* margin,
   return y;
 }
 
+/* Where token t lies in the inverse CDF over r: the prefix just below it and
+ * at it, normalised by the total as inverse_cdf forms them (the same
+ * left-to-right sums), its own share, and the uniform of the draw. */
+static void probe_interval(const double* r, int32_t V, int32_t t, double u,
+                           double out[4]) {
+  out[3] = u;
+  if (t < 0 || t >= V) { out[0] = out[1] = out[2] = NAN; return; }
+  double C = 0.0, below = 0.0, at = 0.0;
+  for (int32_t j = 0; j < V; ++j) {
+    if (j == t) below = C;
+    C += r[j];
+    if (j == t) at = C;
+  }
+  out[0] = below / C;
+  out[1] = at / C;
+  out[2] = r[t] / C;
+}
+
 /* Basic per-row checks shared by all entry points. */
 static int row_header_status(const svref_verify_args* a, int32_t b, int32_t* k_out,
                              int check_sampling) {
@@ -333,9 +351,17 @@ static void sample_row(row_ctx* c, int32_t b) {
     }
   }
 
+  /* what-if: the draw the oracle makes when the scan stops at a given
+   * position (used to check a result that stopped elsewhere) */
+  if (a->forced_accepted) {
+    int32_t f = a->forced_accepted[b];
+    if (f >= 0 && f <= k) acc = f;
+  }
+
   double u1 = svref_uniform(a->seed, row_id(a, b), (uint64_t)acc, 1, a->offset);
   int32_t y;
   double margin = INFINITY, R = -1.0;
+  const double* drawn; /* the distribution the token is drawn from */
   if (acc < k) {
     /* First rejection: resample from norm(max(0, p' - q')) ([SSD] §2.4 and
      * §5.2 insist on the clamp; [SD] §2.1).  If that residual is all zero,
@@ -350,16 +376,19 @@ static void sample_row(row_ctx* c, int32_t b) {
       c->qa[j] = d > 0.0 ? d : 0.0; /* reuse qa as r */
       Rsum += c->qa[j];
     }
-    if (Rsum == 0.0) y = inverse_cdf(c->pa, V, u1, &margin, NULL);
-    else y = inverse_cdf(c->qa, V, u1, &margin, NULL);
+    drawn = Rsum == 0.0 ? c->pa : c->qa;
+    y = inverse_cdf(drawn, V, u1, &margin, NULL);
     R = Rsum;
   } else {
     /* Every draft accepted: one bonus token from p' at position k
      * ([SD] §2.2; [SSD] §2.1 and §4.3). */
     load_target(c, b, k);
     svref_softmax_topp(c->z, V, T, P, c->pa, NULL, NULL, NULL);
-    y = inverse_cdf(c->pa, V, u1, &margin, NULL);
+    drawn = c->pa;
+    y = inverse_cdf(drawn, V, u1, &margin, NULL);
   }
+  if (a->probe_token && a->diag_probe)
+    probe_interval(drawn, V, a->probe_token[b], u1, a->diag_probe + (int64_t)b * 4);
 
   int64_t ob = (int64_t)b * (K + 1);
   for (int32_t j = 0; j <= K; ++j) a->out_tokens[ob + j] = -1;
@@ -458,6 +487,9 @@ static void draft_row(row_ctx* c, int32_t b, int32_t* out) {
     svref_softmax_topp(c->z, V, T, P, c->qa, &G, &above, NULL);
     double u = svref_uniform(a->seed, row_id(a, b), (uint64_t)i, 2, a->offset);
     out[(int64_t)b * K + i] = inverse_cdf(c->qa, V, u, &margin, NULL);
+    if (a->probe_token && a->diag_probe)
+      probe_interval(c->qa, V, a->probe_token[(int64_t)b * K + i], u,
+                     a->diag_probe + ((int64_t)b * K + i) * 4);
     if (a->diag_acc_margin) a->diag_acc_margin[(int64_t)b * K + i] = margin;
     if (a->diag_topp_margin_d) a->diag_topp_margin_d[(int64_t)b * K + i] = topp_margin(P, G, above);
   }
@@ -558,20 +590,21 @@ int svref_kv_rollback(const svref_rollback_args* a) {
     else if (acc < 0 || acc > k || old - (k - acc) < 0) st[b] |= SVREF_ROW_BAD_ACCEPTED;
     if (old < 0 || ceil_div(old, ps) > MP) st[b] |= SVREF_ROW_BAD_PAGES;
     if (!st[b]) {
-      /* Consistency of the table with the length, where the rollback acts:
-       * every page holding a position in [new, old) is mapped (to a page of
-       * the pool), and, when pages are released, the first entry past the
-       * old length is unmapped.  Without a free stack the pages past the
-       * length stay mapped by design ([SD] §4.3), so that entry says
-       * nothing there. */
-      int32_t nl = old - (k - acc);
+      /* The whole row of the page table must agree with the length: every
+       * logical page below ceil(old/ps) maps a page of the pool, and, when
+       * pages are released onto a free stack, every later entry is
+       * unmapped, so the row maps exactly ceil(old/ps) pages and after the
+       * rollback exactly ceil(new/ps).  Without a free stack, pages past the
+       * length stay mapped by design ([SD] §4.3): those entries are free. */
       int32_t used = ceil_div(old, ps);
-      for (int32_t pg = nl / ps; pg < used; ++pg) {
+      for (int32_t pg = 0; pg < MP; ++pg) {
         int32_t e = a->page_table[(int64_t)b * MP + pg];
-        if (e < 0 || (a->num_pages > 0 && e >= a->num_pages)) st[b] |= SVREF_ROW_BAD_PAGES;
+        if (pg < used) {
+          if (e < 0 || (a->num_pages > 0 && e >= a->num_pages)) st[b] |= SVREF_ROW_BAD_PAGES;
+        } else if (a->free_pages && e != -1) {
+          st[b] |= SVREF_ROW_BAD_PAGES;
+        }
       }
-      if (a->free_pages && used < MP && a->page_table[(int64_t)b * MP + used] != -1)
-        st[b] |= SVREF_ROW_BAD_PAGES;
     }
     if (!st[b]) {
       newlen[b] = old - (k - acc);
@@ -640,34 +673,36 @@ int svref_kv_rollback(const svref_rollback_args* a) {
 
 int svref_dynamic_k(const svref_dynk_args* a) {
   if (!a || a->B < 0 || a->window < 1 || a->k_min < 1 || a->k_max < a->k_min ||
-      a->up_den <= 0 || a->down_den <= 0)
+      a->up_den <= 0 || a->down_den <= 0 || a->capacity < 0)
     return -1;
-  if (a->B > 0 && (!a->accepted || !a->k_per_row || !a->state)) return -1;
+  if (a->B > 0 && (!a->accepted || !a->k_per_row || !a->hist_accepted ||
+                   !a->hist_proposed || !a->hist_len))
+    return -1;
+  for (int32_t b = 0; b < a->B; ++b)
+    if (a->hist_len[b] < 0 || a->hist_len[b] > a->capacity) return -1;
   const int32_t W = a->window;
   for (int32_t b = 0; b < a->B; ++b) {
-    int32_t* st = a->state + (int64_t)b * (W + 4);
-    int32_t* slots = st + 4;
     const int32_t k = a->k_per_row[b];
     const int32_t acc = a->accepted[b];
-    /* a row error (accepted outside [0, k]) teaches nothing; a k that does
-     * not fit the 15-bit field of a slot is not a draft length either */
-    if (acc < 0 || acc > k || k > 0x7FFF) continue;
-    /* the round enters the window; when it is full the oldest round leaves */
-    if (st[0] < W) {
-      slots[(st[1] + st[0]) % W] = acc | (k << 16);
-      st[0] += 1;
-    } else {
-      const int32_t old = slots[st[1]];
-      st[2] -= old & 0xFFFF;
-      st[3] -= old >> 16;
-      slots[st[1]] = acc | (k << 16);
-      st[1] = (st[1] + 1) % W;
-    }
-    st[2] += acc;
-    st[3] += k;
+    /* A round teaches the controller only if it verified a draft length the
+     * controller could have chosen and its accepted count is possible: a
+     * row error (accepted -1) or a k outside [k_min, k_max] leaves the row
+     * as it is. */
+    if (k < a->k_min || k > a->k_max || acc < 0 || acc > k) continue;
+    int32_t* ha = a->hist_accepted + (int64_t)b * a->capacity;
+    int32_t* hp = a->hist_proposed + (int64_t)b * a->capacity;
+    int32_t n = a->hist_len[b];
+    if (n == a->capacity) return -1; /* the caller's history is full */
+    ha[n] = acc;
+    hp[n] = k;
+    a->hist_len[b] = ++n;
+    /* [SSD] §3.2: the acceptance rate over the last W rounds, once W rounds
+     * have been seen; above the upper threshold k grows by one, below the
+     * lower one it shrinks by one, within [k_min, k_max] */
     int32_t next = k;
-    if (st[0] == W) {
-      const int64_t sa = st[2], sp = st[3];
+    if (n >= W) {
+      int64_t sa = 0, sp = 0;
+      for (int32_t r = n - W; r < n; ++r) { sa += ha[r]; sp += hp[r]; }
       if (sa * a->up_den > (int64_t)a->up_num * sp) next = k + 1;
       else if (sa * a->down_den < (int64_t)a->down_num * sp) next = k - 1;
     }

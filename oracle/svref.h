@@ -124,6 +124,21 @@ typedef struct {
                                  when the bonus path was taken            */
   /* draft sampling fills diag_acc_margin[b][i] with the CDF margin of its
    * draw at position i and diag_topp_margin_d with the top-p margins      */
+
+  /* What-if inputs, so that a result that differs from the oracle's can be
+   * checked against the oracle's own distributions (each NULL or as sized):
+   * forced_accepted [B]: draw at this position instead of at the scan's
+   *   first rejection (a value outside [0, k_b] is ignored); every
+   *   diagnostic keeps its meaning, and the draw is the one the oracle makes
+   *   when the scan stops there.
+   * probe_token: verification [B], draft sampling [B][k_max]: a token whose
+   *   interval in the drawn distribution is reported in diag_probe as
+   *   {C_{t-1}/R, C_t/R, r_t/R, u}: the CDF just below and at t, the token's
+   *   share of the mass and the uniform of the draw (NaN when t is not in
+   *   [0, V)). */
+  const int32_t* forced_accepted;
+  const int32_t* probe_token;
+  double* diag_probe;
 } svref_verify_args;
 
 /* Rejection-sampling verification, one row at a time ([SSD] §2.4, §4.3;
@@ -168,21 +183,26 @@ int svref_kv_rollback(const svref_rollback_args* a);
 /* Dynamic draft length                                                   */
 /* ---------------------------------------------------------------------- */
 
-/* Per row, the last `window` rounds' (accepted, proposed) pairs.  Once the
- * window is full, every round: the draft length goes up by one when the
- * window's acceptance rate sum_acc / sum_prop is above up_num / up_den, down
- * by one when it is below down_num / down_den, within [k_min, k_max]
- * ([SSD] §3.2: raise k above 85 %, lower it below 70 %).  Rates are
- * compared as integer cross products, so the decision is exact. */
+/* Per row, the history of the rounds seen so far: the accepted count and the
+ * proposed draft length of each, oldest first.  Once `window` rounds have
+ * been seen, every round: the draft length goes up by one when the
+ * acceptance rate of the last `window` rounds, sum_acc / sum_prop, is above
+ * up_num / up_den, down by one when it is below down_num / down_den, within
+ * [k_min, k_max] ([SSD] §3.2: raise k above 85 %, lower it below 70 %).
+ * Rates are compared as integer cross products, so the decision is exact.
+ * A round whose k lies outside [k_min, k_max] or whose accepted count lies
+ * outside [0, k] is not recorded and leaves k as it is. */
 typedef struct {
   int32_t B, window, k_min, k_max;
   int32_t up_num, up_den, down_num, down_den;
-  const int32_t* accepted;  /* [B] this round's accepted count; a value
-                               outside [0, k] leaves the row unchanged     */
+  const int32_t* accepted;  /* [B] this round's accepted count             */
   int32_t* k_per_row;       /* [B] in: k used this round; out: next k      */
-  int32_t* state;           /* [B][window + 4]: filled count, oldest slot,
-                               sum of accepted, sum of proposed, then one
-                               slot per round: accepted | proposed << 16   */
+  int32_t* hist_accepted;   /* [B][capacity] accepted count of each round  */
+  int32_t* hist_proposed;   /* [B][capacity] k of each round               */
+  int32_t* hist_len;        /* [B] rounds recorded so far                  */
+  int32_t capacity;         /* rounds each history row holds; a row that is
+                               full when a round arrives makes the call
+                               return -1                                    */
 } svref_dynk_args;
 
 int svref_dynamic_k(const svref_dynk_args* a);

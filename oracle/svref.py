@@ -44,6 +44,7 @@ class VerifyArgs(C.Structure):
         ("diag_rho", _P), ("diag_acc_margin", _P), ("diag_cdf_margin", _P),
         ("diag_topp_margin_t", _P), ("diag_topp_margin_d", _P),
         ("diag_residual_mass", _P),
+        ("forced_accepted", _P), ("probe_token", _P), ("diag_probe", _P),
     ]
 
 
@@ -61,7 +62,9 @@ class RollbackArgs(C.Structure):
 class DynkArgs(C.Structure):
     _fields_ = [("B", C.c_int32), ("window", C.c_int32), ("k_min", C.c_int32), ("k_max", C.c_int32),
                 ("up_num", C.c_int32), ("up_den", C.c_int32), ("down_num", C.c_int32),
-                ("down_den", C.c_int32), ("accepted", _P), ("k_per_row", _P), ("state", _P)]
+                ("down_den", C.c_int32), ("accepted", _P), ("k_per_row", _P),
+                ("hist_accepted", _P), ("hist_proposed", _P), ("hist_len", _P),
+                ("capacity", C.c_int32)]
 
 
 _lib = None
@@ -183,14 +186,33 @@ def _verify_args(target, draft, draft_tokens, temperature, top_p, k_per_row,
     return a, keep, B, K
 
 
+def _take(x, sel):
+    if x is None:
+        return None
+    x = np.asarray(x)
+    return x if x.ndim == 0 else x[sel]
+
+
 def verify_sample(target, draft, draft_tokens, temperature, top_p=None,
                   k_per_row=None, seed=0, offset=0, flags=0, nthreads=1, V=None,
-                  row_ids=None):
+                  row_ids=None, forced_accepted=None, probe_token=None):
     """Sampled verification of every row; returns a dict of numpy outputs and
     the comparator diagnostics.  row_ids: the batch row index of each given
-    row (for checking a subset of a batch)."""
+    row (for checking a subset of a batch).
+
+    forced_accepted / probe_token ([B] int32): the what-if run -- the draw is
+    taken where forced_accepted says, and "probe" [B][4] gives the probe
+    token's interval {C_(t-1)/R, C_t/R, r_t/R, u} in the drawn distribution.
+    The returned dict's "rerun"(forced, probe, sel) repeats the call on the
+    rows `sel` (indices into this call's rows) with those inputs."""
     a, keep, B, K = _verify_args(target, draft, draft_tokens, temperature, top_p,
                                  k_per_row, seed, offset, flags, nthreads, V, row_ids)
+    if forced_accepted is not None:
+        keep["forced"] = np.ascontiguousarray(forced_accepted, dtype=np.int32).reshape(B)
+        a.forced_accepted = _ptr(keep["forced"])
+    if probe_token is not None:
+        keep["probe"] = np.ascontiguousarray(probe_token, dtype=np.int32).reshape(B)
+        a.probe_token = _ptr(keep["probe"])
     out = {
         "out_tokens": np.full((B, K + 1), -7, np.int32),
         "accepted": np.full(B, -7, np.int32),
@@ -213,9 +235,22 @@ def verify_sample(target, draft, draft_tokens, temperature, top_p=None,
     a.diag_topp_margin_t = _ptr(out["topp_margin_t"])
     a.diag_topp_margin_d = _ptr(out["topp_margin_d"])
     a.diag_residual_mass = _ptr(out["residual_mass"])
+    out["probe"] = np.full((B, 4), np.nan)
+    a.diag_probe = _ptr(out["probe"])
+    out["draft_tokens_in"] = keep["tok"].copy()
     rc = lib().svref_verify_sample(C.byref(a))
     if rc != 0:
         raise ValueError("svref_verify_sample rejected its arguments")
+
+    def rerun(forced, probe, sel):
+        sel = np.asarray(sel, dtype=np.int64)
+        ids = sel if row_ids is None else np.asarray(row_ids)[sel]
+        return verify_sample(_take(target, sel), _take(draft, sel), _take(draft_tokens, sel),
+                             _take(temperature, sel), _take(top_p, sel),
+                             _take(k_per_row, sel), seed, offset, flags, nthreads, V,
+                             row_ids=ids, forced_accepted=forced, probe_token=probe)
+
+    out["rerun"] = rerun
     return out
 
 
@@ -238,9 +273,11 @@ def verify_greedy(target, draft=None, draft_tokens=None, k_per_row=None, nthread
 
 
 def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=0,
-                 flags=0, nthreads=1, V=None, diagnostics=False):
+                 flags=0, nthreads=1, V=None, diagnostics=False, probe_tokens=None):
     """Draft tokens x_i ~ q'_i with draw 2 (int32 [B][k_max]) and row status;
-    with diagnostics=True also the CDF and top-p margins of every draw."""
+    with diagnostics=True also the CDF and top-p margins of every draw.
+    probe_tokens ([B][k_max]): also returns, last, each probe token's
+    interval {C_(t-1)/R, C_t/R, r_t/R, u} in q'_i ([B][k_max][4])."""
     draft, dt = _logits(draft)
     B, K, Vs = draft.shape
     # the argument block wants a target; point it at the draft (unused here)
@@ -256,12 +293,17 @@ def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=
     cdf = np.full((B, K), np.inf)
     topp = np.full((B, K), np.inf)
     a.diag_acc_margin, a.diag_topp_margin_d = _ptr(cdf), _ptr(topp)
+    probe = None
+    if probe_tokens is not None:
+        keep["probe"] = np.ascontiguousarray(probe_tokens, dtype=np.int32).reshape(B, K)
+        a.probe_token = _ptr(keep["probe"])
+        probe = np.full((B, K, 4), np.nan)
+        a.diag_probe = _ptr(probe)
     rc = lib().svref_draft_sample(C.byref(a), _ptr(toks))
     if rc != 0:
         raise ValueError("svref_draft_sample rejected its arguments")
-    if diagnostics:
-        return toks, st, cdf, topp
-    return toks, st
+    res = (toks, st) + ((cdf, topp) if diagnostics else ())
+    return res + (probe,) if probe is not None else res
 
 
 def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
@@ -298,19 +340,32 @@ def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
     return st
 
 
-def dynk_state(B, window=64):
-    """A fresh controller state: every row's window empty."""
-    return np.zeros((B, window + 4), np.int32)
+class DynkHistory:
+    """The controller's per-row history (oracle form): the accepted count and
+    proposed k of every round recorded so far, oldest first."""
+
+    def __init__(self, B, capacity):
+        self.accepted = np.zeros((B, capacity), np.int32)
+        self.proposed = np.zeros((B, capacity), np.int32)
+        self.length = np.zeros(B, np.int32)
+
+    def window(self, b, W):
+        """The last min(W, rounds) (accepted, proposed) pairs of row b, oldest first."""
+        n = int(self.length[b])
+        s = max(0, n - W)
+        return list(zip(self.accepted[b, s:n].tolist(), self.proposed[b, s:n].tolist()))
 
 
-def dynamic_k(accepted, k_per_row, state, window=64, k_min=2, k_max=8, up=(17, 20),
+def dynamic_k(accepted, k_per_row, hist, window=64, k_min=2, k_max=8, up=(17, 20),
               down=(7, 10)):
-    """One controller update, IN PLACE on k_per_row and state (numpy int32)."""
+    """One controller update, IN PLACE on k_per_row (numpy int32) and the
+    DynkHistory `hist`."""
     B = k_per_row.shape[0]
     acc = np.ascontiguousarray(accepted, dtype=np.int32)
     assert k_per_row.dtype == np.int32 and k_per_row.flags.c_contiguous
-    assert state.dtype == np.int32 and state.flags.c_contiguous and state.shape == (B, window + 4)
+    assert hist.accepted.shape[0] == B
     a = DynkArgs(B, window, k_min, k_max, up[0], up[1], down[0], down[1], _ptr(acc),
-                 _ptr(k_per_row), _ptr(state))
+                 _ptr(k_per_row), _ptr(hist.accepted), _ptr(hist.proposed), _ptr(hist.length),
+                 hist.accepted.shape[1])
     if lib().svref_dynamic_k(C.byref(a)) != 0:
         raise ValueError("svref_dynamic_k rejected its arguments")

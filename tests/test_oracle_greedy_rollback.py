@@ -224,3 +224,42 @@ def test_rollback_poisons_exactly_the_rejected_slots(oracle):
     for pos in (5, 6):
         expect[pt0[0, pos // ps], :, :, :, pos % ps, :] = oracle.POISON_BF16
     assert np.array_equal(pool, expect)
+
+
+@pytest.mark.parametrize("free_stack", [True, False])
+def test_rollback_flags_every_page_table_corruption(oracle, free_stack):
+    """The whole row of the page table is checked against the length: rows
+    of 70 tokens (5 pages of 16), 3 drafts of which 1 accepted (new length
+    68, so the rollback itself touches no page boundary).  Each row carries
+    one corruption; the expected flags follow from the rule: the first
+    ceil(old/ps) entries map pages of the pool, and, with a free stack, every
+    later entry is unmapped (without one, entries past the length are
+    free)."""
+    ps, MP, K = 16, 9, 3
+    corrupt = [
+        ("none", None, None, 0),
+        ("unmapped below the new length", 0, -1, 1),
+        ("unmapped in the middle", 2, -1, 1),
+        ("negative other than -1 below", 1, -5, 1),
+        ("beyond the pool below", 3, 10 ** 6, 1),
+        ("last used page unmapped", 4, -1, 1),
+        ("mapped just past the length", 5, 3, 1 if free_stack else 0),
+        ("mapped far past the length", 8, 3, 1 if free_stack else 0),
+        ("negative other than -1 past the length", 7, -2, 1 if free_stack else 0),
+    ]
+    B = len(corrupt)
+    lens = np.full(B, 70, np.int32)
+    pt, free, top, npages = page_setup(lens, ps, MP, spare=4)
+    for b, (_, pg, val, _) in enumerate(corrupt):
+        if pg is not None:
+            pt[b, pg] = val
+    kv = lens.copy()
+    acc = np.ones(B, np.int32)
+    if free_stack:
+        st = oracle.kv_rollback(kv, acc, pt, ps, K, free_pages=free, free_top=top,
+                                free_capacity=free.size, num_pages=npages)
+    else:
+        st = oracle.kv_rollback(kv, acc, pt, ps, K, num_pages=npages)
+    for b, (name, _, _, bad) in enumerate(corrupt):
+        assert st[b] == (oracle.ROW_BAD_PAGES if bad else 0), name
+        assert kv[b] == (70 if bad else 68), name

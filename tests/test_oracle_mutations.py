@@ -17,6 +17,7 @@ import tests.test_oracle_statistics as T_stats
 import tests.test_oracle_greedy_rollback as T_gr
 import tests.test_oracle_softmax_topp as T_sm
 import tests.test_oracle_dynk as T_dk
+import tests.test_oracle_diagnostics as T_dg
 
 SRC = open(obuild.SRC).read()
 
@@ -41,8 +42,8 @@ MUTANTS = [
     ("accept when u > rho",
      "if (!(u < rho)) { acc = i; break; }", "if (!(u > rho)) { acc = i; break; }", _pins_pmf),
     ("bonus drawn from the last draft position",
-     "    load_target(c, b, k);\n    svref_softmax_topp(c->z, V, T, P, c->pa, NULL, NULL, NULL);\n    y = inverse_cdf",
-     "    load_target(c, b, k - 1);\n    svref_softmax_topp(c->z, V, T, P, c->pa, NULL, NULL, NULL);\n    y = inverse_cdf",
+     "    load_target(c, b, k);\n    svref_softmax_topp(c->z, V, T, P, c->pa, NULL, NULL, NULL);\n    drawn = c->pa;",
+     "    load_target(c, b, k - 1);\n    svref_softmax_topp(c->z, V, T, P, c->pa, NULL, NULL, NULL);\n    drawn = c->pa;",
      _pins_pmf),
     ("draft side softmax at temperature 1",
      "svref_softmax_topp(c->z, V, T, Pq, c->qa, &G, &above, NULL);",
@@ -71,8 +72,46 @@ MUTANTS = [
      "if (sa * a->up_den >= (int64_t)a->up_num * sp) next = k + 1;",
      lambda o: T_dk.test_thresholds_are_strict()),
     ("controller acts before its window is full",
-     "if (st[0] == W) {\n      const int64_t sa", "if (st[0] >= W - 1) {\n      const int64_t sa",
+     "if (n >= W) {", "if (n >= W - 1) {",
      lambda o: T_dk.test_all_accepted_climbs_to_k_max_after_the_window_fills()),
+    ("controller window one round short",
+     "for (int32_t r = n - W; r < n; ++r)", "for (int32_t r = n - W + 1; r < n; ++r)",
+     lambda o: T_dk.test_window_forgets_the_oldest_round()),
+    ("controller records a k outside its range",
+     "if (k < a->k_min || k > a->k_max || acc < 0 || acc > k) continue;",
+     "if (acc < 0 || acc > k) continue;",
+     lambda o: [T_dk.test_k_outside_the_controllers_range_is_not_recorded(k) for k in (0, 9)]),
+    ("acceptance margin with its sign reversed",
+     "a->diag_acc_margin[(int64_t)b * K + i] = u - rho;\n    if (!(u < rho))",
+     "a->diag_acc_margin[(int64_t)b * K + i] = rho - u;\n    if (!(u < rho))",
+     lambda o: T_dg.test_acceptance_margin_is_u_minus_rho(o, 5e-6)),
+    ("CDF margin not relative to the drawn mass",
+     "double lo = fabs(prev / R - u), hi = fabs(C / R - u);",
+     "double lo = fabs(prev - u), hi = fabs(C - u);",
+     lambda o: T_dg.test_cdf_margin_of_the_residual_is_relative_to_its_mass(o, 5e-7)),
+    ("CDF margin to the upper edge only",
+     "*margin = lo < hi ? lo : hi;", "*margin = hi;",
+     lambda o: T_dg.test_cdf_margin_of_the_bonus_draw(o, 5e-7)),
+    ("top-p margin from the kept mass only",
+     "return m1 < m2 ? m1 : m2;", "return m2;",
+     lambda o: T_dg.test_topp_margin_when_the_mass_above_the_cut_is_near_top_p(o, 5e-7)),
+    ("top-p margin from the mass above the cut only",
+     "return m1 < m2 ? m1 : m2;", "return m1;",
+     lambda o: T_dg.test_topp_margin_when_the_kept_mass_is_near_top_p(o, 5e-7)),
+    ("probe interval starts after the token's own mass",
+     "    if (j == t) below = C;\n    C += r[j];", "    C += r[j];\n    if (j == t) below = C;",
+     lambda o: T_dg.test_forcing_the_oracles_own_count_changes_nothing(o)),
+    ("what-if run ignores the forced count",
+     "if (f >= 0 && f <= k) acc = f;", "if (f >= 0 && f < 0) acc = f;",
+     lambda o: T_dg.test_forced_count_draws_where_it_is_told(o)),
+    ("page check only near the rolled-back positions",
+     "        if (pg < used) {\n          if (e < 0",
+     "        if (pg < used && pg >= used - 1) {\n          if (e < 0",
+     lambda o: T_gr.test_rollback_flags_every_page_table_corruption(o, True)),
+    ("page check only just past the length",
+     "} else if (a->free_pages && e != -1) {",
+     "} else if (a->free_pages && e != -1 && pg == used) {",
+     lambda o: T_gr.test_rollback_flags_every_page_table_corruption(o, True)),
 ]
 
 
