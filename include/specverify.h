@@ -224,7 +224,9 @@ typedef struct {
                                are overwritten with SV_POISON_BF16           */
   int32_t num_layers, kv_heads, head_dim;
   int32_t* row_status;      /* [B] or NULL                                   */
-  void* workspace;          /* needed only with kv_pool                      */
+  void* workspace;          /* per-row decisions: at least
+                               sv_rollback_workspace_bytes(B) bytes (also
+                               when the call is fused into verification)    */
   size_t workspace_bytes;
 } sv_rollback_args;
 
@@ -242,8 +244,14 @@ sv_status sv_check_rollback_args(const sv_rollback_args* a);
  * to it fits the capacity; otherwise the row gets SV_ROW_FREE_OVERFLOW and is
  * left unchanged.  With free_pages = NULL nothing is released and only the
  * length shrinks ([SD] §4.3).  Rows failing a check (bad k, accepted, page
- * table) are left unchanged and flagged.  With kv_pool, the slots
- * [new, old) of committed rows are poisoned in every layer and head. */
+ * table) are left unchanged and flagged.  The page-table check covers the
+ * whole row: the first ceil(old/ps) entries must map pages in
+ * [0, num_pages) (any non-negative entry when num_pages is 0) and, with a
+ * free stack, every later entry must be -1, so that a row maps exactly
+ * ceil(new/ps) pages after its rollback ([SSD] §3.3 asserts that the write
+ * pointer equals the committed length); without a free stack, entries past
+ * the length are not constrained.  With kv_pool, the slots [new, old) of
+ * committed rows are poisoned in every layer and head. */
 sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s);
 
 /* Verification followed by the rollback of its rows, the two steps of one
@@ -276,8 +284,9 @@ typedef struct {
   int32_t B, window, k_min, k_max;
   int32_t up_num, up_den, down_num, down_den;
   const int32_t* accepted;  /* [B] from a verify call; a value outside
-                               [0, k] (a flagged row), or k > 32767, leaves
-                               the row as is                                */
+                               [0, k] (a flagged row), or a k outside
+                               [k_min, k_max], leaves the row as is (not
+                               recorded, k unchanged)                       */
   int32_t* k_per_row;       /* [B] in: k used this round; out: next round's
                                k (usable directly as the next call's
                                k_per_row)                                    */

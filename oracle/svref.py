@@ -273,7 +273,8 @@ def verify_greedy(target, draft=None, draft_tokens=None, k_per_row=None, nthread
 
 
 def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=0,
-                 flags=0, nthreads=1, V=None, diagnostics=False, probe_tokens=None):
+                 flags=0, nthreads=1, V=None, diagnostics=False, probe_tokens=None,
+                 row_ids=None):
     """Draft tokens x_i ~ q'_i with draw 2 (int32 [B][k_max]) and row status;
     with diagnostics=True also the CDF and top-p margins of every draw.
     probe_tokens ([B][k_max]): also returns, last, each probe token's
@@ -283,7 +284,7 @@ def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=
     # the argument block wants a target; point it at the draft (unused here)
     a, keep, _, _ = _verify_args(np.zeros((B, K + 1, 1), draft.dtype), None, None,
                                  temperature, top_p, k_per_row, seed, offset, flags,
-                                 nthreads)
+                                 nthreads, row_ids=row_ids)
     a.V = Vs if V is None else V
     a.draft, a.draft_vec_stride = _ptr(draft), Vs
     a.dtype = dt
@@ -348,6 +349,20 @@ class DynkHistory:
         self.accepted = np.zeros((B, capacity), np.int32)
         self.proposed = np.zeros((B, capacity), np.int32)
         self.length = np.zeros(B, np.int32)
+
+    def windows(self, W):
+        """Every row's last min(W, rounds) rounds as [B][W] accepted and
+        proposed arrays (oldest first, -1 past the row's count) and the
+        counts."""
+        B = self.length.shape[0]
+        n = np.minimum(self.length, W)
+        acc = np.full((B, W), -1, np.int32)
+        prop = np.full((B, W), -1, np.int32)
+        for b in range(B):
+            L = int(self.length[b])
+            acc[b, :n[b]] = self.accepted[b, L - n[b]:L]
+            prop[b, :n[b]] = self.proposed[b, L - n[b]:L]
+        return acc, prop, n
 
     def window(self, b, W):
         """The last min(W, rounds) (accepted, proposed) pairs of row b, oldest first."""

@@ -5,6 +5,7 @@ HIP stream; every step of the computation runs in the library's kernels.
 The library must have been built (rejection_sampling_verify_11_amd/build.py);
 there is no fallback of any kind.
 """
+import contextlib
 import ctypes as C
 import os
 import threading
@@ -391,25 +392,37 @@ class VerifyCall:
         return self.outputs
 
 
+def _allocating_on(stream):
+    """The one-shot calls below allocate their workspace and outputs and drop
+    the workspace as soon as the launches are queued.  Allocated under the
+    stream the kernels run on, the caching allocator hands that memory only to
+    later work on the same stream, which runs after them."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def verify_sample(target, draft, draft_tokens, temperature, top_p=None, k_per_row=None,
                   seed=0, offset=0, flags=0, stream=None):
     """Rejection-sampling verification (sv_verify_sample).  Returns a dict of
     device tensors: out_tokens, accepted, num_emitted, p_at_draft, q_at_draft,
-    row_status."""
-    return VerifyCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
-                      seed, offset, flags).run(stream)
+    row_status (allocated on `stream` when one is given)."""
+    with _allocating_on(stream):
+        return VerifyCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
+                          seed, offset, flags).run(stream)
 
 
 def verify_greedy(target, draft_tokens=None, draft=None, k_per_row=None, stream=None):
     """Greedy verification (sv_verify_greedy)."""
-    return VerifyCall("greedy", target, draft, draft_tokens, None, None, k_per_row).run(stream)
+    with _allocating_on(stream):
+        return VerifyCall("greedy", target, draft, draft_tokens, None, None,
+                          k_per_row).run(stream)
 
 
 def draft_sample(draft, temperature, top_p=None, k_per_row=None, seed=0, offset=0, flags=0,
                  stream=None):
     """Draft tokens ~ q' with draw 2 (sv_draft_sample); returns (tokens, row_status)."""
-    out = VerifyCall("draft", None, draft, None, temperature, top_p, k_per_row, seed, offset,
-                     flags).run(stream)
+    with _allocating_on(stream):
+        out = VerifyCall("draft", None, draft, None, temperature, top_p, k_per_row, seed,
+                         offset, flags).run(stream)
     return out["draft_tokens"], out["row_status"]
 
 
@@ -439,7 +452,6 @@ class RollbackCall:
             _i32(free_top, (1,), "free_top", dev)
             a.free_pages, a.free_top = _ptr(free_pages), _ptr(free_top)
             a.free_capacity = free_pages.numel()
-        self.workspace = None
         if kv_pool is not None:
             if kv_pool.dtype != torch.bfloat16 or not kv_pool.is_contiguous():
                 raise ValueError("kv_pool must be a contiguous bfloat16 tensor")
@@ -447,9 +459,9 @@ class RollbackCall:
             a.num_layers, a.kv_heads, a.head_dim = int(num_layers), int(kv_heads), int(head_dim)
             if a.num_pages == 0:
                 a.num_pages = kv_pool.shape[0]
-            nbytes = library().sv_rollback_workspace_bytes(B)
-            self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-            a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
+        nbytes = library().sv_rollback_workspace_bytes(B)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
         self.row_status = torch.empty(B, dtype=torch.int32, device=dev)
         a.row_status = _ptr(self.row_status)
         self._keep = (kv_len, accepted, page_table, k_per_row, free_pages, free_top, kv_pool)
@@ -470,9 +482,11 @@ def kv_rollback(kv_len, accepted, page_table, page_size, k_max, k_per_row=None,
                 kv_heads=0, head_dim=0, stream=None):
     """KV pointer / page-table rollback (sv_kv_rollback), in place on the
     given device tensors.  Returns the row_status tensor."""
-    call = RollbackCall(kv_len, accepted, page_table, page_size, k_max, k_per_row, free_pages,
-                        free_top, kv_pool, num_pages, num_layers, kv_heads, head_dim)
-    return call.run(stream)
+    with _allocating_on(stream):
+        call = RollbackCall(kv_len, accepted, page_table, page_size, k_max, k_per_row,
+                            free_pages, free_top, kv_pool, num_pages, num_layers, kv_heads,
+                            head_dim)
+        return call.run(stream)
 
 
 def advance_offset(offset, delta=1, stream=None):
@@ -644,14 +658,16 @@ def verify_sample_sharded(target, draft, draft_tokens, temperature, top_p=None, 
                           shards=8, seed=0, offset=0, flags=0, sharded_draw=True, stream=None):
     """verify_sample with the statistics computed shard by shard and merged,
     and (sharded_draw) the draw split over the shards as well."""
-    return ShardedCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
-                       shards, seed, offset, flags, sharded_draw).run(stream)
+    with _allocating_on(stream):
+        return ShardedCall("sample", target, draft, draft_tokens, temperature, top_p,
+                           k_per_row, shards, seed, offset, flags, sharded_draw).run(stream)
 
 
 def draft_sample_sharded(draft, temperature, top_p=None, k_per_row=None, shards=8, seed=0,
                          offset=0, flags=0, stream=None):
     """draft_sample with the statistics computed shard by shard and merged."""
-    out = ShardedCall("draft", None, draft, None, temperature, top_p, k_per_row, shards, seed,
-                      offset, flags).run(stream)
+    with _allocating_on(stream):
+        out = ShardedCall("draft", None, draft, None, temperature, top_p, k_per_row, shards,
+                          seed, offset, flags).run(stream)
     return out["draft_tokens"], out["row_status"]
 

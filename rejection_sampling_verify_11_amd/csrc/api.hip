@@ -331,10 +331,10 @@ sv_status sv_check_rollback_args(const sv_rollback_args* a) {
   if (a->B == 0) return SV_OK;
   if (!a->kv_len || !a->accepted || !a->page_table) return SV_E_ARG;
   if (a->free_pages && (!a->free_top || a->free_capacity < 0)) return SV_E_ARG;
-  if (a->kv_pool) {
-    if (a->num_pages < 1 || a->num_layers < 1 || a->kv_heads < 1 || a->head_dim < 1) return SV_E_ARG;
-    if (!a->workspace || a->workspace_bytes < sv_rollback_workspace_bytes(a->B)) return SV_E_WORKSPACE;
-  }
+  if (a->kv_pool &&
+      (a->num_pages < 1 || a->num_layers < 1 || a->kv_heads < 1 || a->head_dim < 1))
+    return SV_E_ARG;
+  if (!a->workspace || a->workspace_bytes < sv_rollback_workspace_bytes(a->B)) return SV_E_WORKSPACE;
   return SV_OK;
 }
 

@@ -736,15 +736,16 @@ __device__ __forceinline__ int row_header(const FinalizeParams& p, int b, RowSha
 // Used when the cache has no free stack and no pool: the rollback of one row
 // then needs nothing from the others, and is the rollback kernel's decision
 // for that row ([SSD] §3.3: the write pointer moves back to the accepted
-// prefix; the pages holding the dropped positions must be mapped), taken on
-// the accepted count the row's verification just found (-1 for a flagged
-// row).  Wave 0 takes the decision after the header and loads the page
-// entries it checks (a lane per page), so that their latency overlaps the
-// draw; the entries are tested, and the length written, at the end.
+// prefix, and the page table must agree with the length: the first
+// ceil(old/ps) entries map pages of the pool; past the length, entries are
+// free without a free stack), taken on the accepted count the row's
+// verification just found (-1 for a flagged row).  Every thread loads one
+// page entry after the header, so that the loads overlap the draw; the
+// entries are tested, and the length written, at the end.
 struct RollCheck {
   uint32_t st;
-  int new_len, first, used;
-  int32_t e;  // page entry first + lane (when below used)
+  int new_len, used;
+  int32_t e;  // page entry threadIdx.x (when below used)
 };
 
 __device__ __forceinline__ int ceil_div_i(int x, int d) { return (x + d - 1) / d; }
@@ -759,21 +760,22 @@ __device__ __forceinline__ RollCheck roll_begin(const FinalizeParams& p, int b, 
   if (old < 0 || ceil_div_i(old, p.ps) > p.MP) r.st |= SV_ROW_BAD_PAGES;
   r.new_len = r.st ? old : old - (k - acc);
   r.used = r.st ? 0 : ceil_div_i(old, p.ps);
-  r.first = r.st ? 0 : r.new_len / p.ps;
   // clamped into the row (used <= MP), loaded whether or not it is tested
-  const int pg = min(r.first + (int)(threadIdx.x & 63), max(r.used - 1, 0));
+  const int pg = min((int)threadIdx.x, max(r.used - 1, 0));
   r.e = p.page_table[(int64_t)b * p.MP + pg];
   return r;
 }
 
+// Called by every thread of the workgroup.
+template <int NT>
 __device__ __forceinline__ void roll_end(const FinalizeParams& p, int b, const RollCheck& r) {
-  const int l = threadIdx.x & 63;
+  const int tid = threadIdx.x;
   auto bad_entry = [&](int32_t e) { return e < 0 || (p.num_pages > 0 && e >= p.num_pages); };
-  bool bad = r.first + l < r.used && bad_entry(r.e);
-  for (int pg = r.first + 64 + l; pg < r.used; pg += 64)  // more than 64 pages dropped (rare)
+  bool bad = tid < r.used && bad_entry(r.e);
+  for (int pg = tid + NT; pg < r.used; pg += NT)  // contexts beyond NT pages
     bad = bad || bad_entry(p.page_table[(int64_t)b * p.MP + pg]);
-  const uint32_t st = r.st | (__any(bad) ? (uint32_t)SV_ROW_BAD_PAGES : 0u);
-  if (l == 0) {
+  const uint32_t st = r.st | (__syncthreads_or(bad) ? (uint32_t)SV_ROW_BAD_PAGES : 0u);
+  if (tid == 0) {
     if (!st) p.kv_len[b] = r.new_len;
     if (p.roll_status) p.roll_status[b] = (int32_t)st;
   }
@@ -785,13 +787,13 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
   __shared__ RowShared rs;
   const int b = blockIdx.x, K = p.K, V = p.V, tid = threadIdx.x;
   // the KV length loads with the header's loads
-  const int old = ROLL && tid < 64 ? p.kv_len[b] : 0;
+  const int old = ROLL ? p.kv_len[b] : 0;
   const int x = row_header<true>(p, b, rs);
   __syncthreads();
   RollCheck rc;
-  if (ROLL && tid < 64) rc = roll_begin(p, b, rs, old);
+  if (ROLL) rc = roll_begin(p, b, rs, old);
   if (!rs.go) {
-    if (ROLL && tid < 64) roll_end(p, b, rc);
+    if (ROLL) roll_end<NT>(p, b, rc);
     return;
   }
   const int acc = rs.acc, mode = rs.mode;
@@ -814,8 +816,8 @@ __global__ __launch_bounds__(NT) void finalize_sample_kernel(FinalizeParams p) {
       if (p.num_emitted) p.num_emitted[b] = acc + 1;
       if (p.row_status) p.row_status[b] = 0;
     }
-    if (ROLL) roll_end(p, b, rc);
   }
+  if (ROLL) roll_end<NT>(p, b, rc);
 }
 
 // Draft sampling: one workgroup per (row, draft position).  The header

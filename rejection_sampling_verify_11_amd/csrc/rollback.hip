@@ -8,12 +8,16 @@
 // sequence.  [SD] §4.3: with a preallocated slot per request only the valid
 // length shrinks.
 //
-// One workgroup walks the rows in tiles of 1024: per-row checks, the new
-// length, the number of whole pages released, and an exclusive scan of the
-// releases (valid rows only) that gives every row its slots on the free
-// stack in (row, page) order.  A row whose releases would pass the stack
-// capacity is flagged and left unchanged.  With a KV pool the decision is
-// written to the workspace first, a second kernel poisons the rolled-back
+// The decision is taken by one wave per row: the row's checks, the new
+// length, the number of whole pages released, and the check of the whole
+// page-table row against the old length (every logical page below
+// ceil(old/ps) maps a page of the pool; with a free stack every later entry
+// is unmapped, so the row maps exactly ceil(new/ps) pages afterwards).  Then
+// one workgroup walks the rows in tiles of 1024: an exclusive scan of the
+// releases (valid rows only) gives every row its slots on the free stack in
+// (row, page) order, and a row whose releases would pass the stack capacity
+// is flagged and left unchanged.  With a KV pool the scan writes its
+// decisions to the workspace first, a second kernel poisons the rolled-back
 // slots while the page table still maps them, and a third commits.
 #include "sv_internal.h"
 
@@ -22,47 +26,47 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kCheckRows = 4;  // rows (waves) per check workgroup
 
 __device__ __forceinline__ int ceil_div(int x, int d) { return (x + d - 1) / d; }
 
-struct Decision {
-  uint32_t st;
-  int new_len, old_len, nrel;
-};
-
-__device__ Decision decide_row(const RollbackParams& p, int b) {
-  Decision d;
-  d.st = 0;
-  d.nrel = 0;
+// One wave per row.  The record holds the status, the new and old lengths
+// and the number of pages the row releases.
+__global__ __launch_bounds__(64 * kCheckRows) void rollback_check_kernel(RollbackParams p) {
+  const int b = blockIdx.x * kCheckRows + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (b >= p.B) return;
   const int k = p.k_per_row ? p.k_per_row[b] : p.K;
   const int acc = p.accepted[b];
   const int old = p.kv_len[b];
-  d.old_len = old;
-  d.new_len = old;
-  if (k < 1 || k > p.K) d.st |= SV_ROW_BAD_K;
-  else if (acc < 0 || acc > k || old - (k - acc) < 0) d.st |= SV_ROW_BAD_ACCEPTED;
-  if (old < 0 || ceil_div(old, p.ps) > p.MP) d.st |= SV_ROW_BAD_PAGES;
-  if (!d.st) {
-    // the pages holding the rolled-back positions must be mapped, and, when
-    // pages are released, the first entry past the old length must be
-    // unmapped (without a free stack pages past the length stay mapped)
-    const int nl = old - (k - acc);
+  uint32_t st = 0;
+  if (k < 1 || k > p.K) st |= SV_ROW_BAD_K;
+  else if (acc < 0 || acc > k || old - (k - acc) < 0) st |= SV_ROW_BAD_ACCEPTED;
+  if (old < 0 || ceil_div(old, p.ps) > p.MP) st |= SV_ROW_BAD_PAGES;
+  if (!st) {
     const int used = ceil_div(old, p.ps);
     const int32_t* row = p.page_table + (int64_t)b * p.MP;
-    for (int pg = nl / p.ps; pg < used; ++pg) {
-      const int e = row[pg];
-      if (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) d.st |= SV_ROW_BAD_PAGES;
+    // past the length only a free stack constrains the entries
+    const int span = p.free_pages ? p.MP : used;
+    bool bad = false;
+    for (int pg = l; pg < span; pg += 64) {
+      const int32_t e = row[pg];
+      bad = bad || (pg < used ? (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) : e != -1);
     }
-    if (p.free_pages && used < p.MP && row[used] != -1) d.st |= SV_ROW_BAD_PAGES;
+    if (__any(bad)) st |= SV_ROW_BAD_PAGES;
   }
-  if (!d.st) {
-    d.new_len = old - (k - acc);
-    d.nrel = ceil_div(old, p.ps) - ceil_div(d.new_len, p.ps);
+  if (l == 0) {
+    RollRec r;
+    r.status = (int32_t)st;
+    r.old_len = old;
+    r.new_len = st ? old : old - (k - acc);
+    r.aux = st ? 0 : ceil_div(old, p.ps) - ceil_div(r.new_len, p.ps);
+    p.recs[b] = r;
   }
-  return d;
 }
 
-// phase 0: decide and commit; phase 1: decide into p.recs only.
+// phase 0: scan and commit; phase 1: scan into p.recs only (aux becomes the
+// row's first slot on the free stack, status the final status).
 __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, int phase) {
   __shared__ int wsum[kWaves];
   __shared__ int wmax[kWaves];
@@ -72,10 +76,11 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, in
   int pushed = 0;    // running total at the last committed row that released
   for (int t0 = 0; t0 < p.B; t0 += kThreads) {
     const int b = t0 + tid;
-    Decision d;
-    d.st = 0; d.nrel = 0; d.new_len = 0; d.old_len = 0;
-    if (b < p.B) d = decide_row(p, b);
-    const int rel = (b < p.B && !d.st) ? d.nrel : 0;
+    RollRec d;
+    d.status = 0; d.aux = 0; d.new_len = 0; d.old_len = 0;
+    if (b < p.B) d = p.recs[b];
+    uint32_t st = (uint32_t)d.status;
+    const int rel = (b < p.B && !st) ? d.aux : 0;
     // inclusive scan of rel across the block
     int inc = rel;
 #pragma unroll
@@ -92,21 +97,19 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, in
     }
     __syncthreads();
     const int running = before + inc;  // inclusive, over valid rows
-    if (b < p.B && !d.st && p.free_pages && rel > 0 &&
+    if (b < p.B && !st && p.free_pages && rel > 0 &&
         (top0 < 0 || (int64_t)top0 + running > (int64_t)p.free_capacity))
-      d.st |= SV_ROW_FREE_OVERFLOW;
-    const bool commit = b < p.B && !d.st;
+      st |= SV_ROW_FREE_OVERFLOW;
+    const bool commit = b < p.B && !st;
     const int push_base = top0 + running - rel;
     int my_pushed = (commit && p.free_pages && rel > 0) ? running : 0;
     if (phase == 1) {
       if (b < p.B) {
-        RollRec r;
-        r.committed = commit ? 1 : 0;
-        r.new_len = d.new_len;
-        r.old_len = d.old_len;
-        r.push_base = push_base;
+        RollRec r = d;
+        r.status = (int32_t)st;
+        r.aux = push_base;
         p.recs[b] = r;
-        if (p.row_status) p.row_status[b] = (int32_t)d.st;
+        if (p.row_status) p.row_status[b] = (int32_t)st;
       }
     } else {
       if (commit) {
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, in
         }
         p.kv_len[b] = d.new_len;
       }
-      if (b < p.B && p.row_status) p.row_status[b] = (int32_t)d.st;
+      if (b < p.B && p.row_status) p.row_status[b] = (int32_t)st;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) my_pushed = max(my_pushed, __shfl_xor(my_pushed, o, 64));
@@ -144,16 +147,16 @@ __global__ __launch_bounds__(kThreads) void rollback_commit_kernel(RollbackParam
     int my_pushed = 0;
     if (b < p.B) {
       const RollRec r = p.recs[b];
-      if (r.committed) {
+      if (r.status == 0) {
         int32_t* row = p.page_table + (int64_t)b * p.MP;
         if (p.free_pages) {
           const int first = ceil_div(r.new_len, p.ps);
           const int rel = ceil_div(r.old_len, p.ps) - first;
           for (int j = 0; j < rel; ++j) {
-            p.free_pages[r.push_base + j] = row[first + j];
+            p.free_pages[r.aux + j] = row[first + j];
             row[first + j] = -1;
           }
-          if (rel > 0) my_pushed = r.push_base + rel - top0;
+          if (rel > 0) my_pushed = r.aux + rel - top0;
         }
         p.kv_len[b] = r.new_len;
       }
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void rollback_commit_kernel(RollbackParam
 __global__ __launch_bounds__(256) void poison_kernel(RollbackParams p) {
   const int b = blockIdx.x / p.L, layer = blockIdx.x % p.L;
   const RollRec r = p.recs[b];
-  if (!r.committed) return;
+  if (r.status != 0) return;
   const int nslots = r.old_len - r.new_len;
   const int per_slot = 2 * p.H * p.D;
   const int32_t* row = p.page_table + (int64_t)b * p.MP;
@@ -192,6 +195,13 @@ __global__ __launch_bounds__(256) void poison_kernel(RollbackParams p) {
 
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t) {
   if (p.B == 0) return hipSuccess;
+  {
+    TimedScope ts(t, "rollback_check", s);
+    hipLaunchKernelGGL(rollback_check_kernel, dim3((p.B + kCheckRows - 1) / kCheckRows),
+                       dim3(64 * kCheckRows), 0, s, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (!p.kv_pool) {
     TimedScope ts(t, "rollback", s);
     hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 0);
@@ -201,7 +211,7 @@ hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t) {
     TimedScope ts(t, "rollback_decide", s);
     hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 1);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.L > 0 && p.H > 0 && p.D > 0) {
     TimedScope ts(t, "rollback_poison", s);

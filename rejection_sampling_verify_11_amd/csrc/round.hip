@@ -21,8 +21,9 @@ __global__ void dynk_kernel(DynkParams p) {
   const int32_t k = p.k_per_row[b];
   const int32_t acc = p.accepted[b];
   // A flagged row (accepted outside [0, k]) teaches nothing; neither does a
-  // k too large for the 15-bit proposed field of a slot.
-  if (acc < 0 || acc > k || k > 0x7FFF) return;
+  // k the controller could not have chosen (outside [k_min, k_max]).  The
+  // host keeps k_max <= SV_MAX_K, so a slot's 16-bit fields always suffice.
+  if (k < p.k_min || k > p.k_max || acc < 0 || acc > k) return;
   int32_t filled = st[0], oldest = st[1], sa = st[2], sp = st[3];
   if (filled < W) {
     st[4 + (oldest + filled) % W] = acc | (k << 16);

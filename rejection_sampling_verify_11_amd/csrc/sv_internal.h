@@ -43,10 +43,11 @@ constexpr uint32_t kSawFinite = 1u << 31;
 
 // Rollback decision per row, used when the pool is poisoned.
 struct RollRec {
-  int32_t committed;  // 1 if the row is rolled back
+  int32_t status;   // row status; 0 = the row is rolled back
   int32_t new_len;
   int32_t old_len;
-  int32_t push_base;  // index on the free stack of the row's first release
+  int32_t aux;      // pages released (after the check), then the index on
+                    // the free stack of the row's first release (after the scan)
 };
 static_assert(sizeof(RollRec) == 16, "RollRec layout");
 

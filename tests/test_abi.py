@@ -151,12 +151,15 @@ def test_rollback_validation():
     a = _abi.RollbackArgs()
     a.B, a.k_max, a.page_size, a.max_pages_per_seq = 4, 8, 16, 10
     a.kv_len = a.accepted = a.page_table = 0x10000
+    # the per-row decisions go to the workspace, with or without a pool
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_WORKSPACE
+    a.workspace, a.workspace_bytes = 0x10000, L.sv_rollback_workspace_bytes(4) - 1
+    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_WORKSPACE
+    a.workspace_bytes = L.sv_rollback_workspace_bytes(4)
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_OK
     a.kv_pool = 0x10000
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG  # pool without sizes
     a.num_pages, a.num_layers, a.kv_heads, a.head_dim = 10, 2, 2, 8
-    assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_WORKSPACE
-    a.workspace, a.workspace_bytes = 0x10000, L.sv_rollback_workspace_bytes(4)
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_OK
     a.free_pages = 0x10000
     assert L.sv_check_rollback_args(C.byref(a)) == _abi.SV_E_ARG  # stack without height
@@ -176,6 +179,7 @@ def test_verify_rollback_validation():
         r.B, r.k_max, r.page_size, r.max_pages_per_seq = 4, 3, 16, 10
         r.kv_len = r.page_table = 0x20000
         r.accepted = v.accepted
+        r.workspace, r.workspace_bytes = 0x40000, L.sv_rollback_workspace_bytes(4)
         return r
 
     chk = lambda r: L.sv_check_verify_rollback_args(C.byref(v), C.byref(r))

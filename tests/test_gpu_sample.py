@@ -12,7 +12,7 @@ import torch
 
 import rejection_sampling_verify_11_amd as sv
 from rejection_sampling_verify_11_amd import workloads as W
-from tests.parity import Report, compare_sample
+from tests.parity import Report, compare_draft, compare_sample
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -31,6 +31,19 @@ def oracle_tokens(oracle, inp, seed, offset, flags=0):
                                    seed=seed, offset=offset, flags=flags, nthreads=NT)
     assert np.all(st == 0)
     return toks
+
+
+def check_draft(oracle, draft_host, T, P, kk, seed, offset, g_toks, g_st, flags=0,
+                row_ids=None, nthreads=NT):
+    """The GPU's draft tokens against the oracle's draft sampler; a differing
+    token must sit on a flagged draw, with its interval in q' within the band
+    of u.  row_ids: the batch row of each given row (a subset of a batch).
+    Returns the oracle's tokens and the number of differences."""
+    gt = g_toks.cpu().numpy() if hasattr(g_toks, "cpu") else np.asarray(g_toks)
+    o_toks, o_st, cdf, topp, probe = oracle.draft_sample(
+        draft_host, T, P, kk, seed=seed, offset=offset, flags=flags, nthreads=nthreads,
+        diagnostics=True, probe_tokens=gt, row_ids=row_ids)
+    return o_toks, compare_draft(gt, g_st, o_toks, o_st, cdf, topp, probe)
 
 
 def oracle_verify(oracle, inp, toks, seed, offset, flags=0, rows=None):
@@ -74,7 +87,8 @@ def test_workload1_fp32_all_rounds(oracle):
         toks = oracle_tokens(oracle, inp, 0, r)
         rep.merge(check_round(oracle, inp, toks, 0, r))
     print("workload1:", rep)
-    assert rep.rows == 1000 and rep.exact_rows + rep.flagged_rows == 1000
+    assert rep.rows == 1000
+    rep.bound()
 
 
 def test_workload2_bf16_peaky(oracle):
@@ -135,8 +149,8 @@ def test_workload5_full_batch_sampled_rows(oracle):
     sel = np.linspace(0, B - 1, 16).astype(np.int64)
     rep = check_round(oracle, inp, toks.cpu().numpy(), 0, 0, rows=sel)
     print("workload5 full:", rep)
-    assert rep.rows == 16 and rep.exact_rows + rep.flagged_rows == 16
-    assert rep.excused_mismatches <= 1
+    assert rep.rows == 16
+    rep.bound()
 
 
 @pytest.mark.parametrize("V,dtype,top_p,stride_pad", [
@@ -277,12 +291,9 @@ def test_vectors_filled_with_one_value(oracle, case):
     d = to_dev(inp)
     g_toks, g_st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=21, offset=1)
     torch.cuda.synchronize()
-    o_toks, o_st, cdf, topp = oracle.draft_sample(
-        W.host_logits(inp.draft), inp.temperature.numpy(), inp.top_p.numpy(), seed=21, offset=1,
-        nthreads=NT, diagnostics=True)
-    assert np.array_equal(g_st.cpu().numpy(), o_st)
-    flagged = (cdf < 1e-6) | (topp < 1e-6)
-    assert np.array_equal(g_toks.cpu().numpy()[~flagged], o_toks[~flagged])
+    _, nd = check_draft(oracle, W.host_logits(inp.draft), inp.temperature.numpy(),
+                        inp.top_p.numpy(), None, 21, 1, g_toks, g_st)
+    assert nd <= 1
 
 
 BF16_MIN = -3.3895313892515355e38  # the most negative finite bf16, a common mask value
@@ -343,12 +354,9 @@ def test_negative_logits_above_the_window(oracle, case):
     d = to_dev(inp)
     g_toks, g_st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=23, offset=1)
     torch.cuda.synchronize()
-    o_toks, o_st, cdf, topp = oracle.draft_sample(
-        W.host_logits(inp.draft), inp.temperature.numpy(), inp.top_p.numpy(), seed=23, offset=1,
-        nthreads=NT, diagnostics=True)
-    assert np.array_equal(g_st.cpu().numpy(), o_st)
-    flagged = (cdf < 1e-6) | (topp < 1e-6)
-    assert np.array_equal(g_toks.cpu().numpy()[~flagged], o_toks[~flagged])
+    _, nd = check_draft(oracle, W.host_logits(inp.draft), inp.temperature.numpy(),
+                        inp.top_p.numpy(), None, 23, 1, g_toks, g_st)
+    assert nd <= 1
 
 
 def test_values_below_the_count_window(oracle):
@@ -396,8 +404,7 @@ def test_values_below_the_count_window(oracle):
         toks = oracle_tokens(oracle, inp, 3, r)
         rep.merge(check_round(oracle, inp, toks, 3, r))
     print("below-window:", rep)
-    assert rep.exact_rows + rep.flagged_rows == rep.rows
-    assert rep.exact_rows >= rep.rows - 2
+    rep.bound(max_excused=2)
 
 
 def test_top_p_cut_on_one_side_only(oracle):
@@ -419,8 +426,7 @@ def test_top_p_cut_on_one_side_only(oracle):
         print("one-sided cut:", rep)
         # the flat side's many tied tokens put some draws near a CDF edge
         # (flagged); those must still agree unless a mismatch is excused
-        assert rep.exact_rows + rep.flagged_rows == rep.rows
-        assert rep.excused_mismatches <= 1
+        rep.bound(max_excused=1)
 
 
 def test_degenerate_distributions(oracle):
@@ -514,14 +520,10 @@ def test_draft_sampler_parity(oracle):
         d = to_dev(inp)
         g_toks, g_st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=seed, offset=3)
         torch.cuda.synchronize()
-        o_toks, o_st, cdf, topp = oracle.draft_sample(
-            W.host_logits(inp.draft), inp.temperature.numpy(),
-            None if inp.top_p is None else inp.top_p.numpy(), seed=seed, offset=3,
-            nthreads=NT, diagnostics=True)
-        assert np.array_equal(g_st.cpu().numpy(), o_st)
-        gt = g_toks.cpu().numpy()
-        flagged = (cdf < 1e-6) | (topp < 1e-6)
-        assert np.array_equal(gt[~flagged], o_toks[~flagged])
+        _, nd = check_draft(oracle, W.host_logits(inp.draft), inp.temperature.numpy(),
+                            None if inp.top_p is None else inp.top_p.numpy(), None, seed, 3,
+                            g_toks, g_st)
+        assert nd <= 1
 
 
 @pytest.mark.parametrize("case", range(24))
@@ -555,16 +557,12 @@ def test_random_configuration_sweep(oracle, case):
     d_T, d_P = T.to(DEV), None if P is None else P.to(DEV)
     d_k = None if kk is None else kk.to(DEV)
     # draft sampling on both sides
-    o_toks, o_st, cdf, topp = oracle.draft_sample(
-        W.host_logits(host.draft), T.numpy(), None if P is None else P.numpy(),
-        None if kk is None else kk.numpy(), seed=seed, offset=offset, flags=flags, nthreads=NT,
-        diagnostics=True)
     g_toks, g_st = sv.draft_sample(d_d, d_T, d_P, d_k, seed=seed, offset=offset, flags=flags)
     torch.cuda.synchronize()
-    assert np.array_equal(g_st.cpu().numpy(), o_st)
-    gt = g_toks.cpu().numpy()
-    flagged = (cdf < 1e-6) | (topp < 1e-6)
-    assert np.array_equal(gt[~flagged], o_toks[~flagged])
+    o_toks, nd = check_draft(oracle, W.host_logits(host.draft), T.numpy(),
+                             None if P is None else P.numpy(), None if kk is None else kk.numpy(),
+                             seed, offset, g_toks, g_st, flags)
+    assert nd <= 1
     # verification of the oracle's draft tokens
     out = sv.verify_sample(d_t, d_d, torch.from_numpy(o_toks).to(DEV), d_T, d_P, d_k, seed=seed,
                            offset=offset, flags=flags)
@@ -572,8 +570,7 @@ def test_random_configuration_sweep(oracle, case):
     o = oracle_verify(oracle, host, o_toks, seed, offset, flags)
     rep = compare_sample(out, o, kk, K)
     print("sweep case", case, (B, K, V, str(dtype), pad, mode, kk is not None), rep)
-    assert rep.exact_rows + rep.flagged_rows + rep.error_rows == rep.rows
-    assert rep.excused_mismatches <= 1
+    rep.bound(max_excused=1)
 
 
 # token positions around the segment (2048) and group (16384 / 32768) edges
@@ -619,3 +616,25 @@ def test_pprime_draws_find_a_single_hot_token(oracle, B):
     assert np.array_equal(out["out_tokens"].cpu().numpy()[:, K], np.asarray(bonus))
     o = oracle_verify(oracle, inp, expect, 6, 2, rows=rows)
     assert np.array_equal(o["out_tokens"][:, K], np.asarray(bonus)[rows])
+
+
+def test_one_shot_call_on_a_side_stream(oracle):
+    """verify_sample and draft_sample launched on a side stream while the
+    current stream allocates and fills memory right away: the calls' own
+    workspaces must not be handed to that work while their kernels run."""
+    inp = W.workload4(7, B=16, V=60000)
+    d = to_dev(inp)
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    toks, st = sv.draft_sample(d.draft, d.temperature, d.top_p, seed=4, offset=9, stream=side)
+    out = sv.verify_sample(d.target, d.draft, toks, d.temperature, d.top_p, seed=4, offset=9,
+                           stream=side)
+    # allocation pressure on the current stream while the side stream works
+    junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device=DEV) for _ in range(64)]
+    torch.cuda.synchronize()
+    del junk
+    _, nd = check_draft(oracle, W.host_logits(inp.draft), inp.temperature.numpy(),
+                        inp.top_p.numpy(), None, 4, 9, toks, st)
+    assert nd <= 1
+    o = oracle_verify(oracle, inp, toks.cpu().numpy(), 4, 9)
+    compare_sample(out, o, None, inp.draft.shape[1]).bound()
