@@ -184,6 +184,23 @@ sv_status sv_check_verify_args(const sv_verify_args* a, int mode);
  * i < k_b and 0 beyond. */
 sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s);
 
+/* sv_verify_sample for callers that cannot allocate device memory or hand
+ * in a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results
+ * as sv_verify_sample; a->workspace and a->workspace_bytes are ignored: the
+ * per-vector records and work-queue counters live in a device array of the
+ * library, sv_noalloc_scratch_bytes() (4 MiB) per GPU, held until the
+ * process ends.  The call allocates nothing.  Every call on one GPU uses
+ * that GPU's array: calls that overlap on one GPU (concurrent streams, or
+ * two host threads) race and corrupt each other's results; serialise them.
+ * Errors: as sv_verify_sample; SV_E_WORKSPACE when the records and counters
+ * of B rows at k_max (sv_verify_workspace_bytes for the sampled path) need
+ * more than the array holds; SV_E_ARG with SV_FLAG_RECORDS_READY (records
+ * from a shard merge sit in a caller's workspace); SV_E_DEVICE when the
+ * array's device address could not be looked up at sv_create. */
+size_t sv_noalloc_scratch_bytes(void);
+sv_status sv_verify_sample_noalloc(sv_handle h, const sv_verify_args* a, hipStream_t s);
+
 /* Greedy branch ([SSD] §2.4, §5.2): g_i = argmax of the raw target logits at
  * position i (lowest index on ties; temperature and top-p ignored); x_i =
  * draft_tokens, or the argmax of draft_logits when those are given; a = first

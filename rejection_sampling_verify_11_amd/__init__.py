@@ -10,5 +10,5 @@ from ._abi import (  # noqa: F401
     ROW_FREE_OVERFLOW, ROW_NO_FINITE, ROW_NONFINITE_LOGIT, RollbackCall, ShardedCall,
     SpecVerifyError, VerifyCall, advance_offset, draft_sample, draft_sample_sharded, dynamic_k,
     dynk_state, kv_rollback, library, shard_bounds, timing_enable, timing_read, verify_greedy,
-    verify_sample, verify_sample_sharded,
+    verify_sample, verify_sample_noalloc, verify_sample_sharded, noalloc_scratch_bytes,
 )

@@ -120,6 +120,7 @@ class ShardDrawArgs(C.Structure):
 EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
+           "sv_noalloc_scratch_bytes", "sv_verify_sample_noalloc",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
            "sv_check_verify_rollback_args", "sv_verify_sample_rollback",
            "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset",
@@ -157,9 +158,12 @@ def library():
                 L.sv_verify_workspace_bytes.restype = C.c_size_t
                 L.sv_check_verify_args.argtypes = [C.POINTER(VerifyArgs), C.c_int]
                 L.sv_check_verify_args.restype = C.c_int
-                for f in (L.sv_verify_sample, L.sv_verify_greedy, L.sv_draft_sample):
+                for f in (L.sv_verify_sample, L.sv_verify_greedy, L.sv_draft_sample,
+                          L.sv_verify_sample_noalloc):
                     f.argtypes = [_P, C.POINTER(VerifyArgs), _P]
                     f.restype = C.c_int
+                L.sv_noalloc_scratch_bytes.argtypes = []
+                L.sv_noalloc_scratch_bytes.restype = C.c_size_t
                 L.sv_rollback_workspace_bytes.argtypes = [C.c_int32]
                 L.sv_rollback_workspace_bytes.restype = C.c_size_t
                 L.sv_check_rollback_args.argtypes = [C.POINTER(RollbackArgs)]
@@ -297,8 +301,10 @@ class VerifyCall:
     block filled once; run() only enqueues the library call."""
 
     def __init__(self, mode, target, draft, draft_tokens=None, temperature=None, top_p=None,
-                 k_per_row=None, seed=0, offset=0, flags=0, want_probs=True):
+                 k_per_row=None, seed=0, offset=0, flags=0, want_probs=True, noalloc=False):
         self.mode = mode  # "sample", "greedy" or "draft"
+        if noalloc and mode != "sample":
+            raise ValueError("only sampled verification has a variant without workspace")
         ref = draft if mode == "draft" else target
         dev = ref.device
         if dev.type != "cuda":
@@ -360,14 +366,20 @@ class VerifyCall:
         self.outputs["row_status"] = torch.empty(B, dtype=torch.int32, device=dev)
         a.row_status = _ptr(self.outputs["row_status"])
         L = library()
-        nbytes = L.sv_verify_workspace_bytes(B, K, V, a.dtype, a.flags) if B > 0 else 256
-        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
+        if noalloc:
+            # the library's own device array holds the records
+            self.workspace = None
+        else:
+            nbytes = L.sv_verify_workspace_bytes(B, K, V, a.dtype, a.flags) if B > 0 else 256
+            self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
         self.args = a
         self._keep = keep
         self.device = dev
         self._fn = {"sample": L.sv_verify_sample, "greedy": L.sv_verify_greedy,
                     "draft": L.sv_draft_sample}[mode]
+        if noalloc:
+            self._fn = L.sv_verify_sample_noalloc
         self._h = handle(dev)
         self._ref = C.byref(self.args)
 
@@ -408,6 +420,20 @@ def verify_sample(target, draft, draft_tokens, temperature, top_p=None, k_per_ro
     with _allocating_on(stream):
         return VerifyCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
                           seed, offset, flags).run(stream)
+
+
+def verify_sample_noalloc(target, draft, draft_tokens, temperature, top_p=None, k_per_row=None,
+                          seed=0, offset=0, flags=0, stream=None):
+    """verify_sample through sv_verify_sample_noalloc: the library keeps its
+    records in its own per-GPU device array instead of a workspace (the
+    outputs are still allocated here, as the caller's buffers)."""
+    with _allocating_on(stream):
+        return VerifyCall("sample", target, draft, draft_tokens, temperature, top_p, k_per_row,
+                          seed, offset, flags, noalloc=True).run(stream)
+
+
+def noalloc_scratch_bytes():
+    return int(library().sv_noalloc_scratch_bytes())
 
 
 def verify_greedy(target, draft_tokens=None, draft=None, k_per_row=None, stream=None):

@@ -81,12 +81,22 @@ class EventTimer final : public sv::Timer {
 
 }  // namespace
 
+// Device memory of sv_verify_sample_noalloc: the records and work-queue
+// counters that sv_verify_sample keeps in the caller's workspace.  Every GPU
+// the library runs on holds its own copy for the life of the process.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address is looked up once per device (sv_create) and only that
+// address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 struct sv_handle_s {
   int device;
   int num_cus;
   char arch[64];
   bool timing;
   EventTimer* timer;
+  void* scratch_dev;  // this device's copy of `scratch`, or NULL if the lookup failed
   sv::Timer* active() { return timing ? timer : nullptr; }
 };
 
@@ -141,6 +151,15 @@ sv_status sv_create(int hip_device, sv_handle* out) {
   h->num_cus = prop.multiProcessorCount;
   strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
   h->arch[sizeof(h->arch) - 1] = 0;
+  // the device address of this device's scratch array, with the device current
+  h->scratch_dev = nullptr;
+  int prev = -1;
+  if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(hip_device) == hipSuccess) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) h->scratch_dev = ptr;
+    hipSetDevice(prev);
+  }
+  hipGetLastError();  // a failed lookup only disables sv_verify_sample_noalloc
   *out = h;
   return SV_OK;
 }
@@ -276,6 +295,26 @@ sv_status sv_verify_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   if (sv::launch_finalize_sample(finalize_params(a), h->num_cus, s, h->active()) != hipSuccess)
     return SV_E_DEVICE;
   return SV_OK;
+}
+
+size_t sv_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+sv_status sv_verify_sample_noalloc(sv_handle h, const sv_verify_args* a, hipStream_t s) {
+  if (!a) return SV_E_ARG;
+  sv_verify_args w = *a;
+  w.workspace = nullptr;
+  w.workspace_bytes = 0;
+  // argument errors first (the missing workspace is this call's to supply)
+  const sv_status st = sv_check_verify_args(&w, 0);
+  if (st != SV_OK && st != SV_E_WORKSPACE) return st;
+  if (w.flags & SV_FLAG_RECORDS_READY) return SV_E_ARG;  // records sit in a caller's workspace
+  if (!h) return SV_E_ARG;
+  if (w.B == 0) return SV_OK;
+  if (sample_ws(w.B, w.k_max) > kNoAllocScratchBytes) return SV_E_WORKSPACE;
+  if (!h->scratch_dev) return SV_E_DEVICE;
+  w.workspace = h->scratch_dev;
+  w.workspace_bytes = kNoAllocScratchBytes;
+  return sv_verify_sample(h, &w, s);
 }
 
 sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {

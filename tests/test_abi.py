@@ -361,3 +361,20 @@ def test_shard_draw_validation(field, value, code):
     for fn in (L.sv_shard_draw_mass, L.sv_shard_draw_locate):
         assert fn(None, C.byref(good_draw()), None) == _abi.SV_E_ARG  # no handle
 
+
+
+def test_noalloc_host_validation():
+    """sv_verify_sample_noalloc: argument errors before anything else, no
+    records-ready flag (those records sit in a caller's workspace), a handle
+    required; the scratch array's size is exported."""
+    L = _abi.library()
+    assert L.sv_noalloc_scratch_bytes() == 4 << 20
+    assert L.sv_verify_sample_noalloc(None, None, None) == _abi.SV_E_ARG
+    a = good_args(B=4, K=3)
+    a.workspace, a.workspace_bytes = None, 0
+    assert L.sv_verify_sample_noalloc(None, C.byref(a), None) == _abi.SV_E_ARG  # no handle
+    a.flags = _abi.FLAG_RECORDS_READY
+    assert L.sv_verify_sample_noalloc(None, C.byref(a), None) == _abi.SV_E_ARG
+    a = good_args(B=4, K=3)
+    a.dtype = 7
+    assert L.sv_verify_sample_noalloc(None, C.byref(a), None) == _abi.SV_E_DTYPE
