@@ -4,15 +4,21 @@
 Workload: B=256 sequences, k=6 drafts, V=151936 bf16 logits, Zipf-shaped
 synthetic target logits (sorted -1.1*ln(rank) + N(0, 0.5^2), permuted),
 draft = target + N(0, 1), temperature 1, top-p 0.9 on both sides.  A step is
-one verification round over one batch: sv_verify_sample (softmax statistics,
-top-p thresholds, acceptance scan, residual / bonus draw) followed by
-sv_kv_rollback of every row's write pointer and page table (page size 16,
+one verification round over one batch: sv_verify_sample_rollback, i.e. the
+verification (softmax statistics, top-p thresholds, acceptance scan,
+residual / bonus draw) and the rollback of every row's write pointer and
+page table that it implies (page size 16,
 contexts of 4096..8192 tokens, so that hundreds of steps can each shorten
 every sequence by up to k without running out of context).  Two input batches (2 GB together) alternate
 so that no step finds its logits in the 256 MB last-level cache.
 
+Draft tokens come from the library's draft sampler (x ~ q' at T and top-p,
+as a draft model sampling the same way would propose them).
+
 Beside the headline step, more legs are timed and reported as extra keys:
-greedy verification at B=64, k=8, V=128256 (target logits only); the
+the two small configurations (B=1, k=4, V=32000 fp32 and B=32, k=5,
+V=32000 bf16, latency-bound: microseconds per call); greedy verification at
+B=64, k=8, V=128256 (target logits only); the
 on-device round at B=512, V=128256 with per-row temperatures and k from the
 dynamic controller (verification, page-table rollback, controller update
 and round-counter advance), replayed as a HIP graph and, for comparison,
@@ -47,7 +53,7 @@ def parse():
                     help="rounds (round counters) per input batch in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the greedy and round legs")
-    ap.add_argument("--leg", choices=("greedy", "round", "variants", "sharded"),
+    ap.add_argument("--leg", choices=("greedy", "round", "variants", "sharded", "small"),
                     help="run only this extra leg on the bench inputs and print its JSON (for "
                          "profiling one leg); no headline line")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -104,6 +110,39 @@ def timed(fn, n, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def small_legs(dev, n):
+    """The two small configurations, which are latency-bound: B=1, k=4,
+    V=32000 fp32 (T=1, no top-p) and B=32, k=5, V=32000 bf16 (T=0.8), with
+    draft tokens from the draft sampler.  Microseconds per sv_verify_sample
+    call (HIP events around n back-to-back calls) and verified positions/s;
+    per-kernel times from a second pass."""
+    import torch
+    import rejection_sampling_verify_11_amd as sv
+    from rejection_sampling_verify_11_amd import workloads as W
+    out = {}
+    for name, inp in (("fp32_b1_k4_v32000", W.workload1(0, device=dev)),
+                      ("bf16_b32_k5_v32000", W.workload2(0, device=dev))):
+        B, K, V = inp.draft.shape
+        toks, st = sv.draft_sample(inp.draft, inp.temperature, inp.top_p, seed=0, offset=0)
+        call = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
+                             None, seed=0, offset=0)
+        for _ in range(50):
+            call.run()
+        us = timed(call.run, n, dev) * 1e3
+        sv.timing_enable(dev, True)
+        for _ in range(50):
+            call.run()
+        torch.cuda.synchronize()
+        kt = sv.timing_read(dev)
+        sv.timing_enable(dev, False)
+        assert not st.any() and not call.outputs["row_status"].any()
+        nbytes = B * (2 * K + 1) * V * inp.target.element_size()
+        out[name] = {"us_per_call": us, "verified_positions_per_s": B * K / (us * 1e-6),
+                     "input_gbs": nbytes / (us * 1e-6) / 1e9,
+                     "kernels_us": {k: 1e3 * v[1] / v[0] for k, v in kt.items()}}
+    return out
 
 
 def greedy_leg(dev, n):
@@ -235,7 +274,8 @@ def round_leg(dev, n):
     rows = W.workload5_rows(0, B=B, device=dev)
     k = torch.full((B,), 5, dtype=torch.int32, device=dev)
     inp = W.workload5(0, rows, k, k_max=K, device=dev, V=V)
-    toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 0)
+    # tokens at all k_max positions: the controller moves k between rounds
+    toks, _ = sv.draft_sample(inp.draft, inp.temperature, None, seed=0, offset=0)
     ctx_max = 4096 + (4 * n + 100) * (K + 1)  # every round below lengthens a row by <= K + 1
     MP = (ctx_max + ps - 1) // ps
     page_table = torch.arange(B * MP, dtype=torch.int32, device=dev).view(B, MP)
@@ -328,23 +368,11 @@ def main():
 
     dev = torch.device("cuda:0")
     B, K, V, P = 256, 6, 151936, 0.9
-    sets = []
-    for r in range(args.sets):
-        inp = W.workload4(r, device=dev, B=B, k=K, V=V)
-        toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, r)
-        call = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
-                             None, seed=0, offset=0)
-        sets.append((inp, toks, call))
-    torch.cuda.synchronize()
-
-    if args.leg:
-        n = args.steps
-        leg = {"greedy": lambda: greedy_leg(dev, n), "round": lambda: round_leg(dev, n),
-               "variants": lambda: variant_legs(dev, sets, min(n, 50)),
-               "sharded": lambda: sharded_leg(dev, sets, min(n, 50))}[args.leg]()
-        print(json.dumps({"leg": args.leg, "result": leg}))
-        return
-
+    # Host-side set-up first.  The GPU's clocks ramp over ~20 ms of sustained
+    # load after an idle spell (a per-dispatch trace shows the stats kernel at
+    # ~206 us for its first 40 launches after a 12.6 ms idle gap, 184 us once
+    # settled), so the GPU's own input generation is the last thing before
+    # the warm-up.
     # rollback state: contexts U[4096, 8192] plus the k+1 slots this round wrote
     rows = W.workload5_rows(0, B=B, ctx_lo=4096, ctx_hi=8192)
     kv_len0 = rows.kv_len0 + (K + 1)
@@ -352,15 +380,34 @@ def main():
     MP = int(math.ceil((8192 + K + 1) / ps))
     kv = W.paged_kv(kv_len0, ps, MP, spare_pages=0, seed=0)
     kv_len = kv_len0.to(dev)
-    rb_calls = [sv.RollbackCall(kv_len, c.outputs["accepted"], kv.page_table.to(dev), ps, K,
-                                free_pages=kv.free_pages.to(dev), free_top=kv.free_top.to(dev),
+    pt_dev = kv.page_table.to(dev)
+    free_dev, top_dev = kv.free_pages.to(dev), kv.free_top.to(dev)
+    torch.cuda.synchronize()
+
+    # input batches, with draft tokens drawn by the draft sampler from q'
+    # (x ~ q', draw 2: the tokens a draft model sampling at T and top-p would
+    # propose)
+    sets = []
+    for r in range(args.sets):
+        inp = W.workload4(r, device=dev, B=B, k=K, V=V)
+        toks, st = sv.draft_sample(inp.draft, inp.temperature, inp.top_p, seed=0, offset=r)
+        call = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
+                             None, seed=0, offset=0)
+        sets.append((inp, toks, call))
+
+    if args.leg:
+        torch.cuda.synchronize()
+        n = args.steps
+        leg = {"greedy": lambda: greedy_leg(dev, n), "round": lambda: round_leg(dev, n),
+               "variants": lambda: variant_legs(dev, sets, min(n, 50)),
+               "sharded": lambda: sharded_leg(dev, sets, min(n, 50)),
+               "small": lambda: small_legs(dev, n)}[args.leg]()
+        print(json.dumps({"leg": args.leg, "result": leg}))
+        return
+
+    rb_calls = [sv.RollbackCall(kv_len, c.outputs["accepted"], pt_dev, ps, K,
+                                free_pages=free_dev, free_top=top_dev,
                                 num_pages=kv.num_pages) for (_, _, c) in sets]
-    # one page table / stack shared by all calls
-    pt = rb_calls[0].args.page_table
-    for c in rb_calls[1:]:
-        c.args.page_table = pt
-        c.args.free_pages = rb_calls[0].args.free_pages
-        c.args.free_top = rb_calls[0].args.free_top
 
     step_no = [0]
 
@@ -368,8 +415,7 @@ def main():
         i = step_no[0]
         _, _, call = sets[i % len(sets)]
         call.set_offset(i)
-        call.run()
-        rb_calls[i % len(sets)].run()
+        call.run_with_rollback(rb_calls[i % len(sets)])
         step_no[0] += 1
 
     for _ in range(args.warmup):
@@ -434,6 +480,7 @@ def main():
     }
 
     if not args.no_extra:
+        result["small"] = small_legs(dev, max(args.steps, 100))
         result["greedy"] = greedy_leg(dev, args.steps)
         result["round"] = round_leg(dev, args.steps)
         result.update(variant_legs(dev, sets, min(args.steps, 50)))

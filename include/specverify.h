@@ -275,10 +275,13 @@ sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s);
  * round ([SSD] §3.3 and §4.3): sv_verify_sample(v), then sv_kv_rollback(r)
  * on the accepted counts it wrote, with the results of those two calls on
  * the same stream.  r->accepted must be v->accepted, and r must have the
- * same B, k_max and k_per_row as v.  When r has no free stack and no KV pool,
- * a row's rollback needs nothing from the other rows; each verification
- * workgroup then also rolls its own row back, and the rollback kernel is not
- * launched.  Otherwise the rollback kernels run after the verification.
+ * same B, k_max and k_per_row as v.  Each verification workgroup takes its
+ * row's rollback decision (checks, whole page-table row, new length) on the
+ * accepted count it has just found.  When r has no free stack and no KV
+ * pool, a row's rollback needs nothing from the other rows and the workgroup
+ * commits it; otherwise it writes the decision to r's workspace and the
+ * rollback's scan (and poisoning) kernels follow.  Results equal the two
+ * calls'.
  * Errors: those of the two argument checks, SV_E_ARG for arguments that do
  * not match, nothing launched on an error. */
 sv_status sv_check_verify_rollback_args(const sv_verify_args* v, const sv_rollback_args* r);

@@ -281,6 +281,8 @@ static sv::FinalizeParams finalize_params(const sv_verify_args* a) {
   f.page_table = nullptr;
   f.ps = f.MP = f.num_pages = 0;
   f.roll_status = nullptr;
+  f.roll_recs = nullptr;
+  f.free_stack = 0;
   return f;
 }
 
@@ -377,11 +379,7 @@ sv_status sv_check_rollback_args(const sv_rollback_args* a) {
   return SV_OK;
 }
 
-sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) {
-  const sv_status st = sv_check_rollback_args(a);
-  if (st != SV_OK) return st;
-  if (!h) return SV_E_ARG;
-  if (a->B == 0) return SV_OK;
+static sv::RollbackParams rollback_params(const sv_rollback_args* a) {
   sv::RollbackParams p;
   p.B = a->B;
   p.K = a->k_max;
@@ -401,7 +399,15 @@ sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) 
   p.D = a->head_dim;
   p.row_status = a->row_status;
   p.recs = (sv::RollRec*)a->workspace;
-  if (sv::launch_rollback(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return p;
+}
+
+sv_status sv_kv_rollback(sv_handle h, const sv_rollback_args* a, hipStream_t s) {
+  const sv_status st = sv_check_rollback_args(a);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  if (sv::launch_rollback(rollback_params(a), s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
 }
 
@@ -421,12 +427,6 @@ sv_status sv_verify_sample_rollback(sv_handle h, const sv_verify_args* v,
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (v->B == 0) return SV_OK;
-  if (r->free_pages || r->kv_pool) {
-    // releases are placed on the stack by a scan over all rows
-    const sv_status sv = sv_verify_sample(h, v, s);
-    if (sv != SV_OK) return sv;
-    return sv_kv_rollback(h, r, s);
-  }
   if (!(v->flags & SV_FLAG_RECORDS_READY) &&
       sv::launch_stats(stats_params(v, 0), v->dtype, h->num_cus, s, h->active()) != hipSuccess)
     return SV_E_DEVICE;
@@ -436,8 +436,16 @@ sv_status sv_verify_sample_rollback(sv_handle h, const sv_verify_args* v,
   f.ps = r->page_size;
   f.MP = r->max_pages_per_seq;
   f.num_pages = r->num_pages;
-  f.roll_status = r->row_status;
+  // Without a free stack or pool each row commits its own rollback.  With
+  // one, each row writes its decision, and a scan over all rows places the
+  // releases on the stack (then poisons and commits).
+  const bool scan = r->free_pages || r->kv_pool;
+  f.roll_status = scan ? nullptr : r->row_status;
+  f.roll_recs = scan ? (sv::RollRec*)r->workspace : nullptr;
+  f.free_stack = r->free_pages ? 1 : 0;
   if (sv::launch_finalize_sample(f, h->num_cus, s, h->active()) != hipSuccess)
+    return SV_E_DEVICE;
+  if (scan && sv::launch_rollback_decided(rollback_params(r), s, h->active()) != hipSuccess)
     return SV_E_DEVICE;
   return SV_OK;
 }

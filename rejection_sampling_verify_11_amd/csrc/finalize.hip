@@ -733,19 +733,20 @@ __device__ __forceinline__ int row_header(const FinalizeParams& p, int b, RowSha
 }
 
 // ---- the rollback of a row, fused into its verification
-// Used when the cache has no free stack and no pool: the rollback of one row
-// then needs nothing from the others, and is the rollback kernel's decision
-// for that row ([SSD] §3.3: the write pointer moves back to the accepted
-// prefix, and the page table must agree with the length: the first
-// ceil(old/ps) entries map pages of the pool; past the length, entries are
-// free without a free stack), taken on the accepted count the row's
-// verification just found (-1 for a flagged row).  Every thread loads one
-// page entry after the header, so that the loads overlap the draw; the
-// entries are tested, and the length written, at the end.
+// The rollback kernel's decision for the row ([SSD] §3.3: the write pointer
+// moves back to the accepted prefix, and the page table must agree with the
+// length: the first ceil(old/ps) entries map pages of the pool and, with a
+// free stack, every later entry is unmapped), taken on the accepted count
+// the row's verification just found (-1 for a flagged row).  Without a free
+// stack or pool the row's rollback needs nothing from the others and is
+// committed here; otherwise the decision goes to the rollback's records and
+// its scan over all rows places the releases.  Every thread loads one page
+// entry after the header, so that the loads overlap the draw; the entries
+// are tested, and the result written, at the end.
 struct RollCheck {
   uint32_t st;
-  int new_len, used;
-  int32_t e;  // page entry threadIdx.x (when below used)
+  int old_len, new_len, used, span;
+  int32_t e;  // page entry threadIdx.x (when below span)
 };
 
 __device__ __forceinline__ int ceil_div_i(int x, int d) { return (x + d - 1) / d; }
@@ -758,10 +759,13 @@ __device__ __forceinline__ RollCheck roll_begin(const FinalizeParams& p, int b, 
   if (k < 1 || k > p.K) r.st |= SV_ROW_BAD_K;
   else if (acc < 0 || acc > k || old - (k - acc) < 0) r.st |= SV_ROW_BAD_ACCEPTED;
   if (old < 0 || ceil_div_i(old, p.ps) > p.MP) r.st |= SV_ROW_BAD_PAGES;
+  r.old_len = old;
   r.new_len = r.st ? old : old - (k - acc);
   r.used = r.st ? 0 : ceil_div_i(old, p.ps);
-  // clamped into the row (used <= MP), loaded whether or not it is tested
-  const int pg = min((int)threadIdx.x, max(r.used - 1, 0));
+  // past the length only a free stack constrains the entries
+  r.span = r.st ? 0 : (p.free_stack ? p.MP : r.used);
+  // clamped into the row, loaded whether or not it is tested
+  const int pg = min((int)threadIdx.x, p.MP - 1);
   r.e = p.page_table[(int64_t)b * p.MP + pg];
   return r;
 }
@@ -770,14 +774,26 @@ __device__ __forceinline__ RollCheck roll_begin(const FinalizeParams& p, int b, 
 template <int NT>
 __device__ __forceinline__ void roll_end(const FinalizeParams& p, int b, const RollCheck& r) {
   const int tid = threadIdx.x;
-  auto bad_entry = [&](int32_t e) { return e < 0 || (p.num_pages > 0 && e >= p.num_pages); };
-  bool bad = tid < r.used && bad_entry(r.e);
-  for (int pg = tid + NT; pg < r.used; pg += NT)  // contexts beyond NT pages
-    bad = bad || bad_entry(p.page_table[(int64_t)b * p.MP + pg]);
+  auto bad_entry = [&](int pg, int32_t e) {
+    return pg < r.used ? (e < 0 || (p.num_pages > 0 && e >= p.num_pages)) : e != -1;
+  };
+  bool bad = tid < r.span && bad_entry(tid, r.e);
+  for (int pg = tid + NT; pg < r.span; pg += NT)  // tables longer than NT pages
+    bad = bad || bad_entry(pg, p.page_table[(int64_t)b * p.MP + pg]);
   const uint32_t st = r.st | (__syncthreads_or(bad) ? (uint32_t)SV_ROW_BAD_PAGES : 0u);
   if (tid == 0) {
-    if (!st) p.kv_len[b] = r.new_len;
-    if (p.roll_status) p.roll_status[b] = (int32_t)st;
+    if (p.roll_recs) {
+      // the rollback's record: status, lengths and the pages released
+      RollRec rec;
+      rec.status = (int32_t)st;
+      rec.old_len = r.old_len;
+      rec.new_len = st ? r.old_len : r.new_len;
+      rec.aux = st ? 0 : r.used - ceil_div_i(r.new_len, p.ps);
+      p.roll_recs[b] = rec;
+    } else {
+      if (!st) p.kv_len[b] = r.new_len;
+      if (p.roll_status) p.roll_status[b] = (int32_t)st;
+    }
   }
 }
 

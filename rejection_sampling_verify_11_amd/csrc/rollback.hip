@@ -200,8 +200,14 @@ hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t) {
     hipLaunchKernelGGL(rollback_check_kernel, dim3((p.B + kCheckRows - 1) / kCheckRows),
                        dim3(64 * kCheckRows), 0, s, p);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_rollback_decided(p, s, t);
+}
+
+hipError_t launch_rollback_decided(const RollbackParams& p, hipStream_t s, Timer* t) {
+  if (p.B == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
   if (!p.kv_pool) {
     TimedScope ts(t, "rollback", s);
     hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 0);

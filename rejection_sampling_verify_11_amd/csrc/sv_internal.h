@@ -158,6 +158,12 @@ struct FinalizeParams {
   const int32_t* page_table;
   int32_t ps, MP, num_pages;
   int32_t* roll_status;
+  // with a free stack or a pool, the rows' releases are placed by a scan over
+  // all rows: each row then only writes its decision here (roll_recs
+  // non-null), and the rollback's scan kernels commit; free_stack: entries
+  // past the length must be unmapped
+  RollRec* roll_recs;
+  int32_t free_stack;
 };
 
 struct GreedyParams {
@@ -240,6 +246,9 @@ hipError_t launch_shard_draw(const FinalizeParams& p, const ShardDrawParams& d, 
                              int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
+// The rollback's scan and commit kernels on decisions already in p.recs
+// (written by the verification's finalize kernel).
+hipError_t launch_rollback_decided(const RollbackParams& p, hipStream_t s, Timer* t);
 hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t);
 hipError_t launch_advance_offset(uint64_t* offset_dev, uint64_t delta, hipStream_t s, Timer* t);
 

@@ -3,10 +3,10 @@ against the two calls it stands for -- sv_verify_sample, then sv_kv_rollback
 on the accepted counts -- bit for bit in every output and in the cache state.
 The two calls are checked against the oracle elsewhere.
 
-The fused path runs when the cache has no free stack and no pool (each row's
-rollback then needs nothing from the other rows); with a free stack the
-entry point runs the rollback kernels after the verification, which must
-give the same state too.
+Without a free stack or pool each row's rollback needs nothing from the
+other rows and is committed by its verification workgroup; with one, each
+workgroup writes its row's decision and the rollback's scan kernels place
+the releases.  Both must give the same state as the two calls.
 """
 import numpy as np
 import pytest
@@ -32,7 +32,7 @@ def page_table(lens, ps, MP):
     return pt, nxt
 
 
-def run_both(inp, toks, kpr, lens, ps, pt, num_pages, free_spare=None):
+def run_both(inp, toks, kpr, lens, ps, pt, num_pages, free_spare=None, pool_dims=None):
     d = to_dev(inp)
     K = inp.draft.shape[1]
     t = torch.as_tensor(toks, dtype=torch.int32, device=DEV)
@@ -48,6 +48,13 @@ def run_both(inp, toks, kpr, lens, ps, pt, num_pages, free_spare=None):
             fp[:free_spare] = torch.arange(num_pages, num_pages + free_spare, dtype=torch.int32)
             extra = dict(free_pages=fp, free_top=torch.tensor([free_spare], dtype=torch.int32,
                                                               device=DEV))
+        if pool_dims is not None:
+            L, H, D = pool_dims
+            g = torch.Generator(device=DEV).manual_seed(5)
+            pool = torch.randint(0, 30000, (num_pages + (free_spare or 0), L, 2, H, ps, D),
+                                 generator=g, device=DEV, dtype=torch.int16)
+            extra.update(kv_pool=pool.view(torch.bfloat16), num_layers=L, kv_heads=H,
+                         head_dim=D)
         roll = sv.RollbackCall(kv, call.outputs["accepted"], ptd, ps, K, k_per_row=k,
                                num_pages=num_pages + (free_spare or 0), **extra)
         if fused:
@@ -59,7 +66,8 @@ def run_both(inp, toks, kpr, lens, ps, pt, num_pages, free_spare=None):
         state = {n: x.clone() for n, x in call.outputs.items()}
         state.update(kv_len=kv.clone(), page_table=ptd.clone(), roll_status=roll.row_status.clone())
         for n, x in extra.items():
-            state[n] = x.clone()
+            if isinstance(x, torch.Tensor):
+                state[n] = x.view(torch.int16).clone() if n == "kv_pool" else x.clone()
         res.append(state)
     a, b = res
     for n in a:
@@ -74,7 +82,8 @@ def test_fused_rollback_bench_shape(oracle):
     """B=256, k=6, V=151936 Zipf logits with top-p 0.9; contexts of
     512..4096 tokens plus the round's 7 writes, page size 16."""
     inp = W.workload4(1)
-    toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 1).cpu().numpy()
+    toks = sv.draft_sample(inp.draft.to(DEV), inp.temperature.to(DEV), inp.top_p.to(DEV),
+                           seed=0, offset=1)[0].cpu().numpy()
     rng = np.random.default_rng(5)
     lens = rng.integers(512, 4097, 256) + 7
     ps, MP = 16, (4096 + 7 + 15) // 16
@@ -115,16 +124,18 @@ def test_fused_rollback_bad_rows(oracle, ps):
     assert st[5] & sv.ROW_BAD_ACCEPTED
     assert st[8] & sv.ROW_BAD_PAGES and st[9] & sv.ROW_BAD_PAGES
     for b in (10, 11):
-        # the last page is checked when a position on it is dropped, or when
-        # the new length ends inside it
-        checked = acc[b] < kpr[b] or lens[b] % ps != 0
-        assert bool(st[b] & sv.ROW_BAD_PAGES) == checked, b
+        # the whole row of the table is checked against the length
+        assert st[b] & sv.ROW_BAD_PAGES, b
     assert np.all(out["kv_len"].cpu().numpy()[st != 0] == lens[st != 0])
 
 
-def test_fused_entry_with_a_free_stack(oracle):
-    """With a free stack the rollback runs as its own kernels after the
-    verification: the pages released and the stack match the two calls."""
+@pytest.mark.parametrize("pool", [False, True])
+def test_fused_entry_with_a_free_stack(oracle, pool):
+    """With a free stack (and optionally a pool to poison) each verification
+    workgroup takes its row's rollback decision, whole page-table check
+    included, and the rollback's scan places the releases: lengths, pages
+    released, stack, pool and status match the two calls, also on rows whose
+    table maps a page past the length or leaves one below it unmapped."""
     B, K = 32, 4
     inp = W.workload2(4, B=B, k=K, V=32000)
     toks = oracle_tokens(oracle, inp, 6, 2)
@@ -132,8 +143,15 @@ def test_fused_entry_with_a_free_stack(oracle):
     lens = rng.integers(17, 120, B).astype(np.int32)
     ps, MP = 4, 32
     pt, n = page_table(lens, ps, MP)
-    out = run_both(inp, toks, None, lens, ps, pt, n, free_spare=6)
-    assert torch.all(out["roll_status"] == 0)
+    used = -(-lens // ps)
+    pt[2, min(used[2] + 3, MP - 1)] = 5   # mapped far past the length
+    pt[3, 0] = -1                   # unmapped below it
+    pt[4, used[4]] = -2             # not -1 past the length
+    out = run_both(inp, toks, None, lens, ps, pt, n, free_spare=6,
+                   pool_dims=(2, 1, 8) if pool else None)
+    st = out["roll_status"].cpu().numpy()
+    assert list(np.nonzero(st)[0]) == [2, 3, 4]
+    assert np.all(st[[2, 3, 4]] == sv.ROW_BAD_PAGES)
 
 
 def test_fused_rollback_in_a_replayed_graph(oracle):

@@ -116,7 +116,7 @@ def test_workload4_full_batch_sampled_rows(oracle):
     """The benchmarked shape: B=256, k=6, V=151936 bf16, top-p 0.9, one
     call over the whole batch; 16 rows spread over it are checked."""
     inp = W.workload4(0, device=DEV)
-    toks = W.gumbel_draft_tokens(inp.draft, inp.temperature, 0, 0)
+    toks, _ = sv.draft_sample(inp.draft, inp.temperature, inp.top_p, seed=0, offset=0)
     rows = np.linspace(0, 255, 16).astype(np.int64)
     rep = check_round(oracle, inp, toks.cpu().numpy(), 0, 0, rows=rows)
     print("workload4 full:", rep)
