@@ -638,3 +638,50 @@ def test_one_shot_call_on_a_side_stream(oracle):
     assert nd <= 1
     o = oracle_verify(oracle, inp, toks.cpu().numpy(), 4, 9)
     compare_sample(out, o, None, inp.draft.shape[1]).bound()
+
+
+def test_replayed_graph_and_reused_workspace(oracle):
+    """A captured sv_verify_sample replayed over changing inputs, each replay
+    equal to an eager call on the same inputs and checked against the
+    oracle; halfway the workspace is filled with garbage, which the next
+    replays must shrug off (the captured arming launch re-arms the
+    statistics kernel's work queues every replay)."""
+    B, K, V = 24, 5, 40000
+    tgt = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=DEV)
+    dft = torch.empty((B, K, V), dtype=torch.bfloat16, device=DEV)
+    toks = torch.zeros((B, K), dtype=torch.int32, device=DEV)
+    T = torch.full((B,), 0.9, device=DEV)
+    P = torch.full((B,), 0.9, device=DEV)
+    call = sv.VerifyCall("sample", tgt, dft, toks, T, P, None, seed=3, offset=1)
+    inp = W.workload4(0, B=B, k=K, V=V, device=DEV)
+    tgt.copy_(inp.target)
+    dft.copy_(inp.draft)
+    call.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run()
+    for r in range(4):
+        inp = W.workload4(r + 1, B=B, k=K, V=V, device=DEV)
+        tgt.copy_(inp.target)
+        dft.copy_(inp.draft)
+        t, _ = sv.draft_sample(dft, T, P, seed=3, offset=r)
+        toks.copy_(t)
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in call.outputs.items()}
+        ref = sv.verify_sample(tgt, dft, toks, T, P, seed=3, offset=1)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(torch.nan_to_num(got[k]), torch.nan_to_num(ref[k])), (r, k)
+        if r == 1:
+            call.workspace.random_(0, 256)
+        o = oracle_verify(oracle, W.SampleInputs(inp.target.cpu(), inp.draft.cpu(), T.cpu(),
+                                                 P.cpu()), toks.cpu().numpy(), 3, 1)
+        compare_sample(got, o, None, K).bound()
+    call.run()
+    torch.cuda.synchronize()
+    ref = sv.verify_sample(tgt, dft, toks, T, P, seed=3, offset=1)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(torch.nan_to_num(call.outputs[k]), torch.nan_to_num(ref[k])), k
