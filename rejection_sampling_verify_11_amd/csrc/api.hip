@@ -353,7 +353,7 @@ sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   g.accepted = a->accepted;
   g.num_emitted = a->num_emitted;
   g.row_status = a->row_status;
-  if (sv::launch_greedy(g, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  if (sv::launch_greedy(g, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
 }
 

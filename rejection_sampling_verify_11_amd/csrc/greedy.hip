@@ -4,12 +4,15 @@
 // page asks for this to be its own code path, and here it is: raw logits,
 // no temperature, no top-p, lowest index on ties.
 //
-// Kernel 1 splits every vector into chunks of kGreedyChunk logits, one
-// workgroup of 256 threads per chunk, and writes (max value, first index,
-// flags) per chunk; a thread issues all its 16-byte loads before comparing.
-// Kernel 2 runs one wave per row: lane i folds the chunks of position i
-// (target, and draft when draft logits are given), and a ballot finds the
-// first mismatch.
+// Kernel 1 splits every vector into chunks of kGreedyChunk logits and writes
+// (max value, first index, flags) per chunk.  For bf16 vectors on 16-byte
+// boundaries with V a multiple of 8 (the usual case) a persistent grid of
+// waves streams the chunks, a whole chunk per wave -- each lane issues its
+// eight 16-byte loads, then the wave reduces with shuffles alone (no LDS, no
+// barrier) -- and takes the next chunk; other layouts take a workgroup of
+// 256 threads per chunk.  Kernel 2 runs one wave per row: lane i folds the
+// chunks of position i (target, and draft when draft logits are given), and
+// a ballot finds the first mismatch.
 #include <math.h>
 
 #include "sv_internal.h"
@@ -18,8 +21,10 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kGreedyChunk / kThreads;  // 64 logits
+constexpr int kPerThread = kGreedyChunk / kThreads;  // 16 logits
 constexpr int kLoads = kPerThread / 8;               // 16-byte loads per thread
+constexpr int kLaneLoads = kGreedyChunk / 8 / 64;    // 8: a wave's loads per lane and chunk
+constexpr int kStreamWgPerCu = 4;                    // workgroups of the streaming grid per CU
 
 // (v, i) beats (bv, bi): larger value, or equal value with a lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -205,20 +210,128 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(GreedyParams p)
   }
 }
 
-// Folds the chunk results of vector v: (value, first index) and flags.
+// The vector a chunk item belongs to: target vectors (b, pos) first, then
+// draft vectors; false when the row does not use it (k_b invalid, or a
+// position past k_b).
+__device__ __forceinline__ bool chunk_vector(const GreedyParams& p, int v, const uint16_t** vec) {
+  const int nvec_t = p.B * (p.K + 1);
+  int b, pos;
+  bool draft_side;
+  if (v < nvec_t) { b = v / (p.K + 1); pos = v % (p.K + 1); draft_side = false; }
+  else { b = (v - nvec_t) / p.K; pos = (v - nvec_t) % p.K; draft_side = true; }
+  const int kb = p.k_per_row ? p.k_per_row[b] : p.K;
+  if (kb < 1 || kb > p.K || (draft_side ? pos >= kb : pos > kb)) return false;
+  *vec = draft_side ? (const uint16_t*)p.draft + ((int64_t)b * p.K + pos) * p.d_stride
+                    : (const uint16_t*)p.target + ((int64_t)b * (p.K + 1) + pos) * p.t_stride;
+  return true;
+}
+
+// Streams chunk items (vector-major), one wave per chunk at a time; items
+// wave, wave + waves, ... of the persistent grid.  bf16, every vector on a
+// 16-byte boundary, V a multiple of 8.  Lane l holds the 16-byte groups
+// l + 64 j of the chunk (j < 8), so each load instruction reads 1 KB of
+// consecutive logits; a group past the chunk's end (last chunk of a vector)
+// is loaded clamped and left out.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, kStreamWgPerCu)))
+void argmax_stream_kernel(GreedyParams p, int nitems) {
+  const int l = threadIdx.x & 63;
+  const int waves = gridDim.x * (kThreads / 64);
+  const int nch = greedy_chunks(p.V);
+  const int n8v = p.V >> 3;  // 16-byte groups per vector
+  for (int item = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); item < nitems; item += waves) {
+    const int v = item / nch, c = item % nch;
+    const uint16_t* vec;
+    if (!chunk_vector(p, v, &vec)) continue;  // wave-uniform
+    const int g0 = c * (kGreedyChunk / 8);
+    const int n8 = min(kGreedyChunk / 8, n8v - g0);
+    const uint4* body = (const uint4*)vec + g0;
+    uint4 d[kLaneLoads];
+#pragma unroll
+    for (int j = 0; j < kLaneLoads; ++j) d[j] = body[min(l + 64 * j, n8 - 1)];
+    // the largest and smallest order key of each load's eight logits
+    uint32_t jmax[kLaneLoads];
+    u16x2 kmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int j = 0; j < kLaneLoads; ++j) {
+      const bool valid = l + 64 * j < n8;
+      const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+      u16x2 m = {0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u16x2 k = order_keys(ws[q]);
+        m = __builtin_elementwise_max(m, k);
+        kmin = __builtin_elementwise_min(kmin, k);
+      }
+      // a clamped load repeats the chunk's last group: harmless for the
+      // minimum, and kept out of the maximum (and so of the search)
+      jmax[j] = valid ? max((uint32_t)m.x, (uint32_t)m.y) : 0u;
+    }
+    uint32_t cmax = 0;
+#pragma unroll
+    for (int j = 0; j < kLaneLoads; ++j) cmax = max(cmax, jmax[j]);
+    uint32_t cmin = min((uint32_t)kmin.x, (uint32_t)kmin.y);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o, 64));
+      cmin = min(cmin, (uint32_t)__shfl_xor((int)cmin, o, 64));
+    }
+    // The first index holding the chunk's largest value.  Indices grow with
+    // the load j, then the lane, then the logit within the group: the first
+    // load any lane of which holds the value, its lowest such lane, and that
+    // lane's first logit in the group (the branches on j are wave-uniform).
+    int jstar = 0;
+    uint64_t bal = 0;
+#pragma unroll
+    for (int j = kLaneLoads - 1; j >= 0; --j) {
+      const uint64_t bj = __ballot(same_value(jmax[j], cmax));
+      if (bj) { jstar = j; bal = bj; }
+    }
+    const int L = bal ? __builtin_ctzll(bal) : 0;
+    int first = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kLaneLoads; ++j) {
+      if (j == jstar && l == L) {
+        const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+        for (int t = 7; t >= 0; --t) {
+          const uint32_t h = t & 1 ? ws[t >> 1] >> 16 : ws[t >> 1] & 0xFFFFu;
+          first = same_value(key_of(h), cmax) ? 8 * (g0 + l + 64 * j) + t : first;
+        }
+      }
+    }
+    first = __shfl(first, L, 64);
+    if (l == 0) {
+      uint32_t fl = 0;
+      if (cmax >= kKeyPosInf || cmin < kKeyNegInf) fl |= SV_ROW_NONFINITE_LOGIT;
+      if (cmax > kKeyNegInf && cmax < kKeyPosInf) fl |= kSawFinite;
+      ArgmaxPart r;
+      r.value = value_of_key(cmax);
+      r.index = first;
+      r.status = fl;
+      r.pad = 0;
+      p.parts[item] = r;
+    }
+  }
+}
+
+// Folds the chunk results of vector v: (value, first index) and flags.  The
+// kernel runs a wave per row, so registers are plentiful: up to kFoldBatch
+// chunk results load at once (every one of them for V <= 131072).
+constexpr int kFoldBatch = 32;
 __device__ __forceinline__ int fold_argmax(const GreedyParams& p, int v, int nch, uint32_t* fl) {
   float bv = -INFINITY;
   int bi = -1;
   const ArgmaxPart* r = p.parts + (int64_t)v * nch;
-  for (int c0 = 0; c0 < nch; c0 += 8) {
-    ArgmaxPart q[8];
+  for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
+    ArgmaxPart q[kFoldBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) q[u] = r[min(c0 + u, nch - 1)];
+    for (int u = 0; u < kFoldBatch; ++u) q[u] = r[min(c0 + u, nch - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c0 + u >= nch) break;
-      *fl |= q[u].status;
-      if (better(q[u].value, q[u].index, bv, bi)) { bv = q[u].value; bi = q[u].index; }
+    for (int u = 0; u < kFoldBatch; ++u) {
+      if (c0 + u < nch) {
+        *fl |= q[u].status;
+        if (better(q[u].value, q[u].index, bv, bi)) { bv = q[u].value; bi = q[u].index; }
+      }
     }
   }
   return bi;
@@ -230,26 +343,31 @@ __global__ __launch_bounds__(256) void greedy_finalize_kernel(GreedyParams p) {
   const int l = threadIdx.x & 63;
   if (b >= p.B) return;
   const int K = p.K, nch = greedy_chunks(p.V);
+  // every load of the row is issued before anything waits on one: k_b, the
+  // lane's draft token and its position's chunk results (the latter two
+  // for any lane that could need them, masked by k_b afterwards)
   const int kb = p.k_per_row ? p.k_per_row[b] : K;
+  const int xt = (!p.draft && l < K) ? p.tokens[(int64_t)b * K + l] : -1;
+  uint32_t ft = 0, fd = 0;
+  const int gt = l <= K ? fold_argmax(p, b * (K + 1) + l, nch, &ft) : -1;
+  const int gd = (p.draft && l < K) ? fold_argmax(p, p.B * (K + 1) + b * K + l, nch, &fd) : -1;
   const bool kok = kb >= 1 && kb <= K;
   uint32_t st = kok ? 0u : (uint32_t)SV_ROW_BAD_K;
   int g = -1, x = -1;
   if (kok) {
     uint32_t fl = 0;
     if (l <= kb) {
-      uint32_t f = 0;
-      g = fold_argmax(p, b * (K + 1) + l, nch, &f);
-      fl |= f & SV_ROW_NONFINITE_LOGIT;
-      if (!(f & kSawFinite)) fl |= SV_ROW_NO_FINITE;
+      g = gt;
+      fl |= ft & SV_ROW_NONFINITE_LOGIT;
+      if (!(ft & kSawFinite)) fl |= SV_ROW_NO_FINITE;
     }
     if (l < kb) {
       if (p.draft) {
-        uint32_t f = 0;
-        x = fold_argmax(p, p.B * (K + 1) + b * K + l, nch, &f);
-        fl |= f & SV_ROW_NONFINITE_LOGIT;
-        if (!(f & kSawFinite)) fl |= SV_ROW_NO_FINITE;
+        x = gd;
+        fl |= fd & SV_ROW_NONFINITE_LOGIT;
+        if (!(fd & kSawFinite)) fl |= SV_ROW_NO_FINITE;
       } else {
-        x = p.tokens[(int64_t)b * K + l];
+        x = xt;
         if (x < 0 || x >= p.V) fl |= SV_ROW_BAD_TOKEN;
       }
     }
@@ -271,13 +389,23 @@ __global__ __launch_bounds__(256) void greedy_finalize_kernel(GreedyParams p) {
 
 }  // namespace
 
-hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t) {
+hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Timer* t) {
   if (p.B == 0) return hipSuccess;
   const int nvec = p.B * (p.K + 1) + (p.draft ? p.B * p.K : 0);
-  const unsigned grid = (unsigned)nvec * (unsigned)greedy_chunks(p.V);
-  {
+  const unsigned nitems = (unsigned)nvec * (unsigned)greedy_chunks(p.V);
+  const bool stream = p.dtype == SV_BF16 && (p.V & 7) == 0 &&
+                      ((uintptr_t)p.target & 15u) == 0 && (p.t_stride & 7) == 0 &&
+                      (!p.draft || (((uintptr_t)p.draft & 15u) == 0 && (p.d_stride & 7) == 0));
+  if (stream) {
+    const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
+    const unsigned want = cus * (unsigned)kStreamWgPerCu;
+    const unsigned waves_needed = nitems;
+    const unsigned grid = min(want, (waves_needed + kThreads / 64 - 1) / (kThreads / 64));
     TimedScope ts(t, "greedy_argmax", s);
-    hipLaunchKernelGGL(argmax_chunks_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(argmax_stream_kernel, dim3(grid), dim3(kThreads), 0, s, p, (int)nitems);
+  } else {
+    TimedScope ts(t, "greedy_argmax", s);
+    hipLaunchKernelGGL(argmax_chunks_kernel, dim3(nitems), dim3(kThreads), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -55,7 +55,7 @@ static_assert(sizeof(RollRec) == 16, "RollRec layout");
 inline __host__ __device__ int slots_per_row(int K) { return 2 * K + 1; }
 
 // Greedy chunking of a vector over several workgroups.
-constexpr int kGreedyChunk = 16384;
+constexpr int kGreedyChunk = 4096;
 inline __host__ __device__ int greedy_chunks(int V) { return (V + kGreedyChunk - 1) / kGreedyChunk; }
 
 struct StatsParams {
@@ -244,7 +244,7 @@ hipError_t launch_finalize_sample(const FinalizeParams& p, int num_cus, hipStrea
 hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_shard_draw(const FinalizeParams& p, const ShardDrawParams& d, bool locate,
                              int num_cus, hipStream_t s, Timer* t);
-hipError_t launch_greedy(const GreedyParams& p, hipStream_t s, Timer* t);
+hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
 // The rollback's scan and commit kernels on decisions already in p.recs
 // (written by the verification's finalize kernel).
