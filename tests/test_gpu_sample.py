@@ -404,7 +404,7 @@ def test_values_below_the_count_window(oracle):
         toks = oracle_tokens(oracle, inp, 3, r)
         rep.merge(check_round(oracle, inp, toks, 3, r))
     print("below-window:", rep)
-    rep.bound(max_excused=2)
+    rep.bound()
 
 
 def test_top_p_cut_on_one_side_only(oracle):
@@ -685,3 +685,36 @@ def test_replayed_graph_and_reused_workspace(oracle):
     torch.cuda.synchronize()
     for k in ref:
         assert torch.equal(torch.nan_to_num(call.outputs[k]), torch.nan_to_num(ref[k])), k
+
+
+@pytest.mark.parametrize("eps,boost", [(0.02, 0.01), (0.05, 0.03)])
+def test_small_residual_mass(oracle, eps, boost):
+    """q' close to p': draft = target + eps N(0, 1), with the draft token's
+    draft logit raised so that it holds `boost` of q's mass, so most rows
+    reject their draft and draw from a residual of total mass R about 0.01 /
+    0.04.  The kernels form r = max(0, p' - q') from fp32 probabilities,
+    each within a few ulps (relative 2^-22) of the exact value, so the
+    running CDF of r is off by at most 2^-22 (sum p' + sum q') <= 2^-21 in
+    absolute terms, 2^-21 / R in units of u: a bound that grows as R
+    shrinks (3e-5 at R = 0.015), while the per-token errors, of either sign,
+    mostly cancel.  Every row that differs from the oracle must still be
+    validated within the 1e-6 bands, and such rows stay within the usual
+    1 % cap (5 of 4096 at R = 0.015 on MI355X)."""
+    B, K, V = 4096, 1, 32000
+    g = torch.Generator().manual_seed(int(eps * 1000))
+    zt = torch.randn((B, K + 1, V), generator=g) * 2.0
+    zd = zt[:, :K] + torch.randn((B, K, V), generator=g) * eps
+    x = torch.randint(0, V, (B,), generator=g)
+    # raise the draft logit at x so that q(x) = boost (T = 1): with S the
+    # draft's sum of exp over the other tokens, exp(d_x) = boost S / (1 - boost)
+    d = zd[:, 0].double()
+    others = torch.logsumexp(d.scatter(1, x[:, None], float("-inf")), dim=1)
+    zd[torch.arange(B), 0, x] = (others + np.log(boost / (1 - boost))).float()
+    inp = W.SampleInputs(zt.to(torch.bfloat16), zd.to(torch.bfloat16), torch.ones(B), None)
+    toks = x.view(B, 1).to(torch.int32).numpy()
+    rep = check_round(oracle, inp, toks, 13, 0)
+    o = oracle_verify(oracle, inp, toks, 13, 0)
+    R = o["residual_mass"][o["accepted"] == 0]
+    print("small residual: R median %.4f, rejected %d of %d," % (np.median(R), len(R), B), rep)
+    assert len(R) > B // 2 and np.median(R) < 5 * boost
+    rep.bound()
