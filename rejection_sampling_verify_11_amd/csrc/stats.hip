@@ -176,23 +176,60 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
+// The logits thread tid takes in the generic passes, j = tid, tid + NT, ...
+// in increasing order.  Streamed: read again on every pass.
+template <int NT, class Logits>
+struct StreamedLogits {
+  const Logits& logit;
+  int V;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    for (int64_t j = threadIdx.x; j < V; j += NT) f(logit(j));
+  }
+};
+
+// The same logits held in registers (V <= NT * R): read once, all loads in
+// flight together, so a short vector costs one memory round trip instead of
+// one per pass and per element.  The passes see the values in the same
+// order, so the results are the streamed passes' bit for bit.
+template <int NT, int R>
+struct HeldLogits {
+  float z[R];
+  int V;
+  template <class Logits>
+  __device__ __forceinline__ void load(const Logits& logit, int n) {
+    V = n;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t j = threadIdx.x + (int64_t)NT * i;
+      z[i] = logit(j < n ? j : 0);
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (threadIdx.x + (int64_t)NT * i < V) f(z[i]);
+  }
+};
+
 // All NT threads of the block call this.  hist256 is LDS of 256 doubles.
 // The bf16 kernel reaches it only for a vector its count table cannot hold.
-// logit(j) returns logit j of the vector, j in [0, V).
-template <int NT, class Logits>
-__device__ __forceinline__ void generic_stats(const Logits& logit, int token, float T, double P, int V,
-                                              double* hist256, Scratch<NT / 64>& sc,
-                                              VecRec* rec) {
+// `elems` yields this thread's logits (StreamedLogits or HeldLogits); zx is
+// the draft token's logit (NaN when there is none).
+template <int NT, class Elems>
+__device__ __forceinline__ void generic_stats(const Elems& elems, int token, float zx, float T,
+                                              double P, int V, double* hist256,
+                                              Scratch<NT / 64>& sc, VecRec* rec) {
   const int tid = threadIdx.x;
   const bool T_ok = T > 0.0f && isfinite(T);
   // pass 1: largest finite value, NaN / +inf, any finite entry
   float mx = -INFINITY;
   uint32_t fl = 0, nfin = 0;
-  for (int64_t j = tid; j < V; j += NT) {
-    const float z = logit(j);
+  elems.each([&](float z) {
     if (isnan(z) || z == INFINITY) fl |= SV_ROW_NONFINITE_LOGIT;
     else if (z > -INFINITY) { nfin = 1; mx = fmaxf(mx, z); }
-  }
+  });
   mx = wave_max_f(mx);
   fl = wave_or(fl | (nfin ? 0x80000000u : 0u));
   const int w = tid >> 6, l = tid & 63;
@@ -202,8 +239,6 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
   uint32_t flags = 0;
   for (int i = 0; i < NT / 64; ++i) { m = fmaxf(m, sc.f[i]); flags |= sc.u[i]; }
   __syncthreads();
-  const float zx = (token >= 0 && token < V) ? logit(token)
-                                               : __uint_as_float(0x7FC00000u);
   uint32_t status = flags & SV_ROW_NONFINITE_LOGIT;
   if (!(flags & 0x80000000u)) status |= SV_ROW_NO_FINITE;
   if (status || !T_ok) {
@@ -213,7 +248,7 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
   const float c2 = log2e_over_T(T);
   // pass 2: normaliser S
   double acc = 0.0;
-  for (int64_t j = tid; j < V; j += NT) acc += weight(logit(j), m, c2);
+  elems.each([&](float z) { acc += weight(z, m, c2); });
   const double S = block_sum_d<NT>(acc, sc);
   if (!(P < 1.0)) {
     if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, S, 0, zx, rec);
@@ -229,14 +264,16 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
     const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     for (int i = tid; i < 256; i += NT) hist256[i] = 0.0;
     __syncthreads();
-    for (int64_t j = tid; j < V; j += NT) {
-      const float z = logit(j);
-      if (!(z > -INFINITY)) continue;
+    elems.each([&](float z) {
+      // held values would otherwise keep pass 2's weights alive (and spill)
+      // instead of forming them again
+      asm volatile("" : "+v"(z));
+      if (!(z > -INFINITY)) return;
       const uint32_t k = order_key(z);
-      if ((k & hmask) != (prefix & hmask)) continue;
+      if ((k & hmask) != (prefix & hmask)) return;
       const double wgt = weight(z, m, c2);
       if (wgt > 0.0) atomicAdd(&hist256[(k >> shift) & 255u], wgt);
-    }
+    });
     __syncthreads();
     if (tid == 0) {
       double cum = above;
@@ -262,13 +299,45 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
   if (tid == 0) write_record(token, T, T_ok, V, m, key_value(prefix), kept, 0, zx, rec);
 }
 
+// The generic statistics over one stored vector: its draft token's logit
+// is read with the first pass.
+template <int NT, class Logits>
+__device__ __forceinline__ void generic_stats(const Logits& logit, int token, float T, double P,
+                                              int V, double* hist256, Scratch<NT / 64>& sc,
+                                              VecRec* rec) {
+  const float zx = (token >= 0 && token < V) ? logit(token) : __uint_as_float(0x7FC00000u);
+  generic_stats<NT>(StreamedLogits<NT, Logits>{logit, V}, token, zx, T, P, V, hist256, sc, rec);
+}
+
+// Logits per thread that the generic kernel holds in registers.
+constexpr int kGenHeld = 32;
+
+// fp32 logits of one stored vector (the generic kernel's dtype): a typed
+// read, so that the held loads carry no dtype branch and all issue at once.
+struct Fp32Logits {
+  const float* vec;
+  __device__ __forceinline__ float operator()(int64_t j) const { return vec[j]; }
+};
+
+// One workgroup per vector slot: HELD (fp32, V <= kGenThreads * kGenHeld)
+// reads the vector once into registers, otherwise every pass streams it.
+template <bool HELD>
 __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams p, int dtype) {
   __shared__ double hist256[256];
   __shared__ Scratch<kGenThreads / 64> sc;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
-  generic_stats<kGenThreads>(VecLogits{s.vec, dtype}, s.token, s.T, s.P, p.V, hist256, sc,
-                             p.recs + blockIdx.x);
+  const VecLogits logit{s.vec, dtype};
+  if constexpr (HELD) {
+    HeldLogits<kGenThreads, kGenHeld> held;
+    held.load(Fp32Logits{(const float*)s.vec}, p.V);
+    const float zx = (s.token >= 0 && s.token < p.V) ? logit(s.token)
+                                                      : __uint_as_float(0x7FC00000u);
+    generic_stats<kGenThreads>(held, s.token, zx, s.T, s.P, p.V, hist256, sc,
+                               p.recs + blockIdx.x);
+  } else {
+    generic_stats<kGenThreads>(logit, s.token, s.T, s.P, p.V, hist256, sc, p.recs + blockIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------- bf16 path
@@ -1256,7 +1325,12 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
       hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, p);
   } else {
     TimedScope ts(t, "stats_generic", s);
-    hipLaunchKernelGGL(stats_generic_kernel, dim3(nslots), dim3(kGenThreads), 0, s, p, dtype);
+    if (dtype == SV_FP32 && p.V <= kGenThreads * kGenHeld)
+      hipLaunchKernelGGL(stats_generic_kernel<true>, dim3(nslots), dim3(kGenThreads), 0, s, p,
+                         dtype);
+    else
+      hipLaunchKernelGGL(stats_generic_kernel<false>, dim3(nslots), dim3(kGenThreads), 0, s, p,
+                         dtype);
   }
   return hipGetLastError();
 }
