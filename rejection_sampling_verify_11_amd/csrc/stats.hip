@@ -948,7 +948,8 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
-    if (tid == 0) sh.next = take_ticket(p, queue);
+    // no counters (one vector per workgroup, see launch_stats): no next item
+    if (tid == 0) sh.next = p.tickets ? take_ticket(p, queue) : nitems;
     const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
     // the draft token's logit, loaded by every thread from one address (a
@@ -1312,7 +1313,13 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
     unsigned want = cus * (unsigned)kWgPerCu;
     if (want < (unsigned)kQueues) want = (unsigned)kQueues;
     const unsigned grid = nslots < want ? nslots : want;
-    {
+    // With every slot in use and no more slots than workgroups, each
+    // workgroup's first vector (its own index) is the whole schedule: no
+    // queue counters to arm, no plan launch.
+    StatsParams q = p;
+    if (!p.slot_list && nslots <= want) {
+      q.tickets = nullptr;
+    } else {
       TimedScope ts(t, "stats_plan", s);
       hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
     }
@@ -1320,9 +1327,9 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
     // execution as a kernel trace does
     hipEvent_t e0, e1;
     if (t && t->pair("stats_bf16", &e0, &e1))
-      hipExtLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, e0, e1, 0u, p);
+      hipExtLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, e0, e1, 0u, q);
     else
-      hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, p);
+      hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, q);
   } else {
     TimedScope ts(t, "stats_generic", s);
     if (dtype == SV_FP32 && p.V <= kGenThreads * kGenHeld)
