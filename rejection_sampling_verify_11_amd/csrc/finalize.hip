@@ -11,8 +11,8 @@
 // The draw is an inverse CDF in token-index order: y = min{j : C_j > u R},
 // C the inclusive prefix of r, R its total.  Pass 1 sums r per segment of
 // consecutive tokens; a scan over the segments finds the one holding u R;
-// pass 2 re-derives that segment's values token by token in fp64, scans
-// them across lanes and picks the token.  bf16 vectors that are 16-byte
+// pass 2 re-derives that segment's values token by token, scans them across
+// lanes in fp64 and picks the token.  bf16 vectors that are 16-byte
 // aligned with V a multiple of 8 are read in groups of NT / 64 segments,
 // one per wave (1024 tokens of both vectors for the residual, 2048 for p'
 // alone), with the next group's loads in flight; under a top-p cut on p'
@@ -23,8 +23,9 @@
 // the vector on average -- and the wave holding that segment locates the
 // token from its registers.  Other vectors (fp32, unaligned, ragged V) are
 // read in tiles of 1024 x 8 logits with 512-token segments.  Probabilities
-// are exp2 of fp32 arguments (v_exp_f32) times the 1/G normalisers; segment
-// and prefix sums are fp64.
+// are fp32 on both paths (exp2 of an fp32 argument, v_exp_f32, times the
+// fp32 1/G normaliser); a lane sums its tokens in fp32, and segment and
+// prefix sums are fp64.
 //
 // With a KV rollback that keeps pages mapped (no free stack, no pool), the
 // row's workgroup also rolls the row back on the accepted count it found
@@ -48,8 +49,7 @@ constexpr int kMaxSeg = 4096;         // V <= 2^21 on this path
 struct Dist {
   const void* vec;
   float m, tau, c2;  // c2 = log2(e) / T
-  double inv;
-  float invf;        // inv as fp32 (the bf16 fast path)
+  float invf;        // 1 / G, the kept mass's normaliser, in fp32
 };
 
 // Loads 8 consecutive logits starting at j0 (elements >= V read as -inf).
@@ -81,33 +81,24 @@ __device__ __forceinline__ void load8(const void* vec, int dtype, int64_t j0, in
   }
 }
 
-__device__ __forceinline__ double prob(const Dist& d, float z) {
-  if (!(z >= d.tau)) return 0.0;
-  return (double)__builtin_amdgcn_exp2f((z - d.m) * d.c2) * d.inv;
-}
-
-// The same probability in fp32: exp2 is an fp32 operation anyway, and the
-// residual max(0, p' - q') of two such values is within a few ulp of p' and
-// q'; sums are still taken in fp64.
+// The probability of logit z under d, in fp32: exp2 is an fp32 operation
+// anyway, and the residual max(0, p' - q') of two such values is within a
+// few ulp of p' and q'; sums are taken in fp64.
 __device__ __forceinline__ float prob_f(const Dist& d, float z) {
   return z >= d.tau ? __builtin_amdgcn_exp2f((z - d.m) * d.c2) * d.invf : 0.0f;
 }
 
-// r_j for the 8 logits at j0: residual max(0, p' - q') (mode 0) or p' (mode 1).
+// r_j for the 8 logits at j0: residual max(0, p' - q') (mode 0) or p' (mode
+// 1), from fp32 probabilities as on the bf16 path (the sums are fp64).
 __device__ __forceinline__ void r8(const Dist& P, const Dist& Q, int mode, int dtype,
-                                   int64_t j0, int V, bool aligned, double r[8]) {
+                                   int64_t j0, int V, bool aligned, float r[8]) {
   float zp[8], zq[8];
   load8(P.vec, dtype, j0, V, aligned, zp);
   if (mode == 0) load8(Q.vec, dtype, j0, V, aligned, zq);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const double pp = prob(P, zp[t]);
-    if (mode == 0) {
-      const double d = pp - prob(Q, zq[t]);
-      r[t] = d > 0.0 ? d : 0.0;
-    } else {
-      r[t] = pp;
-    }
+    const float pp = prob_f(P, zp[t]);
+    r[t] = mode == 0 ? fmaxf(pp - prob_f(Q, zq[t]), 0.0f) : pp;
   }
 }
 
@@ -499,11 +490,12 @@ __device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mod
     // pass 1: per-segment sums
     for (int s = 0; s < ntiles; ++s) {
       const int64_t j0 = (int64_t)s * kTile + 8 * tid;
-      double r[8];
+      float r[8];
       r8(P, Q, mode, dtype, j0, V, aligned, r);
-      double ls = 0.0;
+      float lf = 0.0f;  // a lane's 8 tokens in fp32, the wave's sum in fp64
 #pragma unroll
-      for (int t = 0; t < 8; ++t) ls += r[t];
+      for (int t = 0; t < 8; ++t) lf += r[t];
+      double ls = (double)lf;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
       if (l == 0) sc.seg[s * kWaves + w] = ls;
@@ -570,8 +562,11 @@ __device__ __forceinline__ int inverse_cdf(const Dist& P, const Dist& Q, int mod
     if (w == 0) {
       const int st = ss / kWaves, sw = ss % kWaves;
       const int64_t j0 = (int64_t)st * kTile + (int64_t)sw * kSeg + 8 * l;
+      float rf[8];
+      r8(P, Q, mode, dtype, j0, V, aligned, rf);
       double r[8];
-      r8(P, Q, mode, dtype, j0, V, aligned, r);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r[t] = (double)rf[t];
       double ls = 0.0;
 #pragma unroll
       for (int t = 0; t < 8; ++t) ls += r[t];
@@ -614,7 +609,6 @@ __device__ Dist make_dist(const void* base, int64_t vec_index, int64_t stride, i
   d.m = m;
   d.tau = tau;
   d.c2 = log2e_over_T(T);
-  d.inv = inv_kept;
   d.invf = (float)inv_kept;
   return d;
 }
