@@ -483,6 +483,32 @@ def test_deterministic_and_empty_batch():
     assert e["accepted"].numel() == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rows_alike_under_both_workgroup_sizes(dtype):
+    """600 rows take the draw with 512-thread workgroups (two or more rows
+    per CU), their first 48 alone with 1024-thread ones.  The inverse CDF's
+    segments do not depend on the workgroup size, nor do the statistics
+    records on the schedule, so those 48 rows' outputs are bit-identical.
+    Likewise the draft sampler, 600 x 4 draws against 48 x 4."""
+    big = W.workload4(3, device=DEV, B=600, k=4, V=24000)
+    t, d = big.target.to(dtype), big.draft.to(dtype)
+    T, P = big.temperature, big.top_p
+    n = 48
+    ta, sa = sv.draft_sample(d, T, P, seed=5, offset=2)
+    tb, sb = sv.draft_sample(d[:n], T[:n], P[:n], seed=5, offset=2)
+    torch.cuda.synchronize()
+    assert torch.equal(ta[:n], tb) and torch.equal(sa[:n], sb)
+    a = sv.verify_sample(t, d, ta, T, P, seed=5, offset=1)
+    b = sv.verify_sample(t[:n], d[:n], ta[:n], T[:n], P[:n], seed=5, offset=1)
+    torch.cuda.synchronize()
+    assert int((a["row_status"] != 0).sum()) == 0
+    for k in b:
+        x, y = a[k][:n], b[k]
+        if x.is_floating_point():
+            x, y = torch.nan_to_num(x, nan=-7.0), torch.nan_to_num(y, nan=-7.0)
+        assert torch.equal(x, y), k
+
+
 def test_output_law_through_gpu_path(oracle):
     """Chi-square of the emitted token at every reached position against p'
     on V = 16, run through the GPU library (20k rows x 10 rounds)."""
