@@ -15,13 +15,13 @@ class EventTimer final : public sv::Timer {
   static constexpr size_t kMax = 4096;
   ~EventTimer() override {
     for (auto& e : pool_) {
-      hipEventDestroy(e.first);
-      hipEventDestroy(e.second);
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
     }
   }
   void begin(const char* name, hipStream_t s) override {
     cur_ = take(name);
-    if (cur_ >= 0) hipEventRecord(pool_[cur_].first, s);
+    if (cur_ >= 0) (void)hipEventRecord(pool_[cur_].first, s);
   }
   bool pair(const char* name, hipEvent_t* start, hipEvent_t* stop) override {
     const long i = take(name);
@@ -32,7 +32,7 @@ class EventTimer final : public sv::Timer {
     return true;
   }
   void end(hipStream_t s) override {
-    if (cur_ >= 0) hipEventRecord(pool_[cur_].second, s);
+    if (cur_ >= 0) (void)hipEventRecord(pool_[cur_].second, s);
     cur_ = -1;
   }
   int read(int max_entries, const char** names, int32_t* launches, double* total_ms) {
@@ -41,7 +41,7 @@ class EventTimer final : public sv::Timer {
     std::vector<double> ms;
     for (size_t i = 0; i < used_; ++i) {
       float t = 0.f;
-      hipEventSynchronize(pool_[i].second);
+      (void)hipEventSynchronize(pool_[i].second);
       if (hipEventElapsedTime(&t, pool_[i].first, pool_[i].second) != hipSuccess) t = 0.f;
       size_t k = 0;
       while (k < un.size() && strcmp(un[k], names_[i]) != 0) ++k;
@@ -65,7 +65,7 @@ class EventTimer final : public sv::Timer {
     if (used_ == pool_.size()) {
       hipEvent_t a, b;
       if (hipEventCreate(&a) != hipSuccess) return -1;
-      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return -1; }
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return -1; }
       pool_.push_back({a, b});
     }
     const long i = (long)used_++;
@@ -125,7 +125,12 @@ size_t greedy_ws(int32_t B, int32_t K, int32_t V) {
 extern "C" {
 
 const char* sv_status_string(sv_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the argument's bits, not an enum value
+  // the C++ type cannot hold
+  static_assert(sizeof(sv_status) == sizeof(int), "sv_status is an int");
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SV_OK: return "ok";
     case SV_E_ARG: return "invalid argument";
     case SV_E_DTYPE: return "unsupported dtype";
@@ -157,9 +162,9 @@ sv_status sv_create(int hip_device, sv_handle* out) {
   if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(hip_device) == hipSuccess) {
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) h->scratch_dev = ptr;
-    hipSetDevice(prev);
+    (void)hipSetDevice(prev);
   }
-  hipGetLastError();  // a failed lookup only disables sv_verify_sample_noalloc
+  (void)hipGetLastError();  // a failed lookup only disables sv_verify_sample_noalloc
   *out = h;
   return SV_OK;
 }

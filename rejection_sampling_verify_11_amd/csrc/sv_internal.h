@@ -56,7 +56,10 @@ inline __host__ __device__ int slots_per_row(int K) { return 2 * K + 1; }
 
 // Greedy chunking of a vector over several workgroups.
 constexpr int kGreedyChunk = 4096;
-inline __host__ __device__ int greedy_chunks(int V) { return (V + kGreedyChunk - 1) / kGreedyChunk; }
+// (V >= 0; written so that it cannot overflow for any such V)
+inline __host__ __device__ int greedy_chunks(int V) {
+  return V / kGreedyChunk + (V % kGreedyChunk != 0 ? 1 : 0);
+}
 
 struct StatsParams {
   const void* target;
