@@ -294,8 +294,7 @@ def round_leg(dev, n):
         else:
             verify.run()
             roll.run()
-        sv.dynamic_k(acc, k, state)
-        sv.advance_offset(offset)
+        sv.close_round(acc, k, state, offset)
 
     # the controller moves k only once a row's window (64 rounds) is full:
     # run until it has settled, then time eager and replayed rounds in turn

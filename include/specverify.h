@@ -331,6 +331,16 @@ sv_status sv_dynamic_k(sv_handle h, const sv_dynk_args* a, hipStream_t s);
  * 8-byte aligned. */
 sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, hipStream_t s);
 
+/* The end of an on-device round in one launch: sv_dynamic_k(a), then
+ * sv_advance_offset(offset_dev, delta), with the results of those two calls
+ * on the same stream (the controller reads nothing the counter holds), for
+ * one kernel launch per round instead of two.  With a->B == 0 only the
+ * counter moves.  Errors: those of sv_check_dynk_args; SV_E_ARG for a NULL
+ * handle or an offset_dev that is NULL or not 8-byte aligned; nothing is
+ * launched on an error. */
+sv_status sv_close_round(sv_handle h, const sv_dynk_args* a, uint64_t* offset_dev,
+                         uint64_t delta, hipStream_t s);
+
 /* ------------------------------------------------------------------------ */
 /* Vocabulary-sharded statistics                                            */
 /* ------------------------------------------------------------------------ */

@@ -123,7 +123,7 @@ EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "s
            "sv_noalloc_scratch_bytes", "sv_verify_sample_noalloc",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
            "sv_check_verify_rollback_args", "sv_verify_sample_rollback",
-           "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset",
+           "sv_check_dynk_args", "sv_dynamic_k", "sv_advance_offset", "sv_close_round",
            "sv_shard_partial_bytes", "sv_shard_workspace_bytes", "sv_check_shard_stats_args",
            "sv_shard_stats", "sv_check_shard_combine_args", "sv_shard_combine",
            "sv_check_shard_draw_args", "sv_shard_draw_mass", "sv_shard_draw_locate")
@@ -182,6 +182,8 @@ def library():
                 L.sv_dynamic_k.restype = C.c_int
                 L.sv_advance_offset.argtypes = [_P, _P, C.c_uint64, _P]
                 L.sv_advance_offset.restype = C.c_int
+                L.sv_close_round.argtypes = [_P, C.POINTER(DynkArgs), _P, C.c_uint64, _P]
+                L.sv_close_round.restype = C.c_int
                 L.sv_shard_partial_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
                 L.sv_shard_partial_bytes.restype = C.c_size_t
                 L.sv_shard_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
@@ -526,6 +528,26 @@ def advance_offset(offset, delta=1, stream=None):
     if rc != SV_OK:
         raise SpecVerifyError("sv_advance_offset", rc)
     return offset
+
+
+def close_round(accepted, k_per_row, state, offset, delta=1, window=64, k_min=2, k_max=8,
+                up=(17, 20), down=(7, 10), stream=None):
+    """dynamic_k(...) then advance_offset(offset, delta) in one launch
+    (sv_close_round): the end of an on-device round."""
+    dev = k_per_row.device
+    B = k_per_row.shape[0] if k_per_row.dim() == 1 else -1
+    _i32(k_per_row, (B,), "k_per_row", dev)
+    _i32(accepted, (B,), "accepted", dev)
+    _i32(state, (B, window + 4), "state", dev)
+    if offset.dtype != torch.int64 or offset.numel() != 1 or offset.device != dev:
+        raise ValueError("offset must be a one-element int64 tensor on the rows' GPU")
+    a = DynkArgs(B, window, k_min, k_max, up[0], up[1], down[0], down[1], _ptr(accepted),
+                 _ptr(k_per_row), _ptr(state))
+    rc = library().sv_close_round(handle(dev), C.byref(a), _ptr(offset),
+                                  int(delta) & (2**64 - 1), _stream(dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError("sv_close_round", rc)
+    return k_per_row
 
 
 def dynk_state(B, window=64, device="cuda"):

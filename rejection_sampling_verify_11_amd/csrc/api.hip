@@ -120,6 +120,28 @@ size_t greedy_ws(int32_t B, int32_t K, int32_t V) {
   return align_up((size_t)B * (2 * (size_t)K + 1) * sv::greedy_chunks(V) * sizeof(sv::ArgmaxPart), 256);
 }
 
+// The controller update of every row, and the round counter advanced in the
+// same launch when offset_dev is given.
+sv_status dynk_launch(sv_handle h, const sv_dynk_args* a, uint64_t* offset_dev, uint64_t delta,
+                      hipStream_t s) {
+  sv::DynkParams p;
+  p.B = a->B;
+  p.W = a->window;
+  p.k_min = a->k_min;
+  p.k_max = a->k_max;
+  p.up_num = a->up_num;
+  p.up_den = a->up_den;
+  p.down_num = a->down_num;
+  p.down_den = a->down_den;
+  p.accepted = a->accepted;
+  p.k_per_row = a->k_per_row;
+  p.state = a->state;
+  p.offset_dev = offset_dev;
+  p.offset_delta = delta;
+  if (sv::launch_dynk(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -464,25 +486,21 @@ sv_status sv_check_dynk_args(const sv_dynk_args* a) {
   return SV_OK;
 }
 
+
 sv_status sv_dynamic_k(sv_handle h, const sv_dynk_args* a, hipStream_t s) {
   const sv_status st = sv_check_dynk_args(a);
   if (st != SV_OK) return st;
   if (!h) return SV_E_ARG;
   if (a->B == 0) return SV_OK;
-  sv::DynkParams p;
-  p.B = a->B;
-  p.W = a->window;
-  p.k_min = a->k_min;
-  p.k_max = a->k_max;
-  p.up_num = a->up_num;
-  p.up_den = a->up_den;
-  p.down_num = a->down_num;
-  p.down_den = a->down_den;
-  p.accepted = a->accepted;
-  p.k_per_row = a->k_per_row;
-  p.state = a->state;
-  if (sv::launch_dynk(p, s, h->active()) != hipSuccess) return SV_E_DEVICE;
-  return SV_OK;
+  return dynk_launch(h, a, nullptr, 0, s);
+}
+
+sv_status sv_close_round(sv_handle h, const sv_dynk_args* a, uint64_t* offset_dev,
+                         uint64_t delta, hipStream_t s) {
+  const sv_status st = sv_check_dynk_args(a);
+  if (st != SV_OK) return st;
+  if (!h || !offset_dev || ((uintptr_t)offset_dev & 7)) return SV_E_ARG;
+  return dynk_launch(h, a, offset_dev, delta, s);
 }
 
 sv_status sv_advance_offset(sv_handle h, uint64_t* offset_dev, uint64_t delta, hipStream_t s) {

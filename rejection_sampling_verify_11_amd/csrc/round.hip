@@ -7,7 +7,9 @@
 // (accepted | proposed << 16) per round.
 //
 // Round counter: the Philox offset of the next round, kept in device memory
-// so that a captured round needs no host update between replays.
+// so that a captured round needs no host update between replays.  A round
+// that ends with both steps takes them in one launch (the controller kernel
+// also advances the counter).
 #include "sv_internal.h"
 
 namespace sv {
@@ -15,6 +17,8 @@ namespace {
 
 __global__ void dynk_kernel(DynkParams p) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  // closing a round: the counter is read by no other thread of this launch
+  if (b == 0 && p.offset_dev) *p.offset_dev += p.offset_delta;
   if (b >= p.B) return;
   const int W = p.W;
   int32_t* st = p.state + (int64_t)b * (W + 4);
@@ -57,9 +61,9 @@ __global__ void advance_offset_kernel(uint64_t* offset_dev, uint64_t delta) {
 }  // namespace
 
 hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t) {
-  if (p.B == 0) return hipSuccess;
-  TimedScope ts(t, "dynamic_k", s);
-  hipLaunchKernelGGL(dynk_kernel, dim3((p.B + 255) / 256), dim3(256), 0, s, p);
+  if (p.B == 0 && !p.offset_dev) return hipSuccess;
+  TimedScope ts(t, p.offset_dev ? "close_round" : "dynamic_k", s);
+  hipLaunchKernelGGL(dynk_kernel, dim3(p.B > 0 ? (p.B + 255) / 256 : 1), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -214,6 +214,8 @@ struct DynkParams {
   const int32_t* accepted;
   int32_t* k_per_row;
   int32_t* state;
+  uint64_t* offset_dev;  // NULL, or the round counter to advance by offset_delta
+  uint64_t offset_delta;
 };
 
 // Optional event bracketing of each launch (see sv_timing_enable).

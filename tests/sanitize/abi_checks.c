@@ -231,6 +231,7 @@ static void dynk_checks(void) {
   CHECK(sv_check_dynk_args(&d) == SV_OK);
   CHECK(sv_dynamic_k(NULL, &d, NULL) == SV_E_ARG);
   CHECK(sv_advance_offset(NULL, (uint64_t*)FAKE(8), 1, NULL) == SV_E_ARG);
+  CHECK(sv_close_round(NULL, &d, (uint64_t*)FAKE(8), 1, NULL) == SV_E_ARG);
   for (int it = 0; it < 20000; ++it) {
     sv_dynk_args m = d;
     switch (rnd() % 9) {
@@ -246,6 +247,7 @@ static void dynk_checks(void) {
     }
     const sv_status s = sv_check_dynk_args(&m);
     CHECK(s >= SV_OK && s <= SV_E_INTERNAL);
+    CHECK(sv_close_round(NULL, &m, (uint64_t*)extreme_ptr(), rnd(), NULL) != SV_OK);
   }
 }
 

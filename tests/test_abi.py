@@ -211,6 +211,11 @@ def test_dynk_validation():
     assert L.sv_check_dynk_args(C.byref(a)) == _abi.SV_OK  # nothing to do
     assert L.sv_dynamic_k(None, C.byref(a), None) == _abi.SV_E_ARG  # no handle
     assert L.sv_advance_offset(None, 0x10000, 1, None) == _abi.SV_E_ARG
+    # closing a round: the controller's checks, then a handle and an aligned counter
+    assert L.sv_close_round(None, C.byref(a), 0x10000, 1, None) == _abi.SV_E_ARG
+    b = _abi.DynkArgs.from_buffer_copy(a)
+    b.window = 0
+    assert L.sv_close_round(None, C.byref(b), 0x10000, 1, None) == _abi.SV_E_ARG
 
 
 def test_device_offset_must_be_aligned():

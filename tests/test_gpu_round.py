@@ -74,6 +74,41 @@ def test_dynamic_k_other_thresholds_and_window_one(oracle):
         check_windows(g_st, o_h, Wn)
 
 
+def test_close_round_is_the_two_calls():
+    """sv_close_round against sv_dynamic_k then sv_advance_offset, round after
+    round (k, state and counter bit for bit), eagerly and replayed from a
+    captured graph; with no rows only the counter moves."""
+    rng = np.random.default_rng(5)
+    B, Wn, R = 700, 4, 40
+    k0 = torch.from_numpy(rng.integers(1, 10, B).astype(np.int32)).to(DEV)
+    two = dict(k=k0.clone(), st=sv.dynk_state(B, Wn, DEV),
+               off=torch.tensor([2**63 - 3], dtype=torch.int64, device=DEV))
+    one = dict(k=k0.clone(), st=sv.dynk_state(B, Wn, DEV), off=two["off"].clone())
+    rep = dict(k=k0.clone(), st=sv.dynk_state(B, Wn, DEV), off=two["off"].clone())
+    acc = torch.zeros(B, dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.close_round(acc, rep["k"], rep["st"], rep["off"], 3, window=Wn)
+    for r in range(R):
+        kk = two["k"].cpu().numpy()
+        a = rng.binomial(np.clip(kk, 0, 8), 0.8).astype(np.int32)
+        a[rng.random(B) < 0.03] = -1
+        acc.copy_(torch.from_numpy(a))
+        sv.dynamic_k(acc, two["k"], two["st"], window=Wn)
+        sv.advance_offset(two["off"], 3)
+        sv.close_round(acc, one["k"], one["st"], one["off"], 3, window=Wn)
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ("k", "st", "off"):
+            assert torch.equal(two[n], one[n]), (r, n)
+            assert torch.equal(two[n], rep[n]), (r, n)
+    assert len(np.unique(two["k"].cpu().numpy())) >= 3  # the controller moved
+    empty = torch.zeros(0, dtype=torch.int32, device=DEV)
+    off = torch.zeros(1, dtype=torch.int64, device=DEV)
+    sv.close_round(empty, empty.clone(), sv.dynk_state(0, Wn, DEV), off, 7, window=Wn)
+    assert int(off.item()) == 7
+
+
 def test_advance_offset_wraps():
     off = torch.tensor([-3], dtype=torch.int64, device=DEV)  # 2^64 - 3 as a word
     sv.advance_offset(off, 5)
@@ -107,8 +142,9 @@ def grow(st, k):
 class Chain:
     """One device-resident chain of rounds over fixed buffers."""
 
-    def __init__(self, target, draft, temperature, state, k0):
+    def __init__(self, target, draft, temperature, state, k0, close_in_one_launch=False):
         B = temperature.shape[0]
+        self.close_in_one_launch = close_in_one_launch
         self.offset = torch.zeros(1, dtype=torch.int64, device=DEV)
         self.k = torch.from_numpy(k0.copy()).to(DEV)
         self.toks = torch.full((B, K), -1, dtype=torch.int32, device=DEV)
@@ -129,8 +165,12 @@ class Chain:
         self.draft_call.run()
         self.verify_call.run()
         self.roll.run()
-        sv.dynamic_k(self.verify_call.outputs["accepted"], self.k, self.dyn, window=WIN)
-        sv.advance_offset(self.offset, 1)
+        if self.close_in_one_launch:
+            sv.close_round(self.verify_call.outputs["accepted"], self.k, self.dyn, self.offset,
+                           1, window=WIN)
+        else:
+            sv.dynamic_k(self.verify_call.outputs["accepted"], self.k, self.dyn, window=WIN)
+            sv.advance_offset(self.offset, 1)
 
     def host_state(self):
         s = {n: t.cpu().numpy() for n, t in self.kv.items()}
@@ -150,7 +190,9 @@ def test_captured_round_matches_eager_and_oracle(oracle):
     8 rounds.  Every round the graph replay equals the eager round bit for
     bit, the draft tokens and the verification are checked against the
     oracle on the same inputs, and the oracle's rollback and controller,
-    fed the GPU's accepted counts, must give the device's state exactly."""
+    fed the GPU's accepted counts, must give the device's state exactly.
+    The captured round closes with sv_close_round, the eager one with the
+    controller and counter calls apart."""
     B, R = 16, 8
     rows = W.workload5_rows(3, B=B)
     T = rows.temperature
@@ -167,7 +209,7 @@ def test_captured_round_matches_eager_and_oracle(oracle):
     dft = torch.empty((B, K, 128256), dtype=torch.bfloat16, device=DEV)
     T_d = T.to(DEV)
     eager = Chain(tgt, dft, T_d, o, o_k)
-    graph = Chain(tgt, dft, T_d, o, o_k)
+    graph = Chain(tgt, dft, T_d, o, o_k, close_in_one_launch=True)
 
     inp = W.workload5(0, rows, torch.from_numpy(o_k))
     tgt.copy_(inp.target)
