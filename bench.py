@@ -152,20 +152,28 @@ def greedy_leg(dev, n):
     from rejection_sampling_verify_11_amd import workloads as W
     B, K, V = 64, 8, 128256
     zt, toks = W.workload3(0, device=dev, B=B, k=K, V=V)
-    call = sv.VerifyCall("greedy", zt, None, toks)
+    # one launch (sv_verify_greedy_one_launch, a zeroed state kept by the
+    # call), and the two launches of sv_verify_greedy for comparison
+    call = sv.VerifyCall("greedy", zt, None, toks, one_launch=True)
+    two = sv.VerifyCall("greedy", zt, None, toks)
     for _ in range(20):
         call.run()
+        two.run()
     ms = timed(call.run, n, dev)
+    ms_two = timed(two.run, n, dev)
     sv.timing_enable(dev, True)
     for _ in range(20):
         call.run()
+        two.run()
     torch.cuda.synchronize()
     kt = sv.timing_read(dev)
     sv.timing_enable(dev, False)
     assert int((call.outputs["row_status"] != 0).sum()) == 0
+    assert all(torch.equal(call.outputs[k], two.outputs[k]) for k in call.outputs)
     target_bytes = B * (K + 1) * V * 2
     return {"workload": "B=64 k=8 V=128256 bf16 greedy, draft = target argmax w.p. 0.85",
             "ms_per_call": ms, "target_gbs": target_bytes / (ms * 1e-3) / 1e9,
+            "two_launch_ms_per_call": ms_two,
             "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "verified_positions_per_s": B * K / (ms * 1e-3),
             "mean_accepted": call.outputs["accepted"].float().mean().item()}

@@ -208,6 +208,23 @@ sv_status sv_verify_sample_noalloc(sv_handle h, const sv_verify_args* a, hipStre
  * q_at_draft are not written. */
 sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s);
 
+/* Greedy verification in one launch instead of two, for callers that keep a
+ * small state buffer between calls: same arguments, checks and results as
+ * sv_verify_greedy (the same decision, [SSD] §2.4 and §5.2), bit for bit.
+ * Each chunk's maximum is published with a device-scope atomic into
+ * `state` and the last chunk of a row decides the row, so no second kernel
+ * folds the chunks.  `state`: device memory of at least
+ * sv_greedy_state_bytes(B, k_max) bytes, 8-byte aligned, all zero before
+ * its first call; every call leaves it zero again.  Two calls must not use
+ * one state buffer at the same time.  Layouts other than the streaming one
+ * (bf16, 16-byte aligned vectors and strides, V a multiple of 8) take
+ * sv_verify_greedy's two launches and leave the state as it is.  Errors:
+ * those of sv_verify_greedy; SV_E_WORKSPACE for a state that is NULL,
+ * misaligned or too small; nothing is launched on an error. */
+size_t sv_greedy_state_bytes(int32_t B, int32_t k_max);
+sv_status sv_verify_greedy_one_launch(sv_handle h, const sv_verify_args* a, void* state,
+                                      size_t state_bytes, hipStream_t s);
+
 /* Draft sampling, the step before verification ([SSD] §4.2; [FS] §3.2):
  * writes draft_tokens[b][i] = inverse CDF of q'_i with u(b,i,2) for i < k_b
  * and -1 beyond (draft_tokens is an OUTPUT here, cast away from const).

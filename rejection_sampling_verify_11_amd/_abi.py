@@ -120,6 +120,7 @@ class ShardDrawArgs(C.Structure):
 EXPORTS = ("sv_create", "sv_destroy", "sv_status_string", "sv_timing_enable", "sv_timing_read",
            "sv_verify_workspace_bytes",
            "sv_check_verify_args", "sv_verify_sample", "sv_verify_greedy", "sv_draft_sample",
+           "sv_greedy_state_bytes", "sv_verify_greedy_one_launch",
            "sv_noalloc_scratch_bytes", "sv_verify_sample_noalloc",
            "sv_rollback_workspace_bytes", "sv_check_rollback_args", "sv_kv_rollback",
            "sv_check_verify_rollback_args", "sv_verify_sample_rollback",
@@ -162,6 +163,11 @@ def library():
                           L.sv_verify_sample_noalloc):
                     f.argtypes = [_P, C.POINTER(VerifyArgs), _P]
                     f.restype = C.c_int
+                L.sv_greedy_state_bytes.argtypes = [C.c_int32, C.c_int32]
+                L.sv_greedy_state_bytes.restype = C.c_size_t
+                L.sv_verify_greedy_one_launch.argtypes = [_P, C.POINTER(VerifyArgs), _P,
+                                                          C.c_size_t, _P]
+                L.sv_verify_greedy_one_launch.restype = C.c_int
                 L.sv_noalloc_scratch_bytes.argtypes = []
                 L.sv_noalloc_scratch_bytes.restype = C.c_size_t
                 L.sv_rollback_workspace_bytes.argtypes = [C.c_int32]
@@ -303,10 +309,13 @@ class VerifyCall:
     block filled once; run() only enqueues the library call."""
 
     def __init__(self, mode, target, draft, draft_tokens=None, temperature=None, top_p=None,
-                 k_per_row=None, seed=0, offset=0, flags=0, want_probs=True, noalloc=False):
+                 k_per_row=None, seed=0, offset=0, flags=0, want_probs=True, noalloc=False,
+                 one_launch=False):
         self.mode = mode  # "sample", "greedy" or "draft"
         if noalloc and mode != "sample":
             raise ValueError("only sampled verification has a variant without workspace")
+        if one_launch and mode != "greedy":
+            raise ValueError("only greedy verification has a one-launch variant")
         ref = draft if mode == "draft" else target
         dev = ref.device
         if dev.type != "cuda":
@@ -382,6 +391,13 @@ class VerifyCall:
                     "draft": L.sv_draft_sample}[mode]
         if noalloc:
             self._fn = L.sv_verify_sample_noalloc
+        self.state = None
+        if one_launch:
+            # zero once; every call leaves it zero
+            self.state = torch.zeros(max(L.sv_greedy_state_bytes(B, K), 256), dtype=torch.uint8,
+                                     device=dev)
+            st, nst = _ptr(self.state), self.state.numel()
+            self._fn = lambda h, ref, s: L.sv_verify_greedy_one_launch(h, ref, st, nst, s)
         self._h = handle(dev)
         self._ref = C.byref(self.args)
 

@@ -359,11 +359,8 @@ sv_status sv_draft_sample(sv_handle h, const sv_verify_args* a, hipStream_t s) {
   return SV_OK;
 }
 
-sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s) {
-  const sv_status st = sv_check_verify_args(a, 1);
-  if (st != SV_OK) return st;
-  if (!h) return SV_E_ARG;
-  if (a->B == 0) return SV_OK;
+namespace {
+sv_status greedy_launch(sv_handle h, const sv_verify_args* a, void* state, hipStream_t s) {
   sv::GreedyParams g;
   g.target = a->target_logits;
   g.draft = a->draft_logits;
@@ -376,12 +373,39 @@ sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s) 
   g.V = a->V;
   g.dtype = a->dtype;
   g.parts = (sv::ArgmaxPart*)a->workspace;
+  g.state = state;
   g.out_tokens = a->out_tokens;
   g.accepted = a->accepted;
   g.num_emitted = a->num_emitted;
   g.row_status = a->row_status;
   if (sv::launch_greedy(g, h->num_cus, s, h->active()) != hipSuccess) return SV_E_DEVICE;
   return SV_OK;
+}
+}  // namespace
+
+sv_status sv_verify_greedy(sv_handle h, const sv_verify_args* a, hipStream_t s) {
+  const sv_status st = sv_check_verify_args(a, 1);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (a->B == 0) return SV_OK;
+  return greedy_launch(h, a, nullptr, s);
+}
+
+size_t sv_greedy_state_bytes(int32_t B, int32_t k_max) {
+  if (B < 0 || k_max < 1 || k_max > SV_MAX_K) return 0;
+  const size_t n = align_up(sv::greedy_state_bytes(B, k_max), 256);
+  return n > 0 ? n : 256;
+}
+
+sv_status sv_verify_greedy_one_launch(sv_handle h, const sv_verify_args* a, void* state,
+                                      size_t state_bytes, hipStream_t s) {
+  const sv_status st = sv_check_verify_args(a, 1);
+  if (st != SV_OK) return st;
+  if (!h) return SV_E_ARG;
+  if (!state || ((uintptr_t)state & 7) || state_bytes < sv_greedy_state_bytes(a->B, a->k_max))
+    return SV_E_WORKSPACE;
+  if (a->B == 0) return SV_OK;
+  return greedy_launch(h, a, state, s);
 }
 
 size_t sv_rollback_workspace_bytes(int32_t B) {

@@ -13,6 +13,18 @@
 // 256 threads per chunk.  Kernel 2 runs one wave per row: lane i folds the
 // chunks of position i (target, and draft when draft logits are given), and
 // a ballot finds the first mismatch.
+//
+// One launch instead of two, for callers that keep a zeroed state buffer
+// (argmax_fused_kernel): the streaming grid publishes each chunk's maximum
+// into its vector's slot with a device-scope atomic max on a packed
+// (order key, -index) word, then counts the chunk for its row; the row's
+// last chunk reads the row's slots, decides the row and zeroes its state.
+// Device-scope atomics are performed where every XCD sees them, and a
+// chunk counts only once its maximum's atomic has returned, so the last
+// chunk finds every maximum in place without a cache write-back.  Items are
+// taken chunk-major (every vector's chunk 0, then chunk 1, ...) so that the
+// chunks in flight at once belong to many vectors and rows: their atomics
+// do not queue on one address.
 #include <math.h>
 
 #include "sv_internal.h"
@@ -387,6 +399,223 @@ __global__ __launch_bounds__(256) void greedy_finalize_kernel(GreedyParams p) {
   }
 }
 
+
+// ---- one launch (argmax_fused_kernel)
+
+// Chunk item `item` taken chunk-major (item = c * nvec + v): its vector's
+// address (valid whether or not the row uses the vector), row and chunk.
+struct FusedItem {
+  const uint16_t* vec;
+  int b, v, g0, n8;
+  bool used;
+};
+__device__ __forceinline__ FusedItem fused_item(const GreedyParams& p, int item, int nvec,
+                                                int n8v) {
+  FusedItem f;
+  const int c = item / nvec;
+  f.v = item % nvec;
+  const int nvec_t = p.B * (p.K + 1);
+  bool draft_side;
+  int pos;
+  if (f.v < nvec_t) { f.b = f.v / (p.K + 1); pos = f.v % (p.K + 1); draft_side = false; }
+  else { f.b = (f.v - nvec_t) / p.K; pos = (f.v - nvec_t) % p.K; draft_side = true; }
+  const int kb = p.k_per_row ? p.k_per_row[f.b] : p.K;
+  f.used = kb >= 1 && kb <= p.K && (draft_side ? pos < kb : pos <= kb);
+  f.vec = draft_side ? (const uint16_t*)p.draft + ((int64_t)f.b * p.K + pos) * p.d_stride
+                     : (const uint16_t*)p.target + ((int64_t)f.b * (p.K + 1) + pos) * p.t_stride;
+  f.g0 = c * (kGreedyChunk / 8);
+  f.n8 = min(kGreedyChunk / 8, n8v - f.g0);
+  return f;
+}
+
+// The chunk's largest and smallest order keys and the first index holding
+// the largest value, as argmax_stream_kernel finds them.
+__device__ __forceinline__ void fused_chunk(const FusedItem& f, uint32_t& cmax, uint32_t& cmin,
+                                            int& first) {
+  const int l = threadIdx.x & 63;
+  const uint4* body = (const uint4*)f.vec + f.g0;
+  uint4 d[kLaneLoads];
+#pragma unroll
+  for (int j = 0; j < kLaneLoads; ++j) d[j] = body[min(l + 64 * j, f.n8 - 1)];
+  uint32_t jmax[kLaneLoads];
+  u16x2 kmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+  for (int j = 0; j < kLaneLoads; ++j) {
+    const bool valid = l + 64 * j < f.n8;
+    const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u16x2 k = order_keys(ws[q]);
+      m = __builtin_elementwise_max(m, k);
+      kmin = __builtin_elementwise_min(kmin, k);
+    }
+    jmax[j] = valid ? max((uint32_t)m.x, (uint32_t)m.y) : 0u;
+  }
+  cmax = 0;
+#pragma unroll
+  for (int j = 0; j < kLaneLoads; ++j) cmax = max(cmax, jmax[j]);
+  cmin = min((uint32_t)kmin.x, (uint32_t)kmin.y);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o, 64));
+    cmin = min(cmin, (uint32_t)__shfl_xor((int)cmin, o, 64));
+  }
+  int jstar = 0;
+  uint64_t bal = 0;
+#pragma unroll
+  for (int j = kLaneLoads - 1; j >= 0; --j) {
+    const uint64_t bj = __ballot(same_value(jmax[j], cmax));
+    if (bj) { jstar = j; bal = bj; }
+  }
+  const int L = bal ? __builtin_ctzll(bal) : 0;
+  first = 0x7FFFFFFF;
+#pragma unroll
+  for (int j = 0; j < kLaneLoads; ++j) {
+    if (j == jstar && l == L) {
+      const uint32_t ws[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+      for (int t = 7; t >= 0; --t) {
+        const uint32_t h = t & 1 ? ws[t >> 1] >> 16 : ws[t >> 1] & 0xFFFFu;
+        first = same_value(key_of(h), cmax) ? 8 * (f.g0 + l + 64 * j) + t : first;
+      }
+    }
+  }
+  first = __shfl(first, L, 64);
+}
+
+struct FusedState {
+  uint32_t* cnt;              // per row: chunks counted so far
+  unsigned long long* best;   // per vector: largest (order key << 32 | ~index)
+  uint32_t* flg;              // per vector: SV_ROW_NONFINITE_LOGIT if seen
+};
+
+// The decision of row b by one wave, as greedy_finalize_kernel takes it,
+// from the row's published maxima; then the row's state is zeroed.  A
+// vector's maximum holds only chunks whose largest value is below +inf (a
+// chunk holding +inf or a NaN flags the vector instead), so the vector has
+// a finite value iff its maximum is finite, the rule the chunk records
+// follow.
+__device__ __forceinline__ void fused_decide_row(const GreedyParams& p, int b,
+                                                 const FusedState& s) {
+  const int l = threadIdx.x & 63, K = p.K;
+  const int kb = p.k_per_row ? p.k_per_row[b] : K;
+  const int xt = (!p.draft && l < K) ? p.tokens[(int64_t)b * K + l] : -1;
+  const int vt = b * (K + 1) + min(l, K);
+  const int vd = p.B * (K + 1) + b * K + min(l, K - 1);
+  const unsigned long long kt = __hip_atomic_load(&s.best[(size_t)vt * kGreedyBestStride],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t ftv = __hip_atomic_load(&s.flg[(size_t)vt * kGreedyFlgStride], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long kd = 0;
+  uint32_t fdv = 0;
+  if (p.draft) {
+    kd = __hip_atomic_load(&s.best[(size_t)vd * kGreedyBestStride], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    fdv = __hip_atomic_load(&s.flg[(size_t)vd * kGreedyFlgStride], __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+  auto flags_of = [](unsigned long long k, uint32_t f) {
+    const uint32_t key = (uint32_t)(k >> 32);
+    return f | (key > kKeyNegInf && key < kKeyPosInf ? kSawFinite : 0u);
+  };
+  const uint32_t ft = flags_of(kt, ftv), fd = flags_of(kd, fdv);
+  const int gt = (int)(0xFFFFFFFFu - (uint32_t)kt), gd = (int)(0xFFFFFFFFu - (uint32_t)kd);
+  const bool kok = kb >= 1 && kb <= K;
+  uint32_t st = kok ? 0u : (uint32_t)SV_ROW_BAD_K;
+  int g = -1, x = -1;
+  if (kok) {
+    uint32_t fl = 0;
+    if (l <= kb) {
+      g = gt;
+      fl |= ft & SV_ROW_NONFINITE_LOGIT;
+      if (!(ft & kSawFinite)) fl |= SV_ROW_NO_FINITE;
+    }
+    if (l < kb) {
+      if (p.draft) {
+        x = gd;
+        fl |= fd & SV_ROW_NONFINITE_LOGIT;
+        if (!(fd & kSawFinite)) fl |= SV_ROW_NO_FINITE;
+      } else {
+        x = xt;
+        if (x < 0 || x >= p.V) fl |= SV_ROW_BAD_TOKEN;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+    st = fl;
+  }
+  const uint64_t miss = __ballot(kok && l < kb && x != g);
+  const int acc = miss ? __builtin_ctzll(miss) : kb;
+  const int y = __shfl(g, (acc >= 0 && acc < 64) ? acc : 0, 64);
+  int32_t* out = p.out_tokens + (int64_t)b * (K + 1);
+  if (l <= K) out[l] = st ? -1 : l < acc ? x : l == acc ? y : -1;
+  if (l == 0) {
+    p.accepted[b] = st ? -1 : acc;
+    if (p.num_emitted) p.num_emitted[b] = st ? 0 : acc + 1;
+    if (p.row_status) p.row_status[b] = (int32_t)st;
+  }
+  // every chunk of the row has been counted: nothing else touches its state
+  if (l <= K) {
+    s.best[(size_t)vt * kGreedyBestStride] = 0ull;
+    s.flg[(size_t)vt * kGreedyFlgStride] = 0u;
+  }
+  if (p.draft && l < K) {
+    s.best[(size_t)vd * kGreedyBestStride] = 0ull;
+    s.flg[(size_t)vd * kGreedyFlgStride] = 0u;
+  }
+  if (l == 0) s.cnt[(size_t)b * kGreedyCntStride] = 0u;
+}
+
+// The streaming grid of argmax_stream_kernel, chunk-major, with the fold and
+// the decision of each row done by the row's last chunk.  Every item counts
+// for its row, used or not (a row with an invalid k_b uses none), so every
+// row is decided once.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, kStreamWgPerCu)))
+void argmax_fused_kernel(GreedyParams p, int nitems, int nvec) {
+  const int l = threadIdx.x & 63;
+  const int waves = gridDim.x * (kThreads / 64);
+  const int n8v = p.V >> 3;
+  FusedState s;
+  s.cnt = (uint32_t*)p.state;
+  s.best = (unsigned long long*)(s.cnt + (size_t)p.B * kGreedyCntStride);
+  s.flg = (uint32_t*)(s.best + (size_t)nvec * kGreedyBestStride);
+  const uint32_t per_row =
+      (uint32_t)greedy_chunks(p.V) * (uint32_t)(p.K + 1 + (p.draft ? p.K : 0));
+  for (int item = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); item < nitems; item += waves) {
+    const FusedItem f = fused_item(p, item, nvec, n8v);
+    unsigned long long ret = 0;
+    if (f.used) {  // wave-uniform
+      uint32_t cmax, cmin;
+      int first;
+      fused_chunk(f, cmax, cmin, first);
+      if (l == 0) {
+        if (cmax >= kKeyPosInf || cmin < kKeyNegInf)  // +inf or a NaN
+          ret = __hip_atomic_fetch_or(&s.flg[(size_t)f.v * kGreedyFlgStride],
+                                      (uint32_t)SV_ROW_NONFINITE_LOGIT, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        if (cmax < kKeyPosInf) {
+          const uint32_t key = cmax == 0x7FFFu ? 0x8000u : cmax;  // the two zeros are one value
+          const unsigned long long packed =
+              ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)first);
+          ret |= __hip_atomic_fetch_max(&s.best[(size_t)f.v * kGreedyBestStride], packed,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    // the chunk counts for its row once its atomics have returned: the
+    // increment depends on their result (it is never 2, but the compiler
+    // cannot know that, so it waits for them)
+    uint32_t prev = 0;
+    if (l == 0) {
+      const uint32_t inc = ret == ~0ull ? 2u : 1u;
+      prev = __hip_atomic_fetch_add(&s.cnt[(size_t)f.b * kGreedyCntStride], inc, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
+    prev = (uint32_t)__shfl((int)prev, 0, 64);
+    if (prev == per_row - 1) fused_decide_row(p, f.b, s);
+  }
+}
 }  // namespace
 
 hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Timer* t) {
@@ -401,6 +630,12 @@ hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Time
     const unsigned want = cus * (unsigned)kStreamWgPerCu;
     const unsigned waves_needed = nitems;
     const unsigned grid = min(want, (waves_needed + kThreads / 64 - 1) / (kThreads / 64));
+    if (p.state) {
+      TimedScope ts(t, "greedy_fused", s);
+      hipLaunchKernelGGL(argmax_fused_kernel, dim3(grid), dim3(kThreads), 0, s, p, (int)nitems,
+                         nvec);
+      return hipGetLastError();
+    }
     TimedScope ts(t, "greedy_argmax", s);
     hipLaunchKernelGGL(argmax_stream_kernel, dim3(grid), dim3(kThreads), 0, s, p, (int)nitems);
   } else {

@@ -54,6 +54,17 @@ static_assert(sizeof(RollRec) == 16, "RollRec layout");
 // Vector slots of one row: target positions 0..K, then draft positions 0..K-1.
 inline __host__ __device__ int slots_per_row(int K) { return 2 * K + 1; }
 
+// The one-launch greedy path's state: row counters, then the largest packed
+// (order key, -index) of every vector, then every vector's flags, each
+// entry on its own 128 or 64 bytes.
+constexpr int kGreedyCntStride = 32;   // uint32 words per row counter
+constexpr int kGreedyBestStride = 8;   // uint64 words per vector maximum
+constexpr int kGreedyFlgStride = 16;   // uint32 words per vector's flags
+inline size_t greedy_state_bytes(int B, int K) {  // for any draft-logits choice
+  const size_t nvec = (size_t)B * (2 * (size_t)K + 1);
+  return (size_t)B * kGreedyCntStride * 4 + nvec * (kGreedyBestStride * 8 + kGreedyFlgStride * 4);
+}
+
 // Greedy chunking of a vector over several workgroups.
 constexpr int kGreedyChunk = 4096;
 // (V >= 0; written so that it cannot overflow for any such V)
@@ -177,6 +188,7 @@ struct GreedyParams {
   const int32_t* k_per_row;
   int32_t B, K, V, dtype;
   ArgmaxPart* parts;
+  void* state;  // NULL: two launches; else the one-launch path's zeroed state
   int32_t* out_tokens;
   int32_t* accepted;
   int32_t* num_emitted;

@@ -166,6 +166,8 @@ static void verify_checks(void) {
   CHECK(sv_verify_greedy(NULL, &a, NULL) == SV_E_ARG);
   CHECK(sv_draft_sample(NULL, &a, NULL) == SV_E_ARG);
   CHECK(sv_verify_sample_noalloc(NULL, &a, NULL) == SV_E_ARG);
+  CHECK(sv_verify_greedy_one_launch(NULL, &a, FAKE(0x50000000u), sv_greedy_state_bytes(256, 6),
+                                    NULL) == SV_E_ARG);
   CHECK(sv_verify_sample(NULL, NULL, NULL) == SV_E_ARG);
 
   /* sizes over the whole range, and random mutations of valid blocks */
@@ -181,6 +183,8 @@ static void verify_checks(void) {
     const sv_status s = sv_check_verify_args(&m, mode);
     CHECK(s >= SV_OK && s <= SV_E_INTERNAL);
     CHECK(sv_verify_sample(NULL, &m, NULL) != SV_OK);
+    (void)sv_greedy_state_bytes(extreme_i32(), extreme_i32());
+    CHECK(sv_verify_greedy_one_launch(NULL, &m, extreme_ptr(), extreme_size(), NULL) != SV_OK);
     sv_rollback_args r = good_rollback(B, K);
     r.accepted = m.accepted;
     if (rnd() & 1) mutate_rollback(&r);

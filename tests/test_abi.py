@@ -137,6 +137,20 @@ def test_entry_points_validate_before_touching_the_device():
     assert L.sv_verify_sample(None, C.byref(e), None) == _abi.SV_E_ARG  # but a handle
 
 
+def test_one_launch_greedy_state_checks():
+    L = _abi.library()
+    assert L.sv_greedy_state_bytes(64, 8) >= 64 * 128 + 64 * 17 * 128
+    assert L.sv_greedy_state_bytes(1, 0) == 0
+    a = good_args(4, 3, 1000)
+    n = L.sv_greedy_state_bytes(4, 3)
+    f = L.sv_verify_greedy_one_launch
+    assert f(None, C.byref(a), 0x10000, n, None) == _abi.SV_E_ARG        # no handle
+    h = C.c_void_p(0x1)  # never dereferenced: the state is checked first
+    assert f(h, C.byref(a), None, n, None) == _abi.SV_E_WORKSPACE
+    assert f(h, C.byref(a), 0x10004, n, None) == _abi.SV_E_WORKSPACE     # misaligned
+    assert f(h, C.byref(a), 0x10000, n - 1, None) == _abi.SV_E_WORKSPACE
+
+
 def test_workspace_sizes():
     L = _abi.library()
     n = L.sv_verify_workspace_bytes(256, 6, 151936, 1, 0)

@@ -91,6 +91,95 @@ def test_greedy_row_errors(oracle):
     assert list(o["row_status"]) == [0, 1, 1, 2, 4, 4, 8, 0]
 
 
+# ------------------------------------------------------ greedy in one launch
+
+def one_launch_matches(target, toks=None, draft=None, k_per_row=None, calls=3):
+    """sv_verify_greedy_one_launch against sv_verify_greedy on the same
+    inputs, bit for bit, over several calls on one state buffer; the state
+    is all zero after every call."""
+    two = sv.VerifyCall("greedy", target, draft, toks, k_per_row=k_per_row)
+    one = sv.VerifyCall("greedy", target, draft, toks, k_per_row=k_per_row, one_launch=True)
+    ref = {k: v.clone() for k, v in two.run().items()}
+    for c in range(calls):
+        out = one.run()
+        torch.cuda.synchronize()
+        for k in GREEDY_KEYS:
+            assert torch.equal(out[k], ref[k]), (c, k)
+        assert int(one.state.count_nonzero()) == 0, c
+    return ref
+
+
+def test_one_launch_greedy_full_size(oracle):
+    """Workload 3 (B=64, k=8, V=128256) through the one-launch path, four
+    rounds on one state buffer, against the oracle and the two launches."""
+    zt, toks = W.workload3(0, device=DEV)
+    one = sv.VerifyCall("greedy", zt, None, toks, one_launch=True)
+    for r in range(4):
+        z, t = W.workload3(r, device=DEV)
+        zt.copy_(z)
+        toks.copy_(t)
+        out = one.run()
+        torch.cuda.synchronize()
+        o = oracle.verify_greedy(W.host_logits(z), draft_tokens=t.cpu().numpy(), nthreads=8)
+        compare_exact(out, o, GREEDY_KEYS)
+        assert int(one.state.count_nonzero()) == 0
+    one_launch_matches(zt, toks)
+
+
+def test_one_launch_greedy_edge_rows():
+    """Ties (lowest index), +0 and -0 as one value, NaN, +inf, vectors of
+    -inf or of NaN only, k_b outside [1, k], tokens out of range, draft
+    logits instead of tokens, and a layout that takes the two launches."""
+    B, K, V = 40, 5, 24576
+    g = torch.Generator().manual_seed(3)
+    z = (torch.randn((B, K + 1, V), generator=g) * 2).round() / 2
+    z[:, :, 9000] = 9.0
+    z[:, :, 4100] = 9.0          # tie across chunks: 4100 wins
+    z[1, 2, :] = 0.0
+    z[1, 2, 5] = -0.0            # the zeros tie: index 0
+    z[2, 0, 8191] = float("nan")
+    z[3, 1, 12288] = float("inf")
+    z[4, 2, :] = float("-inf")
+    z[5, 3, :] = float("nan")
+    z[6, 0, :] = -1.0
+    z[6, 0, 20000] = -0.5
+    z[6, 0, 7] = -0.5            # a negative tie: 7
+    zb = z.to(torch.bfloat16).to(DEV)
+    toks = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    toks[:, 0] = 4100
+    toks[7, 1] = V
+    kk = torch.randint(1, K + 1, (B,), generator=g, dtype=torch.int32)
+    kk[8], kk[9] = 0, K + 1
+    kk[1:7] = K
+    one_launch_matches(zb, toks.to(DEV), k_per_row=kk.to(DEV))
+    one_launch_matches(zb, toks.to(DEV))
+    zd = (zb[:, :K].float() + 0.25 * torch.randn((B, K, V), device=DEV)).to(torch.bfloat16)
+    one_launch_matches(zb, draft=zd, k_per_row=kk.to(DEV))
+    # unaligned vectors (V not a multiple of 8): the two launches, state untouched
+    one_launch_matches(zb[:, :, :V - 3], toks.to(DEV))
+
+
+def test_one_launch_greedy_in_a_replayed_graph():
+    """The one-launch call captured once and replayed: every replay gives
+    the eager result and leaves the state zero."""
+    zt, toks = W.workload3(5, device=DEV, B=16)
+    one = sv.VerifyCall("greedy", zt, None, toks, one_launch=True)
+    ref = {k: v.clone() for k, v in sv.VerifyCall("greedy", zt, None, toks).run().items()}
+    one.run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one.run()
+    for r in range(4):
+        for k in GREEDY_KEYS:
+            one.outputs[k].fill_(-9)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in GREEDY_KEYS:
+            assert torch.equal(one.outputs[k], ref[k]), (r, k)
+        assert int(one.state.count_nonzero()) == 0
+
+
 # ------------------------------------------------------------------ rollback
 
 def rollback_pair(oracle, lens, acc, kk, K, ps, MP, spare=8, capacity=None, pool_dims=None,
