@@ -159,6 +159,20 @@ def test_one_launch_greedy_edge_rows():
     one_launch_matches(zb[:, :, :V - 3], toks.to(DEV))
 
 
+@pytest.mark.parametrize("B,K,V", [(512, 8, 8192), (3, 1, 4096 * 40), (1000, 2, 4096),
+                                   (7, 32, 12296)])
+def test_one_launch_greedy_shapes(B, K, V):
+    """Many rows with few chunks each (the row counters see many rows'
+    chunks at once), few rows with many chunks (one counter sees them all),
+    k at its limit, and a last chunk shorter than the others."""
+    g = torch.Generator(device=DEV).manual_seed(B + K)
+    zt = (torch.randn((B, K + 1, V), generator=g, device=DEV) * 2).to(torch.bfloat16)
+    top = zt[:, :K].float().argmax(dim=2).to(torch.int32)
+    toks = torch.where(torch.rand((B, K), generator=g, device=DEV) < 0.8, top,
+                       torch.randint(0, V, (B, K), generator=g, device=DEV, dtype=torch.int32))
+    one_launch_matches(zt, toks, calls=2)
+
+
 def test_one_launch_greedy_in_a_replayed_graph():
     """The one-launch call captured once and replayed: every replay gives
     the eager result and leaves the state zero."""
