@@ -988,6 +988,9 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     for (int j = 0; j < kGpt; ++j) {
       const int g = tid + kT * j;
       const uint4 d0 = hist4[g], d1 = copy1[g];
+      // most groups are empty and come in runs: a wave whose groups are
+      // all empty has nothing to merge, count or clear
+      if (!__any((d0.x | d0.y | d0.z | d0.w | d1.x | d1.y | d1.z | d1.w) != 0u)) continue;
       const uint32_t a0[4] = {d0.x, d0.y, d0.z, d0.w};
       const uint32_t a1[4] = {d1.x, d1.y, d1.z, d1.w};
       uint32_t xs[4];
@@ -1183,13 +1186,12 @@ __global__ __launch_bounds__(kT, kWgPerCu) void shard_combine_kernel(CombinePara
       }
     }
   }
-  uint32_t st = 0, Z = 0, NI = 0, NT = 0;
+  uint32_t st = 0, Z = 0, NT = 0;
   int MP = -1, MN = 0x7FFFFFFF;
   for (int g = 0; g < G; ++g) {
     const ShardHead& hg = heads[g];
     st |= hg.status;
     Z += hg.zeros;
-    NI += hg.ninf;
     NT += hg.ntiny;
     MP = max(MP, hg.maxpos);
     MN = min(MN, hg.minneg);
