@@ -37,6 +37,7 @@ constexpr int kPerThread = kGreedyChunk / kThreads;  // 16 logits
 constexpr int kLoads = kPerThread / 8;               // 16-byte loads per thread
 constexpr int kLaneLoads = kGreedyChunk / 8 / 64;    // 8: a wave's loads per lane and chunk
 constexpr int kStreamWgPerCu = 4;                    // workgroups of the streaming grid per CU
+constexpr int kFusedWgPerCu = 5;                     // workgroups of the one-launch grid per CU
 
 // (v, i) beats (bv, bi): larger value, or equal value with a lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -571,7 +572,7 @@ __device__ __forceinline__ void fused_decide_row(const GreedyParams& p, int b,
 // the decision of each row done by the row's last chunk.  Every item counts
 // for its row, used or not (a row with an invalid k_b uses none), so every
 // row is decided once.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, kStreamWgPerCu)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, kFusedWgPerCu)))
 void argmax_fused_kernel(GreedyParams p, int nitems, int nvec) {
   const int l = threadIdx.x & 63;
   const int waves = gridDim.x * (kThreads / 64);
@@ -627,15 +628,15 @@ hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Time
                       (!p.draft || (((uintptr_t)p.draft & 15u) == 0 && (p.d_stride & 7) == 0));
   if (stream) {
     const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
-    const unsigned want = cus * (unsigned)kStreamWgPerCu;
-    const unsigned waves_needed = nitems;
-    const unsigned grid = min(want, (waves_needed + kThreads / 64 - 1) / (kThreads / 64));
+    const unsigned wgs_needed = (nitems + kThreads / 64 - 1) / (kThreads / 64);
     if (p.state) {
+      const unsigned grid = min(cus * (unsigned)kFusedWgPerCu, wgs_needed);
       TimedScope ts(t, "greedy_fused", s);
       hipLaunchKernelGGL(argmax_fused_kernel, dim3(grid), dim3(kThreads), 0, s, p, (int)nitems,
                          nvec);
       return hipGetLastError();
     }
+    const unsigned grid = min(cus * (unsigned)kStreamWgPerCu, wgs_needed);
     TimedScope ts(t, "greedy_argmax", s);
     hipLaunchKernelGGL(argmax_stream_kernel, dim3(grid), dim3(kThreads), 0, s, p, (int)nitems);
   } else {
