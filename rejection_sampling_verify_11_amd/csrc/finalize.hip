@@ -1066,7 +1066,12 @@ hipError_t launch_draft_sample(const FinalizeParams& p, int num_cus, hipStream_t
   if (p.B == 0) return hipSuccess;
   TimedScope ts(t, "draft_sample", s);
   const unsigned n = (unsigned)p.B * (unsigned)p.K;
-  if (use_half_blocks(n, num_cus))
+  // with many vectors, smaller workgroups: more of them share a CU, so one's
+  // header and locate overlap the others' streaming
+  const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
+  if (n >= 4u * cus)
+    hipLaunchKernelGGL(draft_sample_kernel<256>, dim3(n), dim3(256), 0, s, p);
+  else if (use_half_blocks(n, num_cus))
     hipLaunchKernelGGL(draft_sample_kernel<512>, dim3(n), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL(draft_sample_kernel<1024>, dim3(n), dim3(1024), 0, s, p);

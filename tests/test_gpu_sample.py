@@ -489,7 +489,8 @@ def test_rows_alike_under_both_workgroup_sizes(dtype):
     per CU), their first 48 alone with 1024-thread ones.  The inverse CDF's
     segments do not depend on the workgroup size, nor do the statistics
     records on the schedule, so those 48 rows' outputs are bit-identical.
-    Likewise the draft sampler, 600 x 4 draws against 48 x 4."""
+    Likewise the draft sampler, 600 x 4 draws (256-thread workgroups)
+    against 48 x 4 (1024-thread ones)."""
     big = W.workload4(3, device=DEV, B=600, k=4, V=24000)
     t, d = big.target.to(dtype), big.draft.to(dtype)
     T, P = big.temperature, big.top_p
@@ -599,9 +600,11 @@ def test_random_configuration_sweep(oracle, case):
     rep.bound(max_excused=1)
 
 
-# token positions around the segment (2048) and group (16384 / 32768) edges
-# of the p'-only draws, the two ends and the middle
-HOT = [0, 1, 7, 8, 2047, 2048, 16383, 16384, 32767, 32768, 75967, 151928, 151935]
+# token positions around the segment (2048) and group (8192 / 16384 / 32768
+# for 256-, 512- and 1024-thread workgroups) edges of the p'-only draws, the
+# two ends and the middle
+HOT = [0, 1, 7, 8, 2047, 2048, 8191, 8192, 16383, 16384, 24575, 24576, 32767, 32768, 75967,
+       151928, 151935]
 
 
 def _hot_logits(n, V, positions, cold=-200.0, hot=20.0):
@@ -610,13 +613,14 @@ def _hot_logits(n, V, positions, cold=-200.0, hot=20.0):
     return z
 
 
-@pytest.mark.parametrize("B", [8, 256])
+@pytest.mark.parametrize("B", [8, 256, 512])
 def test_pprime_draws_find_a_single_hot_token(oracle, B):
     """Draws from p' alone (the draft sampler and the bonus position) on
     vectors whose mass sits on one token: the draw is that token whatever u
     is, wherever the token lies relative to the early stop's segments and
-    groups.  B=8 runs 1024-thread workgroups, B=256 512-thread ones.  The
-    oracle agrees on every row."""
+    groups.  B=8 runs 1024-thread workgroups, B=256 512-thread ones; at
+    B=512 the draft sampler's 1024 draws take 256-thread workgroups and the
+    bonus 512-thread ones.  The oracle agrees on every row it checks."""
     K, V = 2, 151936
     n = B * K
     pos = [HOT[i % len(HOT)] for i in range(n)]
