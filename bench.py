@@ -176,7 +176,57 @@ def greedy_leg(dev, n):
             "two_launch_ms_per_call": ms_two,
             "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "verified_positions_per_s": B * K / (ms * 1e-3),
-            "mean_accepted": call.outputs["accepted"].float().mean().item()}
+            "mean_accepted": call.outputs["accepted"].float().mean().item(),
+            "rollback_pool": greedy_rollback(dev, call.outputs["accepted"], B, K, n)}
+
+
+def greedy_rollback(dev, accepted, B, K, n):
+    """The greedy configuration's rollback on the greedy call's accepted
+    counts: a paged cache of 32 layers x 8 KV heads x 128 dims bf16 (page
+    size 16, 2 MiB per page), contexts U[512, 4096] after the k+1 writes, a
+    free stack, and the rolled-back slots poisoned.  Every timed call starts
+    from the same state, restored outside its events; one call per pair of
+    events, so the figure is a call's latency."""
+    import torch
+    import rejection_sampling_verify_11_amd as sv
+    from rejection_sampling_verify_11_amd import workloads as W
+    ps, L, H, D = 16, 32, 8, 128
+    len0 = W.workload5_rows(3, B=B).kv_len0 + (K + 1)
+    kv = W.paged_kv(len0, ps, int((len0.max() + ps - 1) // ps), spare_pages=2 * B, seed=3)
+    pool = torch.zeros((kv.num_pages, L, 2, H, ps, D), dtype=torch.bfloat16, device=dev)
+    state0 = [len0.to(dev), kv.page_table.to(dev), kv.free_pages.to(dev), kv.free_top.to(dev)]
+    state = [t.clone() for t in state0]
+    rb = sv.RollbackCall(state[0], accepted, state[1], ps, K, free_pages=state[2],
+                         free_top=state[3], kv_pool=pool, num_pages=kv.num_pages, num_layers=L,
+                         kv_heads=H, head_dim=D)
+
+    def calls(m, keep):
+        out = []
+        for _ in range(m):
+            for t, t0 in zip(state, state0):
+                t.copy_(t0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rb.run()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3)
+        return out if keep else None
+
+    calls(10, False)
+    us = sorted(calls(max(n, 20), True))
+    sv.timing_enable(dev, True)
+    calls(20, False)
+    kt = sv.timing_read(dev)
+    sv.timing_enable(dev, False)
+    assert int((rb.row_status != 0).sum()) == 0
+    slots = int((len0.to(dev) - state[0]).sum())
+    return {"workload": "32 layers x 8 KV heads x 128 dims bf16, page size 16, contexts "
+                        "U[512, 4096], free stack, poisoning",
+            "us_per_call": us[len(us) // 2], "poisoned_slots": slots,
+            "poisoned_bytes": slots * L * 2 * H * D * 2,
+            "kernels_us": {name: v[1] / v[0] * 1e3 for name, v in kt.items()}}
 
 
 def variant_legs(dev, sets, n):

@@ -258,9 +258,10 @@ typedef struct {
                                are overwritten with SV_POISON_BF16           */
   int32_t num_layers, kv_heads, head_dim;
   int32_t* row_status;      /* [B] or NULL                                   */
-  void* workspace;          /* per-row decisions: at least
+  void* workspace;          /* per-row decisions and counters: at least
                                sv_rollback_workspace_bytes(B) bytes (also
-                               when the call is fused into verification)    */
+                               when the call is fused into verification);
+                               its contents need no initialisation          */
   size_t workspace_bytes;
 } sv_rollback_args;
 

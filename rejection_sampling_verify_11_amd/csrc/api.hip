@@ -408,9 +408,16 @@ sv_status sv_verify_greedy_one_launch(sv_handle h, const sv_verify_args* a, void
   return greedy_launch(h, a, state, s);
 }
 
+// the rows' decisions, then the per-row counters of the commit by the
+// poisoning
+static size_t rollback_recs_bytes(int32_t B) {
+  return align_up((size_t)B * sizeof(sv::RollRec), 256);
+}
+
 size_t sv_rollback_workspace_bytes(int32_t B) {
   if (B < 0) return 0;
-  const size_t n = align_up((size_t)B * sizeof(sv::RollRec), 256);
+  const size_t n = rollback_recs_bytes(B) +
+                   align_up((size_t)B * sv::kRollCntStride * sizeof(uint32_t), 256);
   return n > 0 ? n : 256;
 }
 
@@ -450,6 +457,7 @@ static sv::RollbackParams rollback_params(const sv_rollback_args* a) {
   p.D = a->head_dim;
   p.row_status = a->row_status;
   p.recs = (sv::RollRec*)a->workspace;
+  p.row_cnt = (uint32_t*)((char*)a->workspace + rollback_recs_bytes(a->B));
   return p;
 }
 

@@ -17,8 +17,9 @@
 // releases (valid rows only) gives every row its slots on the free stack in
 // (row, page) order, and a row whose releases would pass the stack capacity
 // is flagged and left unchanged.  With a KV pool the scan writes its
-// decisions to the workspace first, a second kernel poisons the rolled-back
-// slots while the page table still maps them, and a third commits.
+// decisions to the workspace first, then a kernel poisons the rolled-back
+// slots while the page table still maps them, and the last of each row's
+// poisoning workgroups commits the row.
 #include "sv_internal.h"
 
 namespace sv {
@@ -65,8 +66,10 @@ __global__ __launch_bounds__(64 * kCheckRows) void rollback_check_kernel(Rollbac
   }
 }
 
-// phase 0: scan and commit; phase 1: scan into p.recs only (aux becomes the
-// row's first slot on the free stack, status the final status).
+// phase 0: scan and commit; phase 1 (before the poisoning, which commits):
+// scan into p.recs (aux becomes the row's first slot on the free stack,
+// status the final status) and zero the rows' commit counters.  Both move
+// the stack's top.
 __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, int phase) {
   __shared__ int wsum[kWaves];
   __shared__ int wmax[kWaves];
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, in
         r.aux = push_base;
         p.recs[b] = r;
         if (p.row_status) p.row_status[b] = (int32_t)st;
+        p.row_cnt[(size_t)b * kRollCntStride] = 0u;
       }
     } else {
       if (commit) {
@@ -133,62 +137,80 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackParams p, in
     __syncthreads();
     carry += tot;
   }
-  if (phase == 0 && tid == 0 && p.free_pages) p.free_top[0] = top0 + pushed;
-}
-
-// Commit from recorded decisions (after poisoning).
-__global__ __launch_bounds__(kThreads) void rollback_commit_kernel(RollbackParams p) {
-  __shared__ int wmax[kWaves];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int top0 = p.free_pages ? p.free_top[0] : 0;
-  int pushed = 0;
-  for (int t0 = 0; t0 < p.B; t0 += kThreads) {
-    const int b = t0 + tid;
-    int my_pushed = 0;
-    if (b < p.B) {
-      const RollRec r = p.recs[b];
-      if (r.status == 0) {
-        int32_t* row = p.page_table + (int64_t)b * p.MP;
-        if (p.free_pages) {
-          const int first = ceil_div(r.new_len, p.ps);
-          const int rel = ceil_div(r.old_len, p.ps) - first;
-          for (int j = 0; j < rel; ++j) {
-            p.free_pages[r.aux + j] = row[first + j];
-            row[first + j] = -1;
-          }
-          if (rel > 0) my_pushed = r.aux + rel - top0;
-        }
-        p.kv_len[b] = r.new_len;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) my_pushed = max(my_pushed, __shfl_xor(my_pushed, o, 64));
-    if (l == 0) wmax[w] = my_pushed;
-    __syncthreads();
-    for (int k = 0; k < kWaves; ++k) pushed = max(pushed, wmax[k]);
-    __syncthreads();
-  }
   if (tid == 0 && p.free_pages) p.free_top[0] = top0 + pushed;
 }
 
 // One workgroup per (row, layer): overwrite the rolled-back slots with the
-// poison pattern.  Pool layout [page][layer][K|V][head][slot][dim].
+// poison pattern.  Pool layout [page][layer][K|V][head][slot][dim]: for one
+// (page, layer, K|V, head) the page's slots are rows of D contiguous values,
+// so consecutive slots of a row that share a page are contiguous too.  With
+// D a multiple of 8 and the pool on a 16-byte boundary a thread writes 8
+// values at once, consecutive threads along a slot row, then along the
+// slots of one (K|V, head); otherwise one value at a time.  The rolled-back
+// slots (at most k_max of them) lie on a few pages, whose numbers are read
+// once into LDS.
+//
+// The rows are committed here too: each workgroup counts
+// itself done for its row with a device-scope atomic once its page numbers
+// are read, and the row's last one releases the row's pages onto the free
+// stack (at the place the scan gave it) and sets the new length.  Only the
+// row's own workgroups read its page-table row, so nothing reads an entry
+// after the commit unmaps it.
+constexpr int kPoisonPages = 64;
+static_assert(kPoisonPages >= SV_MAX_K + 2, "rolled-back slots span at most k_max + 1 pages");
+
 __global__ __launch_bounds__(256) void poison_kernel(RollbackParams p) {
-  const int b = blockIdx.x / p.L, layer = blockIdx.x % p.L;
+  __shared__ int32_t pages[kPoisonPages];
+  __shared__ int last;
+  const int b = blockIdx.x / p.L, layer = blockIdx.x % p.L, tid = threadIdx.x;
   const RollRec r = p.recs[b];
   if (r.status != 0) return;
   const int nslots = r.old_len - r.new_len;
-  const int per_slot = 2 * p.H * p.D;
-  const int32_t* row = p.page_table + (int64_t)b * p.MP;
-  for (int e = threadIdx.x; e < nslots * per_slot; e += blockDim.x) {
-    const int s = e / per_slot, rem = e % per_slot;
-    const int kvh = rem / p.D, dim = rem % p.D;  // kvh = kv * H + head
-    const int pos = r.new_len + s;
-    const int page = row[pos / p.ps];
-    const int64_t off =
-        ((((int64_t)page * p.L + layer) * 2 * p.H + kvh) * p.ps + pos % p.ps) * p.D + dim;
-    p.kv_pool[off] = (uint16_t)SV_POISON_BF16;
+  if (nslots <= 0) return;  // nothing rolled back: nothing to release either
+  int32_t* row = p.page_table + (int64_t)b * p.MP;
+  const int lp0 = r.new_len / p.ps, npg = (r.old_len - 1) / p.ps - lp0 + 1;
+  for (int j = tid; j < npg; j += blockDim.x) pages[j] = row[lp0 + j];
+  __syncthreads();
+  if ((p.D & 7) == 0 && ((uintptr_t)p.kv_pool & 15u) == 0) {
+    const int dq = p.D >> 3;               // 16-byte pieces per slot row
+    const int per_kvh = nslots * dq;       // pieces of one (K|V, head)
+    const int n = 2 * p.H * per_kvh;
+    const uint32_t w = (uint32_t)SV_POISON_BF16 * 0x10001u;
+    for (int e = tid; e < n; e += blockDim.x) {
+      const int kvh = e / per_kvh, rem = e - kvh * per_kvh;
+      const int s = rem / dq, c = rem - s * dq;
+      const int pos = r.new_len + s;
+      const int page = pages[pos / p.ps - lp0];
+      const int64_t off =
+          ((((int64_t)page * p.L + layer) * 2 * p.H + kvh) * p.ps + pos % p.ps) * p.D + 8 * c;
+      *reinterpret_cast<uint4*>(p.kv_pool + off) = make_uint4(w, w, w, w);
+    }
+  } else {
+    const int per_slot = 2 * p.H * p.D;
+    for (int e = tid; e < nslots * per_slot; e += blockDim.x) {
+      const int s = e / per_slot, rem = e % per_slot;
+      const int kvh = rem / p.D, dim = rem % p.D;  // kvh = kv * H + head
+      const int pos = r.new_len + s;
+      const int page = pages[pos / p.ps - lp0];
+      const int64_t off =
+          ((((int64_t)page * p.L + layer) * 2 * p.H + kvh) * p.ps + pos % p.ps) * p.D + dim;
+      p.kv_pool[off] = (uint16_t)SV_POISON_BF16;
+    }
   }
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&p.row_cnt[(size_t)b * kRollCntStride], 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.L - 1);
+  __syncthreads();
+  if (!last) return;
+  if (p.free_pages) {
+    const int first = ceil_div(r.new_len, p.ps);
+    const int rel = ceil_div(r.old_len, p.ps) - first;
+    for (int j = tid; j < rel; j += blockDim.x) {
+      p.free_pages[r.aux + j] = row[first + j];
+      row[first + j] = -1;
+    }
+  }
+  if (tid == 0) p.kv_len[b] = r.new_len;
 }
 
 }  // namespace
@@ -213,22 +235,17 @@ hipError_t launch_rollback_decided(const RollbackParams& p, hipStream_t s, Timer
     hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 0);
     return hipGetLastError();
   }
+  // decide, then poison; the poisoning commits the rows (the argument
+  // checks give a pool at least one layer, head and dim)
+  if (!p.row_cnt || p.L < 1 || p.H < 1 || p.D < 1) return hipErrorInvalidValue;
   {
     TimedScope ts(t, "rollback_decide", s);
     hipLaunchKernelGGL(rollback_kernel, dim3(1), dim3(kThreads), 0, s, p, 1);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.L > 0 && p.H > 0 && p.D > 0) {
-    TimedScope ts(t, "rollback_poison", s);
-    hipLaunchKernelGGL(poison_kernel, dim3((unsigned)p.B * (unsigned)p.L), dim3(256), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    TimedScope ts(t, "rollback_commit", s);
-    hipLaunchKernelGGL(rollback_commit_kernel, dim3(1), dim3(kThreads), 0, s, p);
-  }
+  TimedScope ts(t, "rollback_poison", s);
+  hipLaunchKernelGGL(poison_kernel, dim3((unsigned)p.B * (unsigned)p.L), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

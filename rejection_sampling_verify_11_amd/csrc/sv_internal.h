@@ -209,7 +209,11 @@ struct RollbackParams {
   int32_t L, H, D;
   int32_t* row_status;
   RollRec* recs;
+  // per-row counters (kRollCntStride words apart) through which the last of
+  // a row's poisoning workgroups commits the row
+  uint32_t* row_cnt;
 };
+constexpr int kRollCntStride = 16;
 
 // One shard's part of the draw: its columns of every vector, and the
 // exchange buffer of all shards' per-row masses.

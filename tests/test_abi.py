@@ -193,7 +193,9 @@ def test_verify_rollback_validation():
         r.B, r.k_max, r.page_size, r.max_pages_per_seq = 4, 3, 16, 10
         r.kv_len = r.page_table = 0x20000
         r.accepted = v.accepted
-        r.workspace, r.workspace_bytes = 0x40000, L.sv_rollback_workspace_bytes(4)
+        # room for more rows than the call has, so that only the mismatch
+        # itself is wrong below
+        r.workspace, r.workspace_bytes = 0x40000, L.sv_rollback_workspace_bytes(8)
         return r
 
     chk = lambda r: L.sv_check_verify_rollback_args(C.byref(v), C.byref(r))

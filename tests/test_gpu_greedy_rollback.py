@@ -271,6 +271,31 @@ def test_rollback_small_pool_poison_exact(oracle):
     rollback_pair(oracle, lens, acc, kk, K, ps, 12, spare=6, pool_dims=(3, 2, 8), seed=4)
 
 
+@pytest.mark.parametrize("D", [8, 6])
+def test_rollback_pool_bad_rows_overflow_and_many_rows(oracle, D):
+    """Poisoning with the commit done by each row's last poisoning
+    workgroup: 1100 rows (two tiles of the scan), rows with a bad accepted
+    count or k, rows that roll nothing back, a free stack that overflows,
+    and a pool without a free stack.  D = 8 takes the 16-byte stores, D = 6
+    the one-value path."""
+    rng = np.random.default_rng(7 + D)
+    B, K, ps = 1100, 4, 4
+    lens = rng.integers(5, 60, B)
+    kk = rng.integers(1, K + 1, B)
+    acc = np.array([rng.integers(0, k + 1) for k in kk])
+    acc[::9] = kk[::9]  # nothing rolled back
+    acc[3], acc[4], kk[5] = -1, kk[4] + 1, 0
+    MP = 16
+    st, _ = rollback_pair(oracle, lens, acc, kk, K, ps, MP, spare=40, pool_dims=(2, 3, D),
+                          seed=8)
+    assert (st == 0).sum() > B // 2
+    st, _ = rollback_pair(oracle, lens, acc, kk, K, ps, MP, spare=0, capacity=30,
+                          pool_dims=(2, 3, D), seed=9)
+    assert (st & sv.ROW_FREE_OVERFLOW).any()
+    rollback_pair(oracle, lens, acc, kk, K, ps, MP, keep_pages=True, pool_dims=(1, 2, D),
+                  seed=10)
+
+
 def test_rollback_keep_pages_overflow_and_bad_rows(oracle):
     rng = np.random.default_rng(5)
     B, K, ps = 300, 4, 8
