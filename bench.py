@@ -112,35 +112,61 @@ def timed(fn, n, dev):
     return e0.elapsed_time(e1) / n
 
 
+COLD_BYTES = 512 << 20  # input rotated over at least this much: none of it in the 256 MB MALL
+
+
+def rotating(calls):
+    """A function that runs the calls in turn, one per invocation."""
+    i = [0]
+
+    def run():
+        calls[i[0] % len(calls)].run()
+        i[0] += 1
+    return run
+
+
 def small_legs(dev, n):
     """The two small configurations, which are latency-bound: B=1, k=4,
     V=32000 fp32 (T=1, no top-p) and B=32, k=5, V=32000 bf16 (T=0.8), with
     draft tokens from the draft sampler.  Microseconds per sv_verify_sample
-    call (HIP events around n back-to-back calls) and verified positions/s;
-    per-kernel times from a second pass."""
+    call (HIP events around n back-to-back calls) and verified positions/s,
+    the calls rotating over input sets of at least 512 MB in all so that no
+    call finds its logits in the last-level cache; then the same with one
+    input set (warm cache, labelled so).  Per-kernel times from a second,
+    rotating pass."""
     import torch
     import rejection_sampling_verify_11_amd as sv
     from rejection_sampling_verify_11_amd import workloads as W
     out = {}
-    for name, inp in (("fp32_b1_k4_v32000", W.workload1(0, device=dev)),
-                      ("bf16_b32_k5_v32000", W.workload2(0, device=dev))):
-        B, K, V = inp.draft.shape
-        toks, st = sv.draft_sample(inp.draft, inp.temperature, inp.top_p, seed=0, offset=0)
-        call = sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature, inp.top_p,
-                             None, seed=0, offset=0)
+    for name, gen in (("fp32_b1_k4_v32000", W.workload1), ("bf16_b32_k5_v32000", W.workload2)):
+        calls, nbytes, nsets = [], 0, 1
+        while len(calls) < nsets:
+            inp = gen(len(calls), device=dev)
+            B, K, V = inp.draft.shape
+            nbytes = B * (2 * K + 1) * V * inp.target.element_size()
+            nsets = -(-COLD_BYTES // nbytes)
+            toks, st = sv.draft_sample(inp.draft, inp.temperature, inp.top_p, seed=0,
+                                       offset=len(calls))
+            assert not st.any()
+            calls.append(sv.VerifyCall("sample", inp.target, inp.draft, toks, inp.temperature,
+                                       inp.top_p, None, seed=0, offset=len(calls)))
+        cold = rotating(calls)
+        for _ in range(2 * len(calls)):
+            cold()
+        us = timed(cold, max(n, len(calls)), dev) * 1e3
         for _ in range(50):
-            call.run()
-        us = timed(call.run, n, dev) * 1e3
+            calls[0].run()
+        us_warm = timed(calls[0].run, n, dev) * 1e3
         sv.timing_enable(dev, True)
-        for _ in range(50):
-            call.run()
+        for _ in range(len(calls)):
+            cold()
         torch.cuda.synchronize()
         kt = sv.timing_read(dev)
         sv.timing_enable(dev, False)
-        assert not st.any() and not call.outputs["row_status"].any()
-        nbytes = B * (2 * K + 1) * V * inp.target.element_size()
+        assert all(not c.outputs["row_status"].any() for c in calls)
         out[name] = {"us_per_call": us, "verified_positions_per_s": B * K / (us * 1e-6),
-                     "input_gbs": nbytes / (us * 1e-6) / 1e9,
+                     "input_gbs": nbytes / (us * 1e-6) / 1e9, "input_sets": len(calls),
+                     "warm_cache_us_per_call": us_warm,
                      "kernels_us": {k: 1e3 * v[1] / v[0] for k, v in kt.items()}}
     return out
 
@@ -151,33 +177,45 @@ def greedy_leg(dev, n):
     import rejection_sampling_verify_11_amd as sv
     from rejection_sampling_verify_11_amd import workloads as W
     B, K, V = 64, 8, 128256
-    zt, toks = W.workload3(0, device=dev, B=B, k=K, V=V)
-    # one launch (sv_verify_greedy_one_launch, a zeroed state kept by the
-    # call), and the two launches of sv_verify_greedy for comparison
-    call = sv.VerifyCall("greedy", zt, None, toks, one_launch=True)
-    two = sv.VerifyCall("greedy", zt, None, toks)
+    target_bytes = B * (K + 1) * V * 2
+    # input sets rotated so that no call finds its 148 MB in the 256 MB
+    # last-level cache; one launch (sv_verify_greedy_one_launch, a zeroed
+    # state kept by each call) and, on the same inputs, the two launches of
+    # sv_verify_greedy
+    ones, twos = [], []
+    for r in range(-(-COLD_BYTES // target_bytes)):
+        zt, toks = W.workload3(r, device=dev, B=B, k=K, V=V)
+        ones.append(sv.VerifyCall("greedy", zt, None, toks, one_launch=True))
+        twos.append(sv.VerifyCall("greedy", zt, None, toks))
+    one, two = rotating(ones), rotating(twos)
+    for _ in range(5 * len(ones)):
+        one()
+        two()
+    ms = timed(one, n, dev)
+    ms_two = timed(two, n, dev)
     for _ in range(20):
-        call.run()
-        two.run()
-    ms = timed(call.run, n, dev)
-    ms_two = timed(two.run, n, dev)
+        ones[0].run()
+    ms_warm = timed(ones[0].run, n, dev)
     sv.timing_enable(dev, True)
-    for _ in range(20):
-        call.run()
-        two.run()
+    for _ in range(5 * len(ones)):
+        one()
+        two()
     torch.cuda.synchronize()
     kt = sv.timing_read(dev)
     sv.timing_enable(dev, False)
-    assert int((call.outputs["row_status"] != 0).sum()) == 0
-    assert all(torch.equal(call.outputs[k], two.outputs[k]) for k in call.outputs)
-    target_bytes = B * (K + 1) * V * 2
+    for c1, c2 in zip(ones, twos):
+        assert int((c1.outputs["row_status"] != 0).sum()) == 0
+        assert all(torch.equal(c1.outputs[k], c2.outputs[k]) for k in c1.outputs)
+    acc = torch.cat([c.outputs["accepted"] for c in ones]).float().mean().item()
     return {"workload": "B=64 k=8 V=128256 bf16 greedy, draft = target argmax w.p. 0.85",
             "ms_per_call": ms, "target_gbs": target_bytes / (ms * 1e-3) / 1e9,
-            "two_launch_ms_per_call": ms_two,
+            "input_sets": len(ones), "two_launch_ms_per_call": ms_two,
+            "warm_cache_ms_per_call": ms_warm,
+            "warm_cache_target_gbs": target_bytes / (ms_warm * 1e-3) / 1e9,
             "kernels_ms": {name: v[1] / v[0] for name, v in kt.items()},
             "verified_positions_per_s": B * K / (ms * 1e-3),
-            "mean_accepted": call.outputs["accepted"].float().mean().item(),
-            "rollback_pool": greedy_rollback(dev, call.outputs["accepted"], B, K, n)}
+            "mean_accepted": acc,
+            "rollback_pool": greedy_rollback(dev, ones[0].outputs["accepted"], B, K, n)}
 
 
 def greedy_rollback(dev, accepted, B, K, n):
