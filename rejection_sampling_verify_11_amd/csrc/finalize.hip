@@ -39,10 +39,11 @@
 namespace sv {
 namespace {
 
-// Workgroups have NT = 1024 or 512 threads (a template parameter): 1024 when
-// the launch has about one workgroup per CU, 512 when it has two or more
-// per CU, so that two fit a CU (registers and LDS) and one's serial steps
-// (row header, scan, located segment) overlap the other's streaming.
+// Workgroups have NT = 1024, 512 or 256 threads (a template parameter): 1024
+// when the launch has about one workgroup per CU, 512 when it has two or
+// more per CU, so that two fit a CU (registers and LDS) and one's serial
+// steps (row header, scan, located segment) overlap the other's streaming;
+// the draft sampler takes 256 from four per CU on.
 constexpr int kSeg = 512;             // logits per (tile, wave) segment
 constexpr int kMaxSeg = 4096;         // V <= 2^21 on this path
 

@@ -267,8 +267,9 @@ hipError_t launch_shard_draw(const FinalizeParams& p, const ShardDrawParams& d, 
                              int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_greedy(const GreedyParams& p, int num_cus, hipStream_t s, Timer* t);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t s, Timer* t);
-// The rollback's scan and commit kernels on decisions already in p.recs
-// (written by the verification's finalize kernel).
+// The rollback's scan and commit (with a KV pool: the scan, then the
+// poisoning, which commits) on decisions already in p.recs (written by the
+// verification's finalize kernel).
 hipError_t launch_rollback_decided(const RollbackParams& p, hipStream_t s, Timer* t);
 hipError_t launch_dynk(const DynkParams& p, hipStream_t s, Timer* t);
 hipError_t launch_advance_offset(uint64_t* offset_dev, uint64_t delta, hipStream_t s, Timer* t);
