@@ -188,6 +188,44 @@ struct StreamedLogits {
   }
 };
 
+// fp32 logits of a vector on a 16-byte boundary, streamed on every pass in
+// 16-byte loads, kU of them in flight per thread: thread tid takes the
+// groups of four logits tid, tid + NT, ..., then the tail logits past the
+// last whole group, in that order.
+template <int NT>
+struct StreamedF32 {
+  const float* vec;
+  int V;
+  static constexpr int kU = 4;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int tid = threadIdx.x;
+    const int n4 = V >> 2;
+    const float4* v4 = reinterpret_cast<const float4*>(vec);
+    int g = tid;
+    for (; g + (kU - 1) * NT < n4; g += kU * NT) {
+      float4 a[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) a[u] = v4[g + u * NT];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        f(a[u].x);
+        f(a[u].y);
+        f(a[u].z);
+        f(a[u].w);
+      }
+    }
+    for (; g < n4; g += NT) {
+      const float4 a = v4[g];
+      f(a.x);
+      f(a.y);
+      f(a.z);
+      f(a.w);
+    }
+    for (int j = 4 * n4 + tid; j < V; j += NT) f(vec[j]);
+  }
+};
+
 // The same logits held in registers (V <= NT * R): read once, all loads in
 // flight together, so a short vector costs one memory round trip instead of
 // one per pass and per element.  The passes see the values in the same
@@ -335,6 +373,11 @@ __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams 
                                                       : __uint_as_float(0x7FC00000u);
     generic_stats<kGenThreads>(held, s.token, zx, s.T, s.P, p.V, hist256, sc,
                                p.recs + blockIdx.x);
+  } else if (dtype == SV_FP32 && ((uintptr_t)s.vec & 15u) == 0) {
+    const float* vec = (const float*)s.vec;
+    const float zx = (s.token >= 0 && s.token < p.V) ? vec[s.token] : __uint_as_float(0x7FC00000u);
+    generic_stats<kGenThreads>(StreamedF32<kGenThreads>{vec, p.V}, s.token, zx, s.T, s.P, p.V,
+                               hist256, sc, p.recs + blockIdx.x);
   } else {
     generic_stats<kGenThreads>(logit, s.token, s.T, s.P, p.V, hist256, sc, p.recs + blockIdx.x);
   }

@@ -160,6 +160,12 @@ def test_workload5_full_batch_sampled_rows(oracle):
     (8191, torch.float32, 0.9, 1),
     (20000, torch.float32, 0.95, 0),
     (50001, torch.bfloat16, None, 5),
+    # fp32 past the held path: 16-byte streamed passes (rows on 16-byte
+    # boundaries, tails of 0 and 3 logits) and 4-byte ones (odd strides)
+    (151936, torch.float32, 0.9, 0),
+    (151936, torch.float32, 0.9, 1),
+    (40003, torch.float32, 0.8, 1),
+    (40003, torch.float32, None, 0),
 ])
 def test_shapes_alignment_dtypes(oracle, V, dtype, top_p, stride_pad):
     B, K = 5, 3
