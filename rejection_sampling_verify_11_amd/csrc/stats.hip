@@ -251,11 +251,16 @@ struct HeldLogits {
   }
 };
 
-// All NT threads of the block call this.  hist256 is LDS of 256 doubles.
+// Doubles between the copies of the radix passes' 256-bin histogram: one
+// more than the bins, so that copies of one bin lie in different banks.
+constexpr int kHistStride = 257;
+
+// All NT threads of the block call this.  hist256 is LDS of HC * kHistStride
+// doubles (256 for one copy).
 // The bf16 kernel reaches it only for a vector its count table cannot hold.
 // `elems` yields this thread's logits (StreamedLogits or HeldLogits); zx is
 // the draft token's logit (NaN when there is none).
-template <int NT, class Elems>
+template <int NT, class Elems, int HC = 1>
 __device__ __forceinline__ void generic_stats(const Elems& elems, int token, float zx, float T,
                                               double P, int V, double* hist256,
                                               Scratch<NT / 64>& sc, VecRec* rec) {
@@ -284,35 +289,60 @@ __device__ __forceinline__ void generic_stats(const Elems& elems, int token, flo
     return;
   }
   const float c2 = log2e_over_T(T);
-  // pass 2: normaliser S
+  // pass 2: normaliser S and, with a top-p cut, the masses of the radix
+  // select's first digit; passes 3-5: the other three digits (8 bits each)
+  const bool cut = P < 1.0;
+  // with HC copies, lane l adds into copy l % HC: lanes of one wave that
+  // land in one bin (few bins take most logits in the first passes) then
+  // mostly hit different words
+  double* hist = hist256 + (HC > 1 ? (tid & 63) % HC * kHistStride : 0);
+  if (cut) {
+    for (int i = tid; i < HC * kHistStride; i += NT) hist256[i] = 0.0;
+    __syncthreads();
+  }
   double acc = 0.0;
-  elems.each([&](float z) { acc += weight(z, m, c2); });
+  elems.each([&](float z) {
+    const double wgt = weight(z, m, c2);
+    acc += wgt;
+    if (cut && wgt > 0.0) atomicAdd(&hist[order_key(z) >> 24], wgt);
+  });
   const double S = block_sum_d<NT>(acc, sc);
-  if (!(P < 1.0)) {
+  if (!cut) {
     if (tid == 0) write_record(token, T, T_ok, V, m, -INFINITY, S, 0, zx, rec);
     return;
   }
-  // passes 3-6: radix select of the threshold key, 8 bits at a time
+  __syncthreads();
   const double target = P * S;
   uint32_t prefix = 0;
   double kept = S;
   double above = 0.0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = tid; i < 256; i += NT) hist256[i] = 0.0;
-    __syncthreads();
-    elems.each([&](float z) {
-      // held values would otherwise keep pass 2's weights alive (and spill)
-      // instead of forming them again
-      asm volatile("" : "+v"(z));
-      if (!(z > -INFINITY)) return;
-      const uint32_t k = order_key(z);
-      if ((k & hmask) != (prefix & hmask)) return;
-      const double wgt = weight(z, m, c2);
-      if (wgt > 0.0) atomicAdd(&hist256[(k >> shift) & 255u], wgt);
-    });
-    __syncthreads();
+    if (pass > 0) {
+      const uint32_t hmask = 0xFFFFFFFFu << (shift + 8);
+      for (int i = tid; i < HC * kHistStride; i += NT) hist256[i] = 0.0;
+      __syncthreads();
+      elems.each([&](float z) {
+        // held values would otherwise keep pass 2's weights alive (and
+        // spill) instead of forming them again
+        asm volatile("" : "+v"(z));
+        if (!(z > -INFINITY)) return;
+        const uint32_t k = order_key(z);
+        if ((k & hmask) != (prefix & hmask)) return;
+        const double wgt = weight(z, m, c2);
+        if (wgt > 0.0) atomicAdd(&hist[(k >> shift) & 255u], wgt);
+      });
+      __syncthreads();
+    }
+    if constexpr (HC > 1) {
+      for (int bin = tid; bin < 256; bin += NT) {
+        double t = 0.0;
+#pragma unroll
+        for (int c = 0; c < HC; ++c) t += hist256[c * kHistStride + bin];
+        hist256[bin] = t;
+      }
+      __syncthreads();
+    }
     if (tid == 0) {
       double cum = above;
       int sel = -1, last = -1;
@@ -349,6 +379,8 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
 
 // Logits per thread that the generic kernel holds in registers.
 constexpr int kGenHeld = 32;
+// Copies of the radix histogram in the generic kernel.
+constexpr int kGenHistCopies = 16;
 
 // fp32 logits of one stored vector (the generic kernel's dtype): a typed
 // read, so that the held loads carry no dtype branch and all issue at once.
@@ -361,7 +393,7 @@ struct Fp32Logits {
 // reads the vector once into registers, otherwise every pass streams it.
 template <bool HELD>
 __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams p, int dtype) {
-  __shared__ double hist256[256];
+  __shared__ double hist256[kGenHistCopies * kHistStride];
   __shared__ Scratch<kGenThreads / 64> sc;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
@@ -371,13 +403,14 @@ __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams 
     held.load(Fp32Logits{(const float*)s.vec}, p.V);
     const float zx = (s.token >= 0 && s.token < p.V) ? logit(s.token)
                                                       : __uint_as_float(0x7FC00000u);
-    generic_stats<kGenThreads>(held, s.token, zx, s.T, s.P, p.V, hist256, sc,
+    generic_stats<kGenThreads, decltype(held), kGenHistCopies>(held, s.token, zx, s.T, s.P, p.V, hist256, sc,
                                p.recs + blockIdx.x);
   } else if (dtype == SV_FP32 && ((uintptr_t)s.vec & 15u) == 0) {
     const float* vec = (const float*)s.vec;
     const float zx = (s.token >= 0 && s.token < p.V) ? vec[s.token] : __uint_as_float(0x7FC00000u);
-    generic_stats<kGenThreads>(StreamedF32<kGenThreads>{vec, p.V}, s.token, zx, s.T, s.P, p.V,
-                               hist256, sc, p.recs + blockIdx.x);
+    generic_stats<kGenThreads, StreamedF32<kGenThreads>, kGenHistCopies>(
+        StreamedF32<kGenThreads>{vec, p.V}, s.token, zx, s.T, s.P, p.V, hist256, sc,
+        p.recs + blockIdx.x);
   } else {
     generic_stats<kGenThreads>(logit, s.token, s.T, s.P, p.V, hist256, sc, p.recs + blockIdx.x);
   }
