@@ -188,10 +188,11 @@ struct StreamedLogits {
   }
 };
 
-// fp32 logits of a vector on a 16-byte boundary, streamed on every pass in
-// 16-byte loads, kU of them in flight per thread: thread tid takes the
-// groups of four logits tid, tid + NT, ..., then the tail logits past the
-// last whole group, in that order.
+// fp32 logits of a vector, streamed on every pass in 16-byte loads, kU of
+// them in flight per thread: the logits before the first 16-byte boundary
+// (at most three, threads 0..2), then thread tid takes the groups of four
+// logits tid, tid + NT, ..., then the tail logits past the last whole group,
+// in that order.
 template <int NT>
 struct StreamedF32 {
   const float* vec;
@@ -200,8 +201,12 @@ struct StreamedF32 {
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
     const int tid = threadIdx.x;
-    const int n4 = V >> 2;
-    const float4* v4 = reinterpret_cast<const float4*>(vec);
+    const int head = min(V, (int)((((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u)) >> 2));
+    if (tid < head) f(vec[tid]);
+    const float* body = vec + head;
+    const int nb = V - head;
+    const int n4 = nb >> 2;
+    const float4* v4 = reinterpret_cast<const float4*>(body);
     int g = tid;
     for (; g + (kU - 1) * NT < n4; g += kU * NT) {
       float4 a[kU];
@@ -222,7 +227,7 @@ struct StreamedF32 {
       f(a.z);
       f(a.w);
     }
-    for (int j = 4 * n4 + tid; j < V; j += NT) f(vec[j]);
+    for (int j = 4 * n4 + tid; j < nb; j += NT) f(body[j]);
   }
 };
 
@@ -405,14 +410,17 @@ __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams 
                                                       : __uint_as_float(0x7FC00000u);
     generic_stats<kGenThreads, decltype(held), kGenHistCopies>(held, s.token, zx, s.T, s.P, p.V, hist256, sc,
                                p.recs + blockIdx.x);
-  } else if (dtype == SV_FP32 && ((uintptr_t)s.vec & 15u) == 0) {
+  } else if (dtype == SV_FP32) {
     const float* vec = (const float*)s.vec;
     const float zx = (s.token >= 0 && s.token < p.V) ? vec[s.token] : __uint_as_float(0x7FC00000u);
     generic_stats<kGenThreads, StreamedF32<kGenThreads>, kGenHistCopies>(
         StreamedF32<kGenThreads>{vec, p.V}, s.token, zx, s.T, s.P, p.V, hist256, sc,
         p.recs + blockIdx.x);
   } else {
-    generic_stats<kGenThreads>(logit, s.token, s.T, s.P, p.V, hist256, sc, p.recs + blockIdx.x);
+    const float zx = (s.token >= 0 && s.token < p.V) ? logit(s.token) : __uint_as_float(0x7FC00000u);
+    generic_stats<kGenThreads, StreamedLogits<kGenThreads, VecLogits>, kGenHistCopies>(
+        StreamedLogits<kGenThreads, VecLogits>{logit, p.V}, s.token, zx, s.T, s.P, p.V, hist256, sc,
+        p.recs + blockIdx.x);
   }
 }
 
