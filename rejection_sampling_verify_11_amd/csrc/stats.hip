@@ -265,10 +265,11 @@ constexpr int kHistStride = 257;
 // The bf16 kernel reaches it only for a vector its count table cannot hold.
 // `elems` yields this thread's logits (StreamedLogits or HeldLogits); zx is
 // the draft token's logit (NaN when there is none).
-template <int NT, class Elems, int HC = 1>
+template <int NT, class Elems, int HC = 1, int CAP = 0>
 __device__ __forceinline__ void generic_stats(const Elems& elems, int token, float zx, float T,
                                               double P, int V, double* hist256,
-                                              Scratch<NT / 64>& sc, VecRec* rec) {
+                                              Scratch<NT / 64>& sc, VecRec* rec,
+                                              float* cand = nullptr, uint32_t* ncand = nullptr) {
   const int tid = threadIdx.x;
   const bool T_ok = T > 0.0f && isfinite(T);
   // pass 1: largest finite value, NaN / +inf, any finite entry
@@ -326,17 +327,30 @@ __device__ __forceinline__ void generic_stats(const Elems& elems, int token, flo
     if (pass > 0) {
       const uint32_t hmask = 0xFFFFFFFFu << (shift + 8);
       for (int i = tid; i < HC * kHistStride; i += NT) hist256[i] = 0.0;
+      if (CAP > 0 && pass == 2 && tid == 0) *ncand = 0u;
       __syncthreads();
-      elems.each([&](float z) {
+      const auto add = [&](float z, bool keep) {
         // held values would otherwise keep pass 2's weights alive (and
         // spill) instead of forming them again
         asm volatile("" : "+v"(z));
         if (!(z > -INFINITY)) return;
         const uint32_t k = order_key(z);
         if ((k & hmask) != (prefix & hmask)) return;
+        // with CAP, the third digit's pass keeps the logits under its
+        // 16-bit prefix (few: one bf16-wide bucket) for the last digit
+        if (CAP > 0 && keep) {
+          const uint32_t i = atomicAdd(ncand, 1u);
+          if (i < (uint32_t)CAP) cand[i] = z;
+        }
         const double wgt = weight(z, m, c2);
         if (wgt > 0.0) atomicAdd(&hist[(k >> shift) & 255u], wgt);
-      });
+      };
+      if (CAP > 0 && pass == 3 && *ncand <= (uint32_t)CAP) {
+        const int n = (int)*ncand;
+        for (int i = tid; i < n; i += NT) add(cand[i], false);
+      } else {
+        elems.each([&](float z) { add(z, pass == 2); });
+      }
       __syncthreads();
     }
     if constexpr (HC > 1) {
@@ -386,6 +400,9 @@ __device__ __forceinline__ void generic_stats(const Logits& logit, int token, fl
 constexpr int kGenHeld = 32;
 // Copies of the radix histogram in the generic kernel.
 constexpr int kGenHistCopies = 16;
+// Logits under the threshold's 16-bit key prefix that the generic kernel
+// keeps in LDS, so that the last radix digit needs no pass over the vector.
+constexpr int kGenCand = 4096;
 
 // fp32 logits of one stored vector (the generic kernel's dtype): a typed
 // read, so that the held loads carry no dtype branch and all issue at once.
@@ -400,6 +417,8 @@ template <bool HELD>
 __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams p, int dtype) {
   __shared__ double hist256[kGenHistCopies * kHistStride];
   __shared__ Scratch<kGenThreads / 64> sc;
+  __shared__ float cand[kGenCand];
+  __shared__ uint32_t ncand;
   const Slot s = slot_of(p, dtype, blockIdx.x);
   if (!s.needed) return;
   const VecLogits logit{s.vec, dtype};
@@ -413,9 +432,9 @@ __global__ __launch_bounds__(kGenThreads) void stats_generic_kernel(StatsParams 
   } else if (dtype == SV_FP32) {
     const float* vec = (const float*)s.vec;
     const float zx = (s.token >= 0 && s.token < p.V) ? vec[s.token] : __uint_as_float(0x7FC00000u);
-    generic_stats<kGenThreads, StreamedF32<kGenThreads>, kGenHistCopies>(
+    generic_stats<kGenThreads, StreamedF32<kGenThreads>, kGenHistCopies, kGenCand>(
         StreamedF32<kGenThreads>{vec, p.V}, s.token, zx, s.T, s.P, p.V, hist256, sc,
-        p.recs + blockIdx.x);
+        p.recs + blockIdx.x, cand, &ncand);
   } else {
     const float zx = (s.token >= 0 && s.token < p.V) ? logit(s.token) : __uint_as_float(0x7FC00000u);
     generic_stats<kGenThreads, StreamedLogits<kGenThreads, VecLogits>, kGenHistCopies>(
