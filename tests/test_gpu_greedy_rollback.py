@@ -391,3 +391,60 @@ def test_greedy_random_configuration_sweep(oracle, case):
                               draft_tokens=None if use_draft else toks.numpy(),
                               k_per_row=None if kk is None else kk.numpy(), nthreads=8)
     compare_exact(gg, og, GREEDY_KEYS)
+
+
+def test_pool_rollback_in_a_replayed_graph():
+    """The rollback with a free stack and poisoning, captured once as a HIP
+    graph (state restored inside the graph first) and replayed with other
+    accepted counts each time: every replay equals the eager call on the
+    same state.  The poisoning's per-row commit counters are zeroed by the
+    scan in every call, so replays start clean."""
+    rng = np.random.default_rng(11)
+    B, K, ps, L, H, D = 96, 6, 8, 3, 2, 16
+    lens = (rng.integers(20, 200, B) + K + 1).astype(np.int32)
+    MP = int((lens.max() + ps - 1) // ps)
+    kv = W.paged_kv(torch.from_numpy(lens), ps, MP, spare_pages=16, seed=11)
+    init = [torch.from_numpy(lens).to(DEV), kv.page_table.to(DEV), kv.free_pages.to(DEV),
+            kv.free_top.to(DEV),
+            torch.zeros((kv.num_pages, L, 2, H, ps, D), dtype=torch.bfloat16, device=DEV)]
+
+    def state():
+        return [t.clone() for t in init]
+
+    g, e = state(), state()
+    g_acc = torch.zeros(B, dtype=torch.int32, device=DEV)
+    e_acc = torch.zeros(B, dtype=torch.int32, device=DEV)
+
+    def call(st, acc):
+        return sv.RollbackCall(st[0], acc, st[1], ps, K, free_pages=st[2], free_top=st[3],
+                               kv_pool=st[4], num_pages=kv.num_pages, num_layers=L, kv_heads=H,
+                               head_dim=D)
+
+    g_call, e_call = call(g, g_acc), call(e, e_acc)
+
+    def graphed():
+        for t, t0 in zip(g, init):
+            t.copy_(t0)
+        g_call.run()
+
+    graphed()  # loads the kernels before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed()
+    for r in range(4):
+        acc = torch.from_numpy(rng.integers(0, K + 1, B).astype(np.int32)).to(DEV)
+        g_acc.copy_(acc)
+        e_acc.copy_(acc)
+        for t, t0 in zip(e, init):
+            t.copy_(t0)
+        e_call.run()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert not e_call.row_status.any(), r
+        assert torch.equal(g_call.row_status, e_call.row_status), r
+        for a, b in zip(g, e):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), r
+        assert int((g[4].view(torch.int16) == -1).sum()) == \
+            int((torch.from_numpy(lens).to(DEV) - g[0]).sum()) * L * 2 * H * D, r
