@@ -270,7 +270,9 @@ static sv::StatsParams stats_params(const sv_verify_args* a, int mode) {
   char* plan = (char*)a->workspace + recs_bytes(a->B, a->k_max);
   p.tickets = (uint32_t*)plan;
   p.slot_count = (int32_t*)(plan + align_up(sv::stats_ticket_bytes(), 256));
-  const bool listed = a->k_per_row != nullptr || mode == 1;
+  // a list of the slots in use when rows differ in k; draft sampling with
+  // one k maps its items to the draft slots arithmetically
+  const bool listed = a->k_per_row != nullptr;
   p.slot_list = listed ? p.slot_count + 64 : nullptr;
   p.col_off = 0;
   p.partial = nullptr;

@@ -718,9 +718,19 @@ __device__ __forceinline__ uint32_t list_stride(uint32_t n) {
   return s;
 }
 
+// Items of a call without a slot list: every slot, or every draft slot when
+// sampling drafts.
+__host__ __device__ __forceinline__ int unlisted_items(const StatsParams& p) {
+  return p.mode == 1 ? p.B * p.K : p.B * slots_per_row(p.K);
+}
+
 __device__ __forceinline__ int item_slot(const StatsParams& p, int item, uint32_t n, uint32_t stride) {
   if (p.slot_list) return p.slot_list[(uint32_t)(((uint64_t)item * stride) % n)];
   const int B = p.B, K = p.K, per = slots_per_row(K);
+  if (p.mode == 1) {  // draft positions only, K-1 of every row first
+    const int q = item / B, r = item - q * B;
+    return r * per + K + 1 + (K - 1 - q);
+  }
   if (item < B) return item * per + K;
   const int i = item - B, q = i / (2 * B), r = i - q * 2 * B;
   const int pos = K - 1 - q;
@@ -1035,7 +1045,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   __shared__ Scratch<kWv> sc;           // generic path
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int V = p.V;
-  const int nitems = p.slot_list ? *p.slot_count : p.B * slots_per_row(p.K);
+  const int nitems = p.slot_list ? *p.slot_count : unlisted_items(p);
   uint4* hist4 = reinterpret_cast<uint4*>(hist);
 
   // the first item; a workgroup without one has none later either
@@ -1417,12 +1427,14 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
     // vector); extra workgroups simply wait for a free CU
     unsigned want = cus * (unsigned)kWgPerCu;
     if (want < (unsigned)kQueues) want = (unsigned)kQueues;
-    const unsigned grid = nslots < want ? nslots : want;
+    const unsigned items = p.slot_list ? nslots : (unsigned)unlisted_items(p);
+    if (items == 0) return hipSuccess;
+    const unsigned grid = items < want ? items : want;
     // With every slot in use and no more slots than workgroups, each
     // workgroup's first vector (its own index) is the whole schedule: no
     // queue counters to arm, no plan launch.
     StatsParams q = p;
-    if (!p.slot_list && nslots <= want) {
+    if (!p.slot_list && items <= want) {
       q.tickets = nullptr;
     } else {
       TimedScope ts(t, "stats_plan", s);
