@@ -609,20 +609,23 @@ __device__ __attribute__((noinline)) Side count_pair_slow(uint32_t* hist, uint32
   return sd;
 }
 
-// Loads one batch: groups i, i + kT, ... of a body with nb > 0; an index
-// past the end is clamped to the last group (loaded, not counted).
+// Loads one batch: groups i, i + NTV, ... of a body with nb > 0 (NTV
+// threads stream the vector); an index past the end is clamped to the last
+// group (loaded, not counted).
+template <int NTV>
 __device__ __forceinline__ void load_batch(uint4 (&d)[kBatch], const uint4* body, int i, int nb) {
 #pragma unroll
-  for (int s = 0; s < kBatch; ++s) d[s] = body[min(i + s * kT, nb - 1)];
+  for (int s = 0; s < kBatch; ++s) d[s] = body[min(i + s * NTV, nb - 1)];
 }
 
 // Streams one vector into the table.  Full batches go through the fast path
 // unless a logit of the batch lies outside the window (a wave-uniform test);
 // the last, partial batch and the unaligned head and tail always go through
-// the slow path.  Batch k is counted while batch k + 1 loads.
+// the slow path.  Batch k is counted while batch k + 1 loads.  NTV threads
+// stream the vector; tid is this thread's index among them.
+template <int NTV>
 __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32_t* hist,
-                                              uint32_t* tiny, Side& sd) {
-  const int tid = threadIdx.x;
+                                              uint32_t* tiny, Side& sd, int tid) {
   const uint32_t spare = (uint32_t)tid % (uint32_t)kWords;
   uint32_t* hbase = hist - kBase;
   int head = (int)(((16u - (uint32_t)((uintptr_t)vec & 15u)) & 15u) >> 1);
@@ -635,15 +638,15 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
   const uint32_t xh = vec[has_head ? tid : 0];
   const uint32_t xt = vec[has_tail ? t0 + tid : 0];
   if (nb > 0) {
-    const int step = kBatch * kT;
+    const int step = kBatch * NTV;
     const int nfull = nb / step;
     const bool part = nfull * step < nb;
     uint4 a[kBatch];
-    load_batch(a, body, tid, nb);
+    load_batch<NTV>(a, body, tid, nb);
     int i = tid;
     for (int k = 0; k < nfull; ++k) {
       uint4 n[kBatch];
-      load_batch(n, body, (k + 1 < nfull || part) ? i + step : i, nb);
+      load_batch<NTV>(n, body, (k + 1 < nfull || part) ? i + step : i, nb);
       const uint32_t ex = batch_excess(a);
       if (!__any(ex >= (uint32_t)kWords)) {
 #pragma unroll
@@ -659,7 +662,7 @@ __device__ __forceinline__ void stream_vector(const uint16_t* vec, int V, uint32
       uint32_t vmask = 0, ex = 0;
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const bool valid = i + q * kT < nb;
+        const bool valid = i + q * NTV < nb;
         vmask |= valid ? 1u << q : 0u;
         const uint32_t e = max(max(window_excess(a[q].x), window_excess(a[q].y)),
                                max(window_excess(a[q].z), window_excess(a[q].w)));
@@ -977,65 +980,7 @@ __device__ __forceinline__ void topp_record(const Table& tab, const double* bins
   if (threadIdx.x == 0) write_record(token, T, T_ok, V, m, tau, kept, status, zx, rec);
 }
 
-// The shard pass's epilogue, once the copies are merged into copy 0: the
-// vector's partial -- ShardHead, the values below the window, and the
-// nonzero table words as (word, counts) pairs in thread order (a block-wide
-// exclusive scan of each thread's count places them).  All threads call it.
-__device__ __forceinline__ void shard_emit(const StatsParams& p, int v, const uint4* hist4,
-                                           uint32_t gmask, const uint32_t* tiny, uint32_t NT,
-                                           uint32_t status, int MP, int MN, uint32_t Z,
-                                           uint32_t NI, uint32_t zx, uint32_t* wlist) {
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  uint8_t* base = p.partial + (int64_t)v * p.part_stride;
-  uint2* list = reinterpret_cast<uint2*>(base + kShardListOffset);
-  uint32_t mine = 0;
-#pragma unroll 1
-  for (int j = 0; j < kGpt; ++j) {
-    if ((gmask >> j) & 1u) {
-      const uint4 d = hist4[tid + kT * j];
-      mine += (d.x != 0u ? 1u : 0u) + (d.y != 0u ? 1u : 0u) + (d.z != 0u ? 1u : 0u) +
-              (d.w != 0u ? 1u : 0u);
-    }
-  }
-  const uint32_t incl = wave_scan_u32<OpAddU32>(mine);
-  if (l == 63) wlist[w] = incl;
-  __syncthreads();
-  uint32_t o = incl - mine, total = 0;
-#pragma unroll
-  for (int k = 0; k < kWv; ++k) {
-    o += k < w ? wlist[k] : 0u;
-    total += wlist[k];
-  }
-#pragma unroll 1
-  for (int j = 0; j < kGpt; ++j) {
-    if ((gmask >> j) & 1u) {
-      const int g = tid + kT * j;
-      const uint4 d = hist4[g];
-      const uint32_t xs[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (xs[q]) list[o++] = make_uint2(4u * (uint32_t)g + (uint32_t)q, xs[q]);
-    }
-  }
-  uint32_t* tl = reinterpret_cast<uint32_t*>(base + sizeof(ShardHead));
-  if ((uint32_t)tid < min(NT, (uint32_t)kShardTinyCap)) tl[tid] = tiny[1 + tid];
-  if (tid == 0) {
-    ShardHead h;
-    h.status = status;
-    h.maxpos = MP;
-    h.minneg = MN;
-    h.zeros = Z;
-    h.ninf = NI;
-    h.ntiny = NT;
-    h.nlist = total;
-    h.zx = zx;
-    *reinterpret_cast<ShardHead*>(base) = h;
-  }
-}
 
-// SHARD: the pass over one vocabulary shard (V = the shard's columns), whose
-// epilogue writes the partial instead of the record.
-template <bool SHARD>
 __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p) {
   __shared__ __align__(16) uint32_t hist[kCopies * kCopyWords];
   __shared__ double bins[kRankBins];
@@ -1057,7 +1002,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
   if (tid == 0) tiny[0] = 0u;
   uint32_t* hcopy = hist + (l & 1) * kCopyWords;  // this lane's copy
   const uint4* copy1 = reinterpret_cast<const uint4*>(hist + kCopyWords);
-  SlotP cur = slot_params<SHARD>(p, v);
+  SlotP cur = slot_params<false>(p, v);
 
   for (;;) {
     __syncthreads();  // every thread has read sh.next
@@ -1065,21 +1010,12 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     if (tid == 0) sh.next = p.tickets ? take_ticket(p, queue) : nitems;
     const bool T_ok = cur.T > 0.0f && isfinite(cur.T);
     VecRec* rec = p.recs + v;
-    // the draft token's logit, loaded by every thread from one address (a
-    // shard holds columns col_off.. of the vector)
-    bool has_zx;
-    uint32_t zbits;
-    if constexpr (SHARD) {
-      const int tokl = cur.token - p.col_off;
-      has_zx = cur.token >= 0 && tokl >= 0 && tokl < V;
-      zbits = cur.vec[has_zx ? tokl : 0];
-    } else {
-      has_zx = cur.token >= 0 && cur.token < V;
-      zbits = cur.vec[has_zx ? cur.token : 0];
-    }
+    // the draft token's logit, loaded by every thread from one address
+    const bool has_zx = cur.token >= 0 && cur.token < V;
+    const uint32_t zbits = cur.vec[has_zx ? cur.token : 0];
 
     Side sd;
-    stream_vector(cur.vec, V, hcopy, tiny, sd);
+    stream_vector<kT>(cur.vec, V, hcopy, tiny, sd, tid);
     {
       const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nzero));
       const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(sd.nninf));
@@ -1090,7 +1026,7 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     const int in = sh.next;
     const bool has_next = in < nitems;
     const int vn = has_next ? item_slot(p, in, (uint32_t)nitems, stride) : v;
-    const SlotP nxt = slot_params<SHARD>(p, vn);  // loads in flight meanwhile
+    const SlotP nxt = slot_params<false>(p, vn);  // loads in flight meanwhile
 
     // ---- E1: thread t merges groups t + kT j of the two copies into copy 0
     // and clears copy 1; largest +magnitude, smallest -magnitude present,
@@ -1146,39 +1082,30 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
     }
     uint32_t status = FL & SV_ROW_NONFINITE_LOGIT;
     const uint32_t NT = tiny[0];
-    if constexpr (SHARD) {
-      // a count that wrapped 16 bits, a logit above the window, or more
-      // values below it than the list holds: the merge redoes the vector
-      const bool over = (FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V;
-      shard_emit(p, v, hist4, gmask, tiny, NT, status | (over ? kShardFallback : 0u), MP, MN, Z,
-                 NI, has_zx ? (1u << 16) | (zbits & 0xFFFFu) : 0u,
-                 reinterpret_cast<uint32_t*>(bins));  // bins are free in this pass
-    } else {
-      // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
-      // count past 65535), a logit above the window, more values below it than
-      // the list holds, or no positive value in the window while some lie
-      // below it (the largest logit would be one of them): the generic path
-      // redoes the vector
-      const bool fallback =
-          !status && ((FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V ||
-                      (MP < 0 && NT > 0));
-      if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
-      const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
-                    : Z > 0   ? 0.0f
-                    : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
-                                      : -INFINITY;
-      const bool stats_ok = !fallback && !status && T_ok;
-      const float c2 = log2e_over_T(cur.T);
+    // a count wrapped 16 bits (65536 equal logits in one copy, or a merged
+    // count past 65535), a logit above the window, more values below it than
+    // the list holds, or no positive value in the window while some lie
+    // below it (the largest logit would be one of them): the generic path
+    // redoes the vector
+    const bool fallback =
+        !status && ((FL & kFallback) || WR || TT + Z + NI + NT != (uint32_t)V ||
+                    (MP < 0 && NT > 0));
+    if (!fallback && TT + Z == 0) status |= SV_ROW_NO_FINITE;
+    const float m = MP >= 0 ? bf16f((uint32_t)MP + kBase)
+                  : Z > 0   ? 0.0f
+                  : MN < 0x7FFFFFFF ? bf16f(((uint32_t)MN + kBase) | 0x8000u)
+                                    : -INFINITY;
+    const bool stats_ok = !fallback && !status && T_ok;
+    const float c2 = log2e_over_T(cur.T);
 
-      if (stats_ok) bin_masses(PackedTable{hist4}, gmask, m, c2, Z, tiny, NT, bins);
-      __syncthreads();  // B3: bins written
-      if (w == 0 && !fallback)
-        topp_record(PackedTable{hist4}, bins, tiny, NT, stats_ok, cur.P, m, c2, cur.token, cur.T,
-                    T_ok, V, status, has_zx ? bf16f(zbits) : __uint_as_float(0x7FC00000u), rec);
-      if (fallback) {
-        generic_stats<kT>(VecLogits{cur.vec, SV_BF16}, cur.token, cur.T, cur.P, V, hist256, sc,
-                          rec);
-      }
+    if (stats_ok) bin_masses(PackedTable{hist4}, gmask, m, c2, Z, tiny, NT, bins);
+    __syncthreads();  // B3: bins written
+    if (w == 0 && !fallback)
+      topp_record(PackedTable{hist4}, bins, tiny, NT, stats_ok, cur.P, m, c2, cur.token, cur.T,
+                  T_ok, V, status, has_zx ? bf16f(zbits) : __uint_as_float(0x7FC00000u), rec);
+    if (fallback) {
+      generic_stats<kT>(VecLogits{cur.vec, SV_BF16}, cur.token, cur.T, cur.P, V, hist256, sc,
+                        rec);
     }
     __syncthreads();  // B4: the table is no longer read
     if (tid == 0) tiny[0] = 0u;
@@ -1187,6 +1114,196 @@ __global__ __launch_bounds__(kT, kWgPerCu) void stats_bf16_kernel(StatsParams p)
       if ((gmask >> j) & 1u) hist4[tid + kT * j] = make_uint4(0u, 0u, 0u, 0u);
     if (!has_next) break;
     v = vn;
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------- shard pass
+
+// A vocabulary shard is a short vector (V/G columns: 38 KB of bf16 at
+// V = 151936 over 8 shards), so a workgroup's per-vector costs -- the first
+// loads' latency, the scan of the table, the list and the header -- weigh
+// about as much as its streaming.  The shard pass therefore takes two
+// vectors per workgroup pass: lanes of even index stream the pair's first
+// vector into table 0, lanes of odd index its second into table 1, one copy
+// each (so there is no merge; each table gets the lanes of one parity, as
+// the two copies of the unsharded kernel do), and waves 0-1 then scan and
+// list table 0 while waves 2-3 do table 1.  Work items are pairs of
+// consecutive items (the last one may be alone).
+constexpr int kHalfT = kT / 2;              // threads per vector while streaming / listing
+constexpr int kHalfGpt = kGroups / kHalfT;  // table groups per listing thread
+static_assert(kGroups % kHalfT == 0 && kHalfGpt <= 32 && kWv == 4, "pair tiling");
+
+struct PairShared {
+  uint32_t wzero[2][kWv], wninf[2][kWv], wflag[2][kWv];  // [vector][wave]: streaming side counts
+  int wmaxpos[kWv], wminneg[kWv];                         // [wave]: the table its wave scanned
+  uint32_t wtot[kWv], wlist[kWv];
+  int slot[2];       // the pair's vectors (slot), -1 for none
+  uint32_t zx[2];    // bit 16: the draft token is one of the shard's columns; low 16: its bits
+  int next;
+};
+
+// The list of one table's nonzero words, its below-window values and its
+// header, written by the kHalfT threads (two waves) of that table; the
+// block barrier inside is reached by every thread of the workgroup.
+__device__ __forceinline__ void pair_emit(const StatsParams& p, int v, const uint4* hist4,
+                                          uint32_t gmask, const uint32_t* tiny, uint32_t NT,
+                                          uint32_t status, int MP, int MN, uint32_t Z,
+                                          uint32_t NI, uint32_t zx, PairShared& sh) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int te = tid & (kHalfT - 1), wp = w & ~1;  // index within the pair of waves; its first wave
+  uint32_t mine = 0;
+#pragma unroll 1
+  for (int j = 0; j < kHalfGpt; ++j) {
+    if ((gmask >> j) & 1u) {
+      const uint4 d = hist4[te + kHalfT * j];
+      mine += (d.x != 0u ? 1u : 0u) + (d.y != 0u ? 1u : 0u) + (d.z != 0u ? 1u : 0u) +
+              (d.w != 0u ? 1u : 0u);
+    }
+  }
+  const uint32_t incl = wave_scan_u32<OpAddU32>(mine);
+  if (l == 63) sh.wlist[w] = incl;
+  __syncthreads();
+  const uint32_t o0 = incl - mine + (w & 1 ? sh.wlist[wp] : 0u);
+  const uint32_t total = sh.wlist[wp] + sh.wlist[wp + 1];
+  if (v < 0) return;
+  uint8_t* base = p.partial + (int64_t)v * p.part_stride;
+  uint2* list = reinterpret_cast<uint2*>(base + kShardListOffset);
+  uint32_t o = o0;
+#pragma unroll 1
+  for (int j = 0; j < kHalfGpt; ++j) {
+    if ((gmask >> j) & 1u) {
+      const int g = te + kHalfT * j;
+      const uint4 d = hist4[g];
+      const uint32_t xs[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (xs[q]) list[o++] = make_uint2(4u * (uint32_t)g + (uint32_t)q, xs[q]);
+    }
+  }
+  uint32_t* tl = reinterpret_cast<uint32_t*>(base + sizeof(ShardHead));
+  if ((uint32_t)te < min(NT, (uint32_t)kShardTinyCap)) tl[te] = tiny[1 + te];
+  if (te == 0) {
+    ShardHead hd;
+    hd.status = status;
+    hd.maxpos = MP;
+    hd.minneg = MN;
+    hd.zeros = Z;
+    hd.ninf = NI;
+    hd.ntiny = NT;
+    hd.nlist = total;
+    hd.zx = zx;
+    *reinterpret_cast<ShardHead*>(base) = hd;
+  }
+}
+
+__global__ __launch_bounds__(kT, kWgPerCu) void shard_pair_kernel(StatsParams p) {
+  __shared__ __align__(16) uint32_t hist[kCopies * kCopyWords];  // table h at h * kCopyWords
+  __shared__ uint32_t tiny[2][1 + kTinyCap];
+  __shared__ PairShared sh;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int h = l & 1;          // the vector this lane streams
+  const int tv = tid >> 1;      // its index among that vector's threads
+  const int eh = w >> 1;        // the table this thread scans and lists
+  const int te = tid & (kHalfT - 1);
+  const int V = p.V;
+  const int nitems = p.slot_list ? *p.slot_count : unlisted_items(p);
+  const int npairs = (nitems + 1) >> 1;
+  const int queue = (int)(blockIdx.x % kQueues);
+  int pr = queue_item(queue, blockIdx.x / kQueues);
+  if (pr >= npairs) return;
+  const uint32_t stride = list_stride((uint32_t)nitems);
+  for (int i = tid; i < kCopies * kCopyWords; i += kT) hist[i] = 0;
+  if (tid < 2) tiny[tid][0] = 0u;
+  uint32_t* const ht = hist + h * kCopyWords;           // streamed by this lane
+  const uint4* const et = reinterpret_cast<const uint4*>(hist + eh * kCopyWords);  // scanned
+  // this lane's vector of pair pr: slot, logits (slot 0's when the pair has
+  // no second vector, which is then not streamed) and the draft token
+  auto lane_vec = [&](int pair, int& slot, SlotP& sp) {
+    const int item = 2 * pair + h;
+    slot = item < nitems ? item_slot(p, item, (uint32_t)nitems, stride) : -1;
+    sp = slot_params<true>(p, slot >= 0 ? slot : 0);
+  };
+  int slot;
+  SlotP cur;
+  lane_vec(pr, slot, cur);
+
+  for (;;) {
+    __syncthreads();  // every thread has read the previous pass's shared figures
+    if (tid == 0) sh.next = take_ticket(p, queue);
+    if (tid < 2) {  // lanes 0 and 1 of wave 0: the pair's two vectors
+      const int tokl = cur.token - p.col_off;
+      const bool has_zx = slot >= 0 && cur.token >= 0 && tokl >= 0 && tokl < V;
+      sh.slot[h] = slot;
+      sh.zx[h] = has_zx ? (1u << 16) | (uint32_t)cur.vec[tokl] : 0u;
+    }
+    Side sd;
+    stream_vector<kHalfT>(cur.vec, slot >= 0 ? V : 0, ht, tiny[h], sd, tv);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t z = wave_last_u32(wave_scan_u32<OpAddU32>(h == q ? sd.nzero : 0u));
+      const uint32_t n = wave_last_u32(wave_scan_u32<OpAddU32>(h == q ? sd.nninf : 0u));
+      const uint32_t f = wave_last_u32(wave_scan_u32<OpOrU32>(h == q ? sd.flags : 0u));
+      if (l == 0) { sh.wzero[q][w] = z; sh.wninf[q][w] = n; sh.wflag[q][w] = f; }
+    }
+    __syncthreads();  // B1: both tables complete
+    const int in = sh.next;
+    const bool has_next = in < npairs;
+    int nslot = slot;
+    SlotP nxt = cur;
+    if (has_next) lane_vec(in, nslot, nxt);  // loads in flight meanwhile
+
+    // scan of table eh by its two waves: groups te + kHalfT j
+    uint32_t gmask = 0, total = 0;
+    int maxpos = -1, minneg = 0x7FFFFFFF;
+#pragma unroll 1
+    for (int j = 0; j < kHalfGpt; ++j) {
+      const uint4 d = et[te + kHalfT * j];
+      if (!__any((d.x | d.y | d.z | d.w) != 0u)) continue;
+      const uint32_t a[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = a[q] & 0xFFFFu, hi = a[q] >> 16;
+        const int word = 4 * (te + kHalfT * j) + q;
+        total += lo + hi;
+        if (lo) maxpos = max(maxpos, word);
+        if (hi) minneg = min(minneg, word);
+      }
+      if (d.x | d.y | d.z | d.w) gmask |= 1u << j;
+    }
+    {
+      const int a = (int)wave_last_u32(wave_scan_u32<OpMaxI32>((uint32_t)maxpos));
+      const int b = (int)wave_last_u32(wave_scan_u32<OpMinI32>((uint32_t)minneg));
+      const uint32_t t = wave_last_u32(wave_scan_u32<OpAddU32>(total));
+      if (l == 0) { sh.wmaxpos[w] = a; sh.wminneg[w] = b; sh.wtot[w] = t; }
+    }
+    __syncthreads();  // B2
+    const int wp = 2 * eh;
+    const int MP = max(sh.wmaxpos[wp], sh.wmaxpos[wp + 1]);
+    const int MN = min(sh.wminneg[wp], sh.wminneg[wp + 1]);
+    const uint32_t TT = sh.wtot[wp] + sh.wtot[wp + 1];
+    uint32_t Z = 0, NI = 0, FL = 0;
+#pragma unroll
+    for (int k = 0; k < kWv; ++k) {
+      Z += sh.wzero[eh][k];
+      NI += sh.wninf[eh][k];
+      FL |= sh.wflag[eh][k];
+    }
+    const uint32_t NT = tiny[eh][0];
+    // a count that wrapped 16 bits, a logit above the window, or more values
+    // below it than the list holds: the merge redoes the vector
+    const bool over = (FL & kFallback) || TT + Z + NI + NT != (uint32_t)V;
+    const uint32_t status = (FL & SV_ROW_NONFINITE_LOGIT) | (over ? kShardFallback : 0u);
+    pair_emit(p, sh.slot[eh], et, gmask, tiny[eh], NT, status, MP, MN, Z, NI, sh.zx[eh], sh);
+    __syncthreads();  // B3: the tables are no longer read
+    if (te == 0) tiny[eh][0] = 0u;
+    uint4* const et_w = reinterpret_cast<uint4*>(hist + eh * kCopyWords);
+#pragma unroll 1
+    for (int j = 0; j < kHalfGpt; ++j)
+      if ((gmask >> j) & 1u) et_w[te + kHalfT * j] = make_uint4(0u, 0u, 0u, 0u);
+    if (!has_next) break;
+    pr = in;
+    slot = nslot;
     cur = nxt;
   }
 }
@@ -1444,9 +1561,9 @@ hipError_t launch_stats(const StatsParams& p, int dtype, int num_cus, hipStream_
     // execution as a kernel trace does
     hipEvent_t e0, e1;
     if (t && t->pair("stats_bf16", &e0, &e1))
-      hipExtLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, e0, e1, 0u, q);
+      hipExtLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, e0, e1, 0u, q);
     else
-      hipLaunchKernelGGL(stats_bf16_kernel<false>, dim3(grid), dim3(kT), 0, s, q);
+      hipLaunchKernelGGL(stats_bf16_kernel, dim3(grid), dim3(kT), 0, s, q);
   } else {
     TimedScope ts(t, "stats_generic", s);
     if (dtype == SV_FP32 && p.V <= kGenThreads * kGenHeld)
@@ -1465,13 +1582,16 @@ hipError_t launch_shard_stats(const StatsParams& p, int num_cus, hipStream_t s, 
   const unsigned cus = num_cus > 0 ? (unsigned)num_cus : 256u;
   unsigned want = cus * (unsigned)kWgPerCu;
   if (want < (unsigned)kQueues) want = (unsigned)kQueues;
-  const unsigned grid = nslots < want ? nslots : want;
+  // work items are pairs of vectors (of the listed slots when there is a
+  // list, which holds at most nslots)
+  const unsigned npairs = (nslots + 1) / 2;
+  const unsigned grid = npairs < want ? npairs : want;
   {
     TimedScope ts(t, "stats_plan", s);
     hipLaunchKernelGGL(stats_plan_kernel, dim3(1), dim3(kPlanT), 0, s, p, grid);
   }
   TimedScope ts(t, "shard_stats", s);
-  hipLaunchKernelGGL(stats_bf16_kernel<true>, dim3(grid), dim3(kT), 0, s, p);
+  hipLaunchKernelGGL(shard_pair_kernel, dim3(grid), dim3(kT), 0, s, p);
   return hipGetLastError();
 }
 
